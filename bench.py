@@ -1,0 +1,225 @@
+"""Benchmark of the QLoRA NF4 linear hot path on one MI355X.
+
+Step = one training step of the frozen-NF4 QLoRA linear at the LLaMA-7B MLP
+shape (4096 tokens, 4096 -> 11008, r = 64, alpha = 16): forward (U = X·Aᵀ, then
+the dequant-GEMM with the LoRA prologue) and backward (V = dY·B, the
+transposed dequant-GEMM for dX, dA and dB), on resident synthetic inputs.
+`value` = algorithmic TFLOP/s of that step.  The same run also measures the
+other rows of the hot path: the fused NF4 + double-quant quantiser and the
+dequantiser (GB/s over the weight), and the few-token forward at 8192 -> 28672
+(GB/s over the weight it streams, M = 1..8, weight copies rotated past the
+256 MB Infinity Cache).
+
+Prints ONE JSON line.  --gpus N > 1 is not supported (single-GPU build).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _time_ms(fn, iters, warmup=2):
+    import torch
+    for _ in range(warmup):
+        fn()
+    s, e = _events()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="time only the training step")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the build has no multi-GPU path "
+              "(the linear shards by tokens with one all-reduce of dA, dB; not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wlc = wl.LLAMA7B_MLP
+    M, K, N, r, alpha = wlc.M, wlc.k_in, wlc.n_out, wlc.r, wlc.alpha
+    inp = wlc.inputs()
+    W = torch.from_numpy(inp["W"]).to(dev)
+    X, A, B, dY = (inp[k].to(dev) for k in ("X", "A", "B", "dY"))
+    wq = q.quantize_weight(W)
+    ws_f = torch.empty(q.workspace_size(0, M, N, K, r), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(q.workspace_size(1, M, N, K, r), dtype=torch.uint8, device=dev)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    U = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(r, K, dtype=torch.float32, device=dev)
+    dB = torch.empty(N, r, dtype=torch.float32, device=dev)
+
+    def step():
+        q.linear_fwd(wq, X, A, B, alpha, workspace=ws_f, Y=Y, U=U)
+        q.linear_bwd(wq, X, dY, A, B, U, alpha, workspace=ws_b, dX=dX, dA=dA, dB=dB)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s, e = _events()
+    s.record()
+    for _ in range(args.steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = s.elapsed_time(e) / args.steps
+    flops = wlc.flops_fwd + wlc.flops_bwd
+    tflops = flops / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel: the forward dequant-GEMM (one launch: Y = X·Ŵᵀ + s·U·Bᵀ)
+    gemm_flops = 2 * M * K * N + 2 * M * r * N
+    ms_gemm = _time_ms(lambda: q.nf4_matmul_fwd(wq, X, U, B, alpha, workspace=ws_f, Y=Y),
+                       args.steps)
+    gemm_tflops = gemm_flops / (ms_gemm * 1e-3) / 1e12
+    # the input-gradient GEMM, timed through the backward (reported for context)
+    ms_bwd = _time_ms(lambda: q.linear_bwd(wq, X, dY, A, B, U, alpha, workspace=ws_b, dX=dX,
+                                           dA=dA, dB=dB), args.steps)
+    ms_fwd = _time_ms(lambda: q.linear_fwd(wq, X, A, B, alpha, workspace=ws_f, Y=Y, U=U),
+                      args.steps)
+
+    rows = {}
+    if not args.no_rows:
+        n = K * N
+        # quantiser (fused NF4 + DQ): reads 4 B, writes 0.5 + 1/64 + 4/16384 B per weight
+        qbytes = n * 4 + n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4
+        ms_q = _time_ms(lambda: q.quantize_nf4_dq(W), 10)
+        # dequantiser: reads the NF4 storage, writes bf16
+        dbytes = n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4 + 2 * n
+        wd = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+        ms_d = _time_ms(lambda: q.dequantize_nf4(wq, out=wd), 10)
+        rows["quantize_nf4_dq"] = dict(shape=[N, K], ms=ms_q, GBps=qbytes / ms_q / 1e6,
+                                       hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS)
+        rows["dequantize_nf4"] = dict(shape=[N, K], ms=ms_d, GBps=dbytes / ms_d / 1e6,
+                                      hbm_frac=dbytes / ms_d / 1e6 / HBM_PEAK_GBS)
+        del wd
+        # few-token forward, 8192 -> 28672, r = 16; 5 weight copies (> 2x the MALL)
+        g = wl.GEMV_70B
+        gin = g.inputs(M=8)
+        copies = []
+        Wg = torch.from_numpy(gin["W"]).to(dev)
+        for c in range(5):
+            copies.append(q.quantize_weight(Wg if c == 0 else Wg * (1.0 + c * 1e-3)))
+        del Wg
+        Ag, Bg = gin["A"].to(dev), gin["B"].to(dev)
+        gemv = {}
+        for m in wl.GEMV_TOKENS:
+            Xg = wl.bf16_normal(4, (m, g.k_in), 1.0, tensor=wl.T_X).to(dev)
+            wsg = torch.empty(q.workspace_size(0, m, g.n_out, g.k_in, g.r), dtype=torch.uint8,
+                              device=dev)
+            Yg = torch.empty(m, g.n_out, dtype=torch.bfloat16, device=dev)
+            Ug = torch.empty(m, g.r, dtype=torch.bfloat16, device=dev)
+            it = [0]
+
+            def fwd():
+                w_ = copies[it[0] % len(copies)]
+                it[0] += 1
+                q.linear_fwd(w_, Xg, Ag, Bg, g.alpha, workspace=wsg, Y=Yg, U=Ug)
+            ms = _time_ms(fwd, 50, warmup=5)
+            gbytes = copies[0].nbytes + 2 * m * g.k_in + 2 * g.r * (g.k_in + g.n_out) \
+                + 2 * m * g.n_out + 2 * m * g.r
+            gemv[str(m)] = dict(us=ms * 1e3, GBps=gbytes / ms / 1e6,
+                                hbm_frac=gbytes / ms / 1e6 / HBM_PEAK_GBS)
+        rows["few_token_fwd_8192x28672_r16"] = gemv
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, wlc)
+
+    out = {
+        "metric": "QLoRA linear fwd+bwd TFLOP/s (LLaMA-7B MLP 4096x11008, 4096 tokens, r=64)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) fp32 weight -> NF4+DQ; bf16 N(0,1) X, dY; "
+                "bf16 N(0,0.01) A, B)",
+        "config": {"workload": wlc.name, "tokens": M, "k_in": K, "n_out": N, "r": r,
+                   "alpha": alpha, "flops_per_step": flops,
+                   "fwd_ms": ms_fwd, "bwd_ms": ms_bwd},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_kernel<256,256,2,2,B_NF4_COLS,prologue,bf16> (forward dequant-GEMM)",
+            "achieved": gemm_tflops,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / BF16_PEAK_TFLOPS,
+            "ms": ms_gemm,
+            "traffic": None,
+        },
+        "rows": rows,
+        "cpu_baseline": cpu,
+        "wall_s": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(inp, wlc):
+    """The oracle, untuned, on the host cores: decode the weight from its NF4 +
+    DQ storage and run the float64 forward and backward for the whole batch."""
+    import numpy as np
+    import torch
+
+    from oracle.linear import linear_bwd, linear_fwd, lora_scale
+    from oracle.quant import bf16_to_f64, dequantize_nf4, double_quant, quantize_nf4
+
+    cores = len(os.sched_getaffinity(0))
+    packed, absmax = quantize_nf4(inp["W"].ravel())
+    qa, c2 = double_quant(absmax)
+    f64 = lambda t: t.to(torch.float64).numpy()
+    X, A, B, dY = (f64(inp[k]) for k in ("X", "A", "B", "dY"))
+    s = lora_scale(wlc.alpha, wlc.r)
+    t0 = time.perf_counter()
+    w64 = bf16_to_f64(dequantize_nf4(packed, qa, c2, inp["W"].size)).reshape(wlc.n_out, wlc.k_in)
+    Y, U = linear_fwd(X, w64, A, B, s)
+    dX, dA, dB = linear_bwd(X, dY, w64, A, B, s)
+    dt = time.perf_counter() - t0
+    flops = wlc.flops_fwd + wlc.flops_bwd
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"one full step of {wlc.name}: decode + fp64 forward + backward, "
+                      "all 4096 tokens (numpy, float64)"}
+
+
+if __name__ == "__main__":
+    main()

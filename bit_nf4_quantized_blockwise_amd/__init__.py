@@ -1,0 +1,248 @@
+"""Thin Python binding of libqlora.so (the gfx950 QLoRA NF4 linear library).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every computation runs in the library's HIP kernels.  The library must
+have been built (``python -m bit_nf4_quantized_blockwise_amd.build``); there is
+no fallback of any kind — a missing library raises.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qlora.h")
+
+BLOCKSIZE = 64
+DQ_GROUP = 256
+
+STATUS = {
+    0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_ALIGN",
+    4: "QLORA_ERR_UNSUPPORTED", 5: "QLORA_ERR_WORKSPACE", 6: "QLORA_ERR_DEVICE",
+    7: "QLORA_ERR_LAUNCH",
+}
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class NF4Weight(ctypes.Structure):
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("qabsmax", ctypes.c_void_p),
+        ("c2", ctypes.c_void_p),
+        ("n_out", ctypes.c_int64),
+        ("k_in", ctypes.c_int64),
+    ]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_W = ctypes.POINTER(NF4Weight)
+
+_SIGNATURES = {
+    "qlora_quantize_nf4": ([_P, _I64, _I32, _P, _P, _P], _I32),
+    "qlora_double_quant": ([_P, _I64, _I32, _P, _P, _P], _I32),
+    "qlora_quantize_nf4_dq": ([_P, _I64, _P, _P, _P, _P, _P], _I32),
+    "qlora_dequantize_nf4": ([_W, _P, _P], _I32),
+    "qlora_linear_fwd": ([_W, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P], _I32),
+    "qlora_linear_bwd": ([_W, _P, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "qlora_lora_down": ([_P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P], _I32),
+    "qlora_nf4_matmul_fwd": ([_W, _P, _I64, _P, _P, _I32, _F, _P, _P, _SZ, _P], _I32),
+    "qlora_workspace_size": ([_I32, _I64, _I64, _I64, _I32], _SZ),
+    "qlora_nf4_codebook": ([_P], None),
+    "qlora_status_string": ([_I32], ctypes.c_char_p),
+    "qlora_abi_version": ([], _I32),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m bit_nf4_quantized_blockwise_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status, where):
+    if status != 0:
+        raise QloraError(status, where)
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+@dataclass
+class NF4Tensor:
+    """A frozen weight W[n_out][k_in] in NF4 + Double Quantization storage."""
+    packed: torch.Tensor   # uint8 [n_out * k_in / 2]
+    qabsmax: torch.Tensor  # int8  [n_out * k_in / 64]
+    c2: torch.Tensor       # float32 [ceil(n_out * k_in / 64 / 256)]
+    n_out: int
+    k_in: int
+
+    def c_struct(self):
+        return NF4Weight(self.packed.data_ptr(), self.qabsmax.data_ptr(), self.c2.data_ptr(),
+                         self.n_out, self.k_in)
+
+    @property
+    def nbytes(self):
+        return self.packed.numel() + self.qabsmax.numel() + self.c2.numel() * 4
+
+
+def abi_version():
+    return lib().qlora_abi_version()
+
+
+def codebook():
+    out = (ctypes.c_float * 16)()
+    lib().qlora_nf4_codebook(ctypes.cast(out, ctypes.c_void_p))
+    return [out[i] for i in range(16)]
+
+
+def status_string(s):
+    return lib().qlora_status_string(s).decode()
+
+
+def workspace_size(op, M, n_out, k_in, r):
+    return lib().qlora_workspace_size(op, M, n_out, k_in, r)
+
+
+def _nblocks(n):
+    return (n + BLOCKSIZE - 1) // BLOCKSIZE
+
+
+def quantize_nf4(w):
+    """First level: (packed uint8, absmax float32) of a float32 CUDA tensor."""
+    n = w.numel()
+    nb = _nblocks(n)
+    packed = torch.empty(nb * 32, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(nb, dtype=torch.float32, device=w.device)
+    _check(lib().qlora_quantize_nf4(_ptr(w), n, BLOCKSIZE, _ptr(packed), _ptr(absmax),
+                                    _stream(w.device)), "qlora_quantize_nf4")
+    return packed, absmax
+
+
+def double_quant(absmax):
+    """Second level: (qabsmax int8, c2 float32)."""
+    nb = absmax.numel()
+    q = torch.empty(nb, dtype=torch.int8, device=absmax.device)
+    c2 = torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=absmax.device)
+    _check(lib().qlora_double_quant(_ptr(absmax), nb, DQ_GROUP, _ptr(q), _ptr(c2),
+                                    _stream(absmax.device)), "qlora_double_quant")
+    return q, c2
+
+
+def quantize_nf4_dq(w, want_absmax=False):
+    """Both levels in one pass: (packed, qabsmax, c2[, absmax])."""
+    n = w.numel()
+    nb = _nblocks(n)
+    dev = w.device
+    packed = torch.empty(nb * 32, dtype=torch.uint8, device=dev)
+    q = torch.empty(nb, dtype=torch.int8, device=dev)
+    c2 = torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=dev)
+    absmax = torch.empty(nb, dtype=torch.float32, device=dev) if want_absmax else None
+    _check(lib().qlora_quantize_nf4_dq(_ptr(w), n, _ptr(packed), _ptr(q), _ptr(c2),
+                                       _ptr(absmax), _stream(dev)), "qlora_quantize_nf4_dq")
+    return (packed, q, c2, absmax) if want_absmax else (packed, q, c2)
+
+
+def quantize_weight(w):
+    """NF4Tensor of a float32 CUDA weight [n_out][k_in]."""
+    n_out, k_in = w.shape
+    packed, q, c2 = quantize_nf4_dq(w)
+    return NF4Tensor(packed, q, c2, n_out, k_in)
+
+
+def dequantize_nf4(wq, out=None):
+    """bf16 [n_out][k_in] decoded weight."""
+    if out is None:
+        out = torch.empty(wq.n_out, wq.k_in, dtype=torch.bfloat16, device=wq.packed.device)
+    ws = wq.c_struct()
+    _check(lib().qlora_dequantize_nf4(ctypes.byref(ws), _ptr(out), _stream(out.device)),
+           "qlora_dequantize_nf4")
+    return out
+
+
+def _workspace(op, M, wq, r, device):
+    nbytes = workspace_size(op, M, wq.n_out, wq.k_in, r)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def linear_fwd(wq, X, A, B, alpha, workspace=None, Y=None, U=None):
+    """(Y, U): Y = X·Ŵᵀ + (alpha/r)·(X·Aᵀ)·Bᵀ, U = X·Aᵀ, bf16."""
+    M, r = X.shape[0], A.shape[0]
+    dev = X.device
+    Y = torch.empty(M, wq.n_out, dtype=torch.bfloat16, device=dev) if Y is None else Y
+    U = torch.empty(M, r, dtype=torch.bfloat16, device=dev) if U is None else U
+    ws = _workspace(0, M, wq, r, dev) if workspace is None else workspace
+    st = wq.c_struct()
+    _check(lib().qlora_linear_fwd(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, alpha,
+                                  _ptr(Y), _ptr(U), _ptr(ws), ws.numel(), _stream(dev)),
+           "qlora_linear_fwd")
+    return Y, U
+
+
+def lora_down(X, A, workspace=None, U=None):
+    M, K = X.shape
+    r = A.shape[0]
+    dev = X.device
+    U = torch.empty(M, r, dtype=torch.bfloat16, device=dev) if U is None else U
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(0, M, 8, K, r), 256), dtype=torch.uint8,
+                                device=dev)
+    _check(lib().qlora_lora_down(_ptr(X), M, K, _ptr(A), r, _ptr(U), _ptr(workspace),
+                                 workspace.numel(), _stream(dev)), "qlora_lora_down")
+    return U
+
+
+def nf4_matmul_fwd(wq, X, U, B, alpha, workspace=None, Y=None):
+    M, r = X.shape[0], B.shape[1]
+    dev = X.device
+    Y = torch.empty(M, wq.n_out, dtype=torch.bfloat16, device=dev) if Y is None else Y
+    ws = _workspace(0, M, wq, r, dev) if workspace is None else workspace
+    st = wq.c_struct()
+    _check(lib().qlora_nf4_matmul_fwd(ctypes.byref(st), _ptr(X), M, _ptr(U), _ptr(B), r, alpha,
+                                      _ptr(Y), _ptr(ws), ws.numel(), _stream(dev)),
+           "qlora_nf4_matmul_fwd")
+    return Y
+
+
+def linear_bwd(wq, X, dY, A, B, U, alpha, workspace=None, dX=None, dA=None, dB=None):
+    """(dX bf16, dA fp32, dB fp32)."""
+    M, r = dY.shape[0], A.shape[0]
+    dev = dY.device
+    dX = torch.empty(M, wq.k_in, dtype=torch.bfloat16, device=dev) if dX is None else dX
+    dA = torch.empty(r, wq.k_in, dtype=torch.float32, device=dev) if dA is None else dA
+    dB = torch.empty(wq.n_out, r, dtype=torch.float32, device=dev) if dB is None else dB
+    ws = _workspace(1, M, wq, r, dev) if workspace is None else workspace
+    st = wq.c_struct()
+    _check(lib().qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r,
+                                  alpha, _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                  ws.numel(), _stream(dev)), "qlora_linear_bwd")
+    return dX, dA, dB

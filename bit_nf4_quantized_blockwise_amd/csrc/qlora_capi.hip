@@ -1,0 +1,547 @@
+// Host side of libqlora.so: argument validation, workspace layout, launch
+// planning.  Every entry point validates all arguments before enqueuing
+// anything; on an error status nothing is launched.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+
+#include "qlora_kernels.h"
+
+using namespace qlora;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+qlora_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QLORA_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int s = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (s == 1) return QLORA_OK;
+    if (s == 2) return QLORA_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QLORA_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? QLORA_OK : QLORA_ERR_DEVICE;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t rup(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+#define QCHECK(cond, err) \
+  do {                    \
+    if (!(cond)) return (err); \
+  } while (0)
+
+inline qlora_status launched() {
+  return hipGetLastError() == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int grid_for(int64_t n, int per = 256, int cap = 65536) {
+  int64_t g = (n + per - 1) / per;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+// ---- GEMM launch plans ----------------------------------------------------------
+
+struct Plan {
+  int tiles_m, tiles_n, nkt, kt_per_split, nsplit;
+};
+
+Plan plan(int64_t rows, int64_t cols, int64_t red, int mt, int nt, bool allow_split,
+          int target_wgs = 512) {
+  Plan p;
+  p.tiles_m = (int)ceil_div(rows, mt);
+  p.tiles_n = (int)ceil_div(cols, nt);
+  p.nkt = (int)ceil_div(red, 64);
+  int s = 1;
+  const int tiles = p.tiles_m * p.tiles_n;
+  if (allow_split && tiles > 0 && tiles < target_wgs && p.nkt > 1) s = (int)std::min<int64_t>(ceil_div(target_wgs, tiles), p.nkt);
+  p.kt_per_split = (int)ceil_div(std::max(p.nkt, 1), s);
+  p.nsplit = (int)ceil_div(std::max(p.nkt, 1), p.kt_per_split);
+  return p;
+}
+
+// Tile shapes of the instantiated kernels.
+constexpr int BIG_MT = 256, BIG_NT = 256;   // NF4 GEMMs, many tokens
+constexpr int SM_MT = 64, SM_NT = 256;      // NF4 GEMMs, few tokens (split-K)
+constexpr int SK_MT = 128, SK_NT = 64;      // skinny: U = X·Aᵀ, V = dY·B
+constexpr int TR_MT = 64, TR_NT = 256;      // token-reduction: dA, dB
+constexpr int64_t kBigM = 128;              // use the big tiles from this many tokens on
+
+bool use_big(int64_t M) { return M >= kBigM; }
+
+// Forward workspace layout.
+struct FwdWs {
+  size_t u_part, pad_u, pad_b, y_part, total;
+  Plan pu, py;
+  int64_t rp;
+};
+
+FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  FwdWs w{};
+  w.rp = rup(r, 8);
+  w.pu = plan(M, r, K, SK_MT, SK_NT, true);
+  const int64_t ldu = (int64_t)w.pu.tiles_n * SK_NT;
+  size_t off = 0;
+  w.u_part = off;
+  off += align256((size_t)w.pu.nsplit * M * ldu * 4);
+  w.pad_u = w.pad_b = off;
+  if (r % 8 != 0) {
+    w.pad_u = off;
+    off += align256((size_t)M * w.rp * 2);
+    w.pad_b = off;
+    off += align256((size_t)N * w.rp * 2);
+  }
+  w.y_part = off;
+  if (!use_big(M)) {
+    w.py = plan(M, N, K, SM_MT, SM_NT, true);
+    off += align256((size_t)w.py.nsplit * M * N * 4);
+  }
+  w.total = std::max<size_t>(off, 256);
+  return w;
+}
+
+struct BwdWs {
+  size_t bt, v, vt, ut, at, part, total;
+  Plan pv, pdx, pda, pdb;
+  int64_t rp, Mp;
+};
+
+BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  BwdWs w{};
+  w.rp = rup(r, 8);
+  w.Mp = rup(std::max<int64_t>(M, 1), 8);
+  size_t off = 0;
+  w.bt = off; off += align256((size_t)r * N * 2);
+  w.v = off; off += align256((size_t)M * w.rp * 2);
+  w.vt = off; off += align256((size_t)r * w.Mp * 2);
+  w.ut = off; off += align256((size_t)r * w.Mp * 2);
+  w.at = off; off += align256((size_t)K * w.rp * 2);
+  w.part = off;
+  w.pv = plan(M, r, N, SK_MT, SK_NT, true);
+  size_t part = (size_t)w.pv.nsplit * M * ((size_t)w.pv.tiles_n * SK_NT) * 4;
+  if (!use_big(M)) {
+    w.pdx = plan(M, K, N, SM_MT, SM_NT, true);
+    part = std::max(part, (size_t)w.pdx.nsplit * M * K * 4);
+  }
+  w.pda = plan(r, K, M, TR_MT, TR_NT, true);
+  part = std::max(part, (size_t)w.pda.nsplit * r * K * 4);
+  w.pdb = plan(r, N, M, TR_MT, TR_NT, true);
+  part = std::max(part, (size_t)w.pdb.nsplit * r * N * 4);
+  off += align256(part);
+  w.total = std::max<size_t>(off, 256);
+  return w;
+}
+
+template <int MT, int NT, int WM, int WN, int BM, bool PRO, int OM>
+qlora_status run_gemm(GemmArgs g, const Plan& p, hipStream_t st) {
+  g.tiles_m = p.tiles_m;
+  g.tiles_n = p.tiles_n;
+  g.kt_per_split = p.kt_per_split;
+  dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.nsplit);
+  hipLaunchKernelGGL((gemm_kernel<MT, NT, WM, WN, BM, PRO, OM>), grid, dim3(256), 0, st, g);
+  return launched();
+}
+
+qlora_status run_reduce(const float* part, int64_t part_stride, int nsplit, int64_t rows,
+                        int64_t cols, int64_t rows_pad, int64_t cols_pad, int64_t ldp, float scale,
+                        ReduceOut o0, ReduceOut o1, hipStream_t st) {
+  const int64_t total = rows_pad * cols_pad;
+  if (total == 0) return QLORA_OK;
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid_for(total)), dim3(256), 0, st, part,
+                     part_stride, nsplit, rows, cols, rows_pad, cols_pad, ldp, scale, o0, o1);
+  return launched();
+}
+
+constexpr ReduceOut kNoOut{nullptr, nullptr, 0, 0};
+
+qlora_status validate_weight(const qlora_nf4_weight* w) {
+  QCHECK(w != nullptr, QLORA_ERR_NULL);
+  QCHECK(w->n_out >= 0 && w->k_in >= 0, QLORA_ERR_SHAPE);
+  if (w->n_out > 0 && w->k_in > 0) {
+    QCHECK(w->packed && w->qabsmax && w->c2, QLORA_ERR_NULL);
+    QCHECK(aligned16(w->packed) && aligned16(w->qabsmax) && aligned16(w->c2), QLORA_ERR_ALIGN);
+  }
+  return QLORA_OK;
+}
+
+qlora_status validate_linear(const qlora_nf4_weight* w, int64_t M, int32_t r) {
+  qlora_status s = validate_weight(w);
+  if (s != QLORA_OK) return s;
+  QCHECK(M >= 0, QLORA_ERR_SHAPE);
+  QCHECK(w->k_in % 64 == 0 && w->n_out % 8 == 0, QLORA_ERR_SHAPE);
+  QCHECK(w->n_out > 0 && w->k_in > 0, QLORA_ERR_SHAPE);
+  QCHECK(r >= 1 && r <= QLORA_MAX_RANK, QLORA_ERR_UNSUPPORTED);
+  return QLORA_OK;
+}
+
+#define ALIGNED_OR_NULL(p) QCHECK((p) != nullptr, QLORA_ERR_NULL); QCHECK(aligned16(p), QLORA_ERR_ALIGN)
+
+// U = X·Aᵀ (bf16 [M][r]) through split-K partials in ws.
+qlora_status lora_down_impl(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r,
+                            uint16_t* U, uint16_t* Upad, int64_t rp, char* ws, const FwdWs& L,
+                            hipStream_t st) {
+  if (M == 0) return QLORA_OK;
+  GemmArgs g{};
+  g.a = X; g.lda = K; g.rows = M; g.cols = r; g.red = K;
+  g.b = A; g.ldb = K;
+  g.out_f32 = reinterpret_cast<float*>(ws + L.u_part);
+  g.ldo = (int64_t)L.pu.tiles_n * SK_NT;
+  g.part_stride = M * g.ldo;
+  qlora_status s = run_gemm<SK_MT, SK_NT, 4, 1, B_BF16_CR, false, O_F32>(g, L.pu, st);
+  if (s != QLORA_OK) return s;
+  s = run_reduce(g.out_f32, g.part_stride, L.pu.nsplit, M, r, M, r, g.ldo, 1.0f,
+                 ReduceOut{U, nullptr, r, 0}, kNoOut, st);
+  if (s != QLORA_OK || !Upad) return s;
+  // zero-padded copy with a pitch that is a multiple of 8, for the prologue's 16-byte loads
+  return run_reduce(g.out_f32, g.part_stride, L.pu.nsplit, M, r, M, rp, g.ldo, 1.0f,
+                    ReduceOut{Upad, nullptr, rp, 0}, kNoOut, st);
+}
+
+qlora_status matmul_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M,
+                             const uint16_t* Upro, int64_t ldu, const uint16_t* Bpro, int64_t ldb,
+                             int32_t r, float s, uint16_t* Y, char* ws, const FwdWs& L,
+                             hipStream_t st) {
+  if (M == 0) return QLORA_OK;
+  const int64_t N = w->n_out, K = w->k_in;
+  GemmArgs g{};
+  g.a = X; g.lda = K; g.rows = M; g.cols = N; g.red = K;
+  g.packed = w->packed; g.qabsmax = w->qabsmax; g.c2 = w->c2; g.w_kin = K;
+  g.pl = Upro; g.ldpl = ldu; g.pr = Bpro; g.ldpr = ldb; g.rl = r; g.s = s;
+  if (use_big(M)) {
+    g.out_bf16 = Y; g.ldo = N;
+    return run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_COLS, true, O_BF16>(
+        g, plan(M, N, K, BIG_MT, BIG_NT, false), st);
+  }
+  g.out_f32 = reinterpret_cast<float*>(ws + L.y_part);
+  g.ldo = N;
+  g.part_stride = M * N;
+  qlora_status e = run_gemm<SM_MT, SM_NT, 1, 4, B_NF4_COLS, true, O_F32>(g, L.py, st);
+  if (e != QLORA_OK) return e;
+  return run_reduce(g.out_f32, g.part_stride, L.py.nsplit, M, N, M, N, N, 1.0f,
+                    ReduceOut{Y, nullptr, N, 0}, kNoOut, st);
+}
+
+float scale_of(float alpha, int32_t r) { return alpha / (float)r; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t qlora_abi_version(void) { return QLORA_ABI_VERSION; }
+
+void qlora_nf4_codebook(float out[16]) {
+  if (!out) return;
+  for (int i = 0; i < 16; ++i) out[i] = bits_to_float(kNF4Bits[i]);
+}
+
+const char* qlora_status_string(qlora_status s) {
+  switch (s) {
+    case QLORA_OK: return "QLORA_OK";
+    case QLORA_ERR_NULL: return "QLORA_ERR_NULL: a required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "QLORA_ERR_SHAPE: invalid size";
+    case QLORA_ERR_ALIGN: return "QLORA_ERR_ALIGN: device pointer not 16-byte aligned";
+    case QLORA_ERR_UNSUPPORTED: return "QLORA_ERR_UNSUPPORTED: unsupported blocksize, group or rank";
+    case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace missing or too small";
+    case QLORA_ERR_DEVICE: return "QLORA_ERR_DEVICE: no gfx950 device current";
+    case QLORA_ERR_LAUNCH: return "QLORA_ERR_LAUNCH: kernel launch failed";
+  }
+  return "QLORA_ERR_UNKNOWN";
+}
+
+size_t qlora_workspace_size(int32_t op, int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
+  if (M < 0 || n_out <= 0 || k_in <= 0 || r < 1 || r > QLORA_MAX_RANK) return 0;
+  if (op == 0) return fwd_ws(M, n_out, k_in, r).total;
+  if (op == 1) return bwd_ws(M, n_out, k_in, r).total;
+  return 0;
+}
+
+qlora_status qlora_quantize_nf4(const float* w, int64_t n, int32_t blocksize, uint8_t* packed,
+                                float* absmax, void* stream) {
+  QCHECK(n >= 0, QLORA_ERR_SHAPE);
+  QCHECK(blocksize == QLORA_BLOCKSIZE, QLORA_ERR_UNSUPPORTED);
+  if (n == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(w);
+  ALIGNED_OR_NULL(packed);
+  ALIGNED_OR_NULL(absmax);
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  const int64_t nb = ceil_div(n, 64);
+  const int64_t threads = nb * 4;
+  QCHECK(ceil_div(threads, 256) <= 0x7fffffff, QLORA_ERR_SHAPE);
+  hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0,
+                     as_stream(stream), w, n, nb, packed, absmax);
+  return launched();
+}
+
+qlora_status qlora_double_quant(const float* absmax, int64_t nblocks, int32_t group,
+                                int8_t* qabsmax, float* c2, void* stream) {
+  QCHECK(nblocks >= 0, QLORA_ERR_SHAPE);
+  QCHECK(group == QLORA_DQ_GROUP, QLORA_ERR_UNSUPPORTED);
+  if (nblocks == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(absmax);
+  ALIGNED_OR_NULL(qabsmax);
+  ALIGNED_OR_NULL(c2);
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  const int64_t ng = ceil_div(nblocks, 256);
+  QCHECK(ng <= 0x7fffffff, QLORA_ERR_SHAPE);
+  hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ng), dim3(256), 0, as_stream(stream),
+                     absmax, nblocks, qabsmax, c2);
+  return launched();
+}
+
+qlora_status qlora_quantize_nf4_dq(const float* w, int64_t n, uint8_t* packed, int8_t* qabsmax,
+                                   float* c2, float* absmax, void* stream) {
+  QCHECK(n >= 0, QLORA_ERR_SHAPE);
+  if (n == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(w);
+  ALIGNED_OR_NULL(packed);
+  ALIGNED_OR_NULL(qabsmax);
+  ALIGNED_OR_NULL(c2);
+  QCHECK(absmax == nullptr || aligned16(absmax), QLORA_ERR_ALIGN);
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  const int64_t nb = ceil_div(n, 64);
+  const int64_t ng = ceil_div(nb, 256);
+  QCHECK(ng <= 0x7fffffff, QLORA_ERR_SHAPE);
+  hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)ng), dim3(256), 0, as_stream(stream),
+                     w, n, nb, packed, qabsmax, c2, absmax);
+  return launched();
+}
+
+qlora_status qlora_dequantize_nf4(const qlora_nf4_weight* w, qlora_bf16* out, void* stream) {
+  qlora_status s = validate_weight(w);
+  if (s != QLORA_OK) return s;
+  const int64_t n = w->n_out * w->k_in;
+  QCHECK(n % 64 == 0, QLORA_ERR_SHAPE);
+  if (n == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(out);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  const int64_t ndw = n / 8;
+  hipLaunchKernelGGL(dequantize_nf4_kernel, dim3(grid_for(ndw, 256, 1 << 20)), dim3(256), 0,
+                     as_stream(stream), reinterpret_cast<const uint32_t*>(w->packed), w->qabsmax,
+                     w->c2, ndw, reinterpret_cast<u32x4*>(out));
+  return launched();
+}
+
+qlora_status qlora_lora_down(const qlora_bf16* X, int64_t M, int64_t k_in, const qlora_bf16* A,
+                             int32_t r, qlora_bf16* U, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  QCHECK(M >= 0 && k_in > 0 && k_in % 64 == 0, QLORA_ERR_SHAPE);
+  QCHECK(r >= 1 && r <= QLORA_MAX_RANK, QLORA_ERR_UNSUPPORTED);
+  if (M == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(X);
+  ALIGNED_OR_NULL(A);
+  ALIGNED_OR_NULL(U);
+  // the forward's layout, with n_out taken as 8 (only the U region is used)
+  const FwdWs L = fwd_ws(M, 8, k_in, r);
+  QCHECK(workspace != nullptr && aligned16(workspace), QLORA_ERR_WORKSPACE);
+  QCHECK(ws_bytes >= L.u_part + align256((size_t)L.pu.nsplit * M * L.pu.tiles_n * SK_NT * 4),
+         QLORA_ERR_WORKSPACE);
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  return lora_down_impl(X, M, k_in, A, r, U, nullptr, 0, static_cast<char*>(workspace), L,
+                        as_stream(stream));
+}
+
+qlora_status qlora_nf4_matmul_fwd(const qlora_nf4_weight* w, const qlora_bf16* X, int64_t M,
+                                  const qlora_bf16* U, const qlora_bf16* B, int32_t r, float alpha,
+                                  qlora_bf16* Y, void* workspace, size_t ws_bytes, void* stream) {
+  qlora_status s = validate_linear(w, M, r);
+  if (s != QLORA_OK) return s;
+  if (M == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(X);
+  ALIGNED_OR_NULL(U);
+  ALIGNED_OR_NULL(B);
+  ALIGNED_OR_NULL(Y);
+  const FwdWs L = fwd_ws(M, w->n_out, w->k_in, r);
+  QCHECK(workspace != nullptr && aligned16(workspace) && ws_bytes >= L.total, QLORA_ERR_WORKSPACE);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = as_stream(stream);
+  const uint16_t* up = U;
+  const uint16_t* bp = B;
+  int64_t ld = r;
+  if (r % 8 != 0) {
+    uint16_t* Up = reinterpret_cast<uint16_t*>(ws + L.pad_u);
+    uint16_t* Bp = reinterpret_cast<uint16_t*>(ws + L.pad_b);
+    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(M * L.rp)), dim3(256), 0, st, U, (int64_t)r,
+                       M, (int64_t)r, L.rp, Up, L.rp);
+    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(w->n_out * L.rp)), dim3(256), 0, st, B,
+                       (int64_t)r, w->n_out, (int64_t)r, L.rp, Bp, L.rp);
+    if ((s = launched()) != QLORA_OK) return s;
+    up = Up;
+    bp = Bp;
+    ld = L.rp;
+  }
+  return matmul_fwd_impl(w, X, M, up, ld, bp, ld, r, scale_of(alpha, r), Y, ws, L, st);
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const qlora_bf16* X, int64_t M,
+                              const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
+                              qlora_bf16* Y, qlora_bf16* U, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  qlora_status s = validate_linear(w, M, r);
+  if (s != QLORA_OK) return s;
+  if (M == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(X);
+  ALIGNED_OR_NULL(A);
+  ALIGNED_OR_NULL(B);
+  ALIGNED_OR_NULL(Y);
+  ALIGNED_OR_NULL(U);
+  const FwdWs L = fwd_ws(M, w->n_out, w->k_in, r);
+  QCHECK(workspace != nullptr && aligned16(workspace) && ws_bytes >= L.total, QLORA_ERR_WORKSPACE);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = as_stream(stream);
+  const bool pad = r % 8 != 0;
+  uint16_t* Up = pad ? reinterpret_cast<uint16_t*>(ws + L.pad_u) : nullptr;
+  s = lora_down_impl(X, M, w->k_in, A, r, U, Up, L.rp, ws, L, st);
+  if (s != QLORA_OK) return s;
+  const uint16_t* bp = B;
+  if (pad) {
+    uint16_t* Bp = reinterpret_cast<uint16_t*>(ws + L.pad_b);
+    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(w->n_out * L.rp)), dim3(256), 0, st, B,
+                       (int64_t)r, w->n_out, (int64_t)r, L.rp, Bp, L.rp);
+    if ((s = launched()) != QLORA_OK) return s;
+    bp = Bp;
+  }
+  return matmul_fwd_impl(w, X, M, pad ? Up : U, pad ? L.rp : r, bp, pad ? L.rp : r, r,
+                         scale_of(alpha, r), Y, ws, L, st);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const qlora_bf16* X, const qlora_bf16* dY,
+                              int64_t M, const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                              float alpha, const qlora_bf16* U, qlora_bf16* dX, float* dA,
+                              float* dB, void* workspace, size_t ws_bytes, void* stream) {
+  qlora_status s = validate_linear(w, M, r);
+  if (s != QLORA_OK) return s;
+  ALIGNED_OR_NULL(A);
+  ALIGNED_OR_NULL(B);
+  ALIGNED_OR_NULL(dA);
+  ALIGNED_OR_NULL(dB);
+  if (M > 0) {
+    ALIGNED_OR_NULL(X);
+    ALIGNED_OR_NULL(dY);
+    ALIGNED_OR_NULL(U);
+    ALIGNED_OR_NULL(dX);
+  }
+  const int64_t N = w->n_out, K = w->k_in;
+  const BwdWs L = bwd_ws(M, N, K, r);
+  QCHECK(workspace != nullptr && aligned16(workspace) && ws_bytes >= L.total, QLORA_ERR_WORKSPACE);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = as_stream(stream);
+  const float sc = scale_of(alpha, r);
+
+  if (M == 0) {  // no tokens: the adapter gradients are zero
+    s = run_reduce(nullptr, 0, 0, 0, 0, (int64_t)r, K, 0, 0.0f, ReduceOut{nullptr, dA, K, 0},
+                   kNoOut, st);
+    if (s != QLORA_OK) return s;
+    return run_reduce(nullptr, 0, 0, 0, 0, N, (int64_t)r, 0, 0.0f,
+                      ReduceOut{nullptr, dB, (int64_t)r, 0}, kNoOut, st);
+  }
+
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + L.bt);  // [r][N]
+  uint16_t* V = reinterpret_cast<uint16_t*>(ws + L.v);    // [M][rp]
+  uint16_t* Vt = reinterpret_cast<uint16_t*>(ws + L.vt);  // [r][Mp]
+  uint16_t* Ut = reinterpret_cast<uint16_t*>(ws + L.ut);  // [r][Mp]
+  uint16_t* At = reinterpret_cast<uint16_t*>(ws + L.at);  // [K][rp]
+  float* part = reinterpret_cast<float*>(ws + L.part);
+
+  // adapter factors in the layouts the GEMMs read
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(grid_for(N * (int64_t)r)), dim3(256), 0, st, B,
+                     (int64_t)r, N, (int64_t)r, N, (int64_t)r, Bt, N);
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(grid_for(M * (int64_t)r)), dim3(256), 0, st, U,
+                     (int64_t)r, M, (int64_t)r, L.Mp, (int64_t)r, Ut, L.Mp);
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(grid_for(K * L.rp)), dim3(256), 0, st, A, K,
+                     (int64_t)r, K, L.rp, K, At, L.rp);
+  if ((s = launched()) != QLORA_OK) return s;
+
+  // V = dY·B  -> V [M][rp] (zero-padded) and Vᵀ [r][Mp] (zero-padded), bf16
+  {
+    GemmArgs g{};
+    g.a = dY; g.lda = N; g.rows = M; g.cols = r; g.red = N;
+    g.b = Bt; g.ldb = N;
+    g.out_f32 = part;
+    g.ldo = (int64_t)L.pv.tiles_n * SK_NT;
+    g.part_stride = M * g.ldo;
+    if ((s = run_gemm<SK_MT, SK_NT, 4, 1, B_BF16_CR, false, O_F32>(g, L.pv, st)) != QLORA_OK)
+      return s;
+    if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, L.rp, g.ldo, 1.0f,
+                        ReduceOut{V, nullptr, L.rp, 0}, kNoOut, st)) != QLORA_OK)
+      return s;
+    // Vᵀ from the same partials: rows_pad = Mp pads the token axis with zeros
+    if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, L.Mp, r, g.ldo, 1.0f,
+                        ReduceOut{Vt, nullptr, L.Mp, 1}, kNoOut, st)) != QLORA_OK)
+      return s;
+  }
+
+  // dX = dY·Ŵ + s·V·A
+  {
+    GemmArgs g{};
+    g.a = dY; g.lda = N; g.rows = M; g.cols = K; g.red = N;
+    g.packed = w->packed; g.qabsmax = w->qabsmax; g.c2 = w->c2; g.w_kin = K;
+    g.pl = V; g.ldpl = L.rp; g.pr = At; g.ldpr = L.rp; g.rl = r; g.s = sc;
+    if (use_big(M)) {
+      g.out_bf16 = dX; g.ldo = K;
+      s = run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_RED, true, O_BF16>(
+          g, plan(M, K, N, BIG_MT, BIG_NT, false), st);
+      if (s != QLORA_OK) return s;
+    } else {
+      g.out_f32 = part; g.ldo = K; g.part_stride = M * K;
+      if ((s = run_gemm<SM_MT, SM_NT, 1, 4, B_NF4_RED, true, O_F32>(g, L.pdx, st)) != QLORA_OK)
+        return s;
+      if ((s = run_reduce(part, g.part_stride, L.pdx.nsplit, M, K, M, K, K, 1.0f,
+                          ReduceOut{dX, nullptr, K, 0}, kNoOut, st)) != QLORA_OK)
+        return s;
+    }
+  }
+
+  // dA = s·Vᵀ·X   [r][K]
+  {
+    GemmArgs g{};
+    g.a = Vt; g.lda = L.Mp; g.rows = r; g.cols = K; g.red = M;
+    g.b = X; g.ldb = K;
+    g.out_f32 = part; g.ldo = K; g.part_stride = (int64_t)r * K;
+    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pda, st)) != QLORA_OK)
+      return s;
+    if ((s = run_reduce(part, g.part_stride, L.pda.nsplit, r, K, r, K, K, sc,
+                        ReduceOut{nullptr, dA, K, 0}, kNoOut, st)) != QLORA_OK)
+      return s;
+  }
+
+  // dB = s·dYᵀ·U  computed as (s·Uᵀ·dY)ᵀ: rows j, cols n, written transposed into [N][r]
+  {
+    GemmArgs g{};
+    g.a = Ut; g.lda = L.Mp; g.rows = r; g.cols = N; g.red = M;
+    g.b = dY; g.ldb = N;
+    g.out_f32 = part; g.ldo = N; g.part_stride = (int64_t)r * N;
+    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pdb, st)) != QLORA_OK)
+      return s;
+    if ((s = run_reduce(part, g.part_stride, L.pdb.nsplit, r, N, r, N, N, sc,
+                        ReduceOut{nullptr, dB, (int64_t)r, 1}, kNoOut, st)) != QLORA_OK)
+      return s;
+  }
+  return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Kernel declarations and argument structs shared by the kernel sources and
+// the host-side entry points.
+#pragma once
+
+#include "qlora_common.h"
+
+namespace qlora {
+
+enum BMode { B_NF4_COLS = 0, B_NF4_RED = 1, B_BF16_CR = 2, B_BF16_RC = 3 };
+enum OMode { O_BF16 = 0, O_F32 = 1 };
+
+struct GemmArgs {
+  const uint16_t* a;  // [rows][lda], reduction contiguous
+  int64_t lda;
+  int64_t rows, cols, red;  // valid extents (red % 8 == 0)
+  const uint16_t* b;        // bf16 modes
+  int64_t ldb;
+  const uint8_t* packed;  // NF4 modes: W[n_out][k_in]
+  const int8_t* qabsmax;
+  const float* c2;
+  int64_t w_kin;       // k_in of W (row pitch in elements)
+  const uint16_t* pl;  // prologue: s · pl[rows][rl] · pr[cols][rl]ᵀ (pitches % 8 == 0)
+  int64_t ldpl;
+  const uint16_t* pr;
+  int64_t ldpr;
+  int32_t rl;
+  float s;
+  uint16_t* out_bf16;  // O_BF16: [rows][ldo]
+  float* out_f32;      // O_F32: [split][rows][ldo] partial sums
+  int64_t ldo;
+  int64_t part_stride;
+  int32_t tiles_m, tiles_n;
+  int32_t kt_per_split;
+};
+
+struct ReduceOut {
+  uint16_t* bf16;  // bf16 output or nullptr
+  float* f32;      // float32 output or nullptr
+  int64_t ld;
+  int32_t transposed;  // write out[col][row] instead of out[row][col]
+};
+
+template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE>
+__global__ void gemm_kernel(GemmArgs g);
+
+__global__ void quantize_nf4_kernel(const float* w, int64_t n, int64_t nblocks, uint8_t* packed,
+                                    float* absmax);
+__global__ void double_quant_kernel(const float* absmax, int64_t nblocks, int8_t* qabsmax,
+                                    float* c2);
+__global__ void quantize_nf4_dq_kernel(const float* w, int64_t n, int64_t nblocks, uint8_t* packed,
+                                       int8_t* qabsmax, float* c2, float* absmax_out);
+__global__ void dequantize_nf4_kernel(const uint32_t* packed, const int8_t* qabsmax, const float* c2,
+                                      int64_t ndwords, u32x4* out);
+__global__ void reduce_partials_kernel(const float* part, int64_t part_stride, int32_t nsplit,
+                                       int64_t rows, int64_t cols, int64_t rows_pad,
+                                       int64_t cols_pad, int64_t ldp, float scale, ReduceOut o0,
+                                       ReduceOut o1);
+__global__ void transpose_pad_kernel(const uint16_t* in, int64_t ldi, int64_t R, int64_t C,
+                                     int64_t Rp, int64_t Cp, uint16_t* out, int64_t ldo);
+__global__ void pad_cols_kernel(const uint16_t* in, int64_t ldi, int64_t R, int64_t C, int64_t Cp,
+                                uint16_t* out, int64_t ldo);
+
+}  // namespace qlora

@@ -1,0 +1,228 @@
+// NF4 blockwise quantisation, Double Quantization and dequantisation for gfx950.
+//
+// Method ("QLoRAの理論と実装", disassemble-channel.com, §5-1 NF4 process steps
+// 1-3, §5-2 Double Quantization; Qiita explainer, DQ formula
+// W ≈ (c2 · c1^quant) · W^quant):
+//   absmax_b = max |w| over 64 consecutive elements (zero-padded tail)
+//   idx      = nearest of the 16 NF4 levels to w / absmax_b (tie -> lower index)
+//   c2_g     = RN32(max absmax over 256 blocks / 127), q_b = nearest int to absmax_b / c2_g
+//   ŵ        = RNE_bf16(RN32(c_idx · RN32(c2_g · q_b)))
+//
+// Exact decisions without a per-element division: for a > 0 and the level
+// midpoints m_i (i = 0..14), "w / a > m_i" is equivalent to "w > T_i" with
+// T_i = RD32(m_i · a): m_i · a is exact in float64 and, w being a float32,
+// w exceeds the real product exactly when it exceeds the largest float32 not
+// above it.  idx = #{i : w > T_i}, ties at a midpoint go to the lower index.
+//
+// These kernels are HBM-bound: 4 B read + 0.5 B written per weight for the
+// quantiser, 0.52 B read + 2 B written per weight for the dequantiser.
+
+#include "qlora_kernels.h"
+
+namespace qlora {
+
+namespace {
+
+struct Midpoints {
+  double m[15];
+};
+
+constexpr Midpoints make_midpoints() {
+  Midpoints r{};
+  for (int i = 0; i < 15; ++i)
+    r.m[i] = ((double)__builtin_bit_cast(float, kNF4Bits[i]) +
+              (double)__builtin_bit_cast(float, kNF4Bits[i + 1])) * 0.5;
+  return r;
+}
+
+constexpr Midpoints kMid = make_midpoints();
+
+// RD32(m * a): the largest float32 not above the exact product.
+__device__ inline float rd32_mul(double m, float a) {
+  const double p = m * (double)a;  // exact: m has <= 29 significant bits, a 24
+  float f = (float)p;              // round to nearest
+  if ((double)f > p) {
+    uint32_t b = float_to_bits(f);
+    if (f > 0.0f)
+      b -= 1u;                                          // toward zero
+    else
+      b = ((b & 0x7fffffffu) == 0u) ? 0x80000001u : b + 1u;  // away from zero (negative side)
+    f = bits_to_float(b);
+  }
+  return f;
+}
+
+__device__ inline uint32_t nf4_index(float w, const float (&T)[15]) {
+  uint32_t idx = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) idx += (w > T[i]) ? 1u : 0u;
+  return idx;
+}
+
+// Second-level code: integer in [0, 127] nearest to a / step, tie to the lower.
+__device__ inline int dq_code(float a, float step) {
+  if (!(step > 0.0f)) return 0;
+  const double s = (double)step, ad = (double)a;
+  int q = (int)rint(ad / s);
+  q = q < 0 ? 0 : (q > 127 ? 127 : q);
+  // (q ± 1/2) · s is exact in float64; one step each way fixes any rounding of ad / s.
+  if (q < 127 && ad > ((double)q + 0.5) * s) ++q;
+  if (q > 0 && ad <= ((double)q - 0.5) * s) --q;
+  return q;
+}
+
+__device__ inline float dq_step(float gmax) {
+  // IEEE float32 division max / 127, via float64 (double rounding is harmless
+  // for a quotient of two float32 numbers).
+  return (float)((double)gmax / 127.0);
+}
+
+// One lane handles 16 consecutive elements; 4 lanes form one 64-block.
+// Loads the 16 elements (zero beyond n), returns the block absmax (all 4
+// lanes agree) and the packed 8 bytes of this lane.
+__device__ inline float quantize_16(const float* __restrict__ w, int64_t n, int64_t blk, int sub,
+                                    u32x2& out_bytes) {
+  const int64_t base = blk * kBlock + (int64_t)sub * 16;
+  float v[16];
+  if (base + 16 <= n) {
+    const floatx4* p = reinterpret_cast<const floatx4*>(w + base);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      floatx4 x = __builtin_nontemporal_load(p + j);
+      v[4 * j + 0] = x[0];
+      v[4 * j + 1] = x[1];
+      v[4 * j + 2] = x[2];
+      v[4 * j + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = (base + j < n) ? w[base + j] : 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+
+  uint32_t lo = 0x88888888u, hi = 0x88888888u;  // all-zero block: every index 8
+  if (m > 0.0f) {
+    float T[15];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) T[i] = rd32_mul(kMid.m[i], m);
+    lo = 0u;
+    hi = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lo |= nf4_index(v[j], T) << (4 * j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hi |= nf4_index(v[8 + j], T) << (4 * j);
+  }
+  out_bytes = u32x2{lo, hi};
+  return m;
+}
+
+}  // namespace
+
+// packed[nblocks*32], absmax[nblocks]; 64 blocks per 256-thread workgroup.
+__global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ w, int64_t n,
+                                                           int64_t nblocks,
+                                                           uint8_t* __restrict__ packed,
+                                                           float* __restrict__ absmax) {
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t blk = gt >> 2;
+  const int sub = (int)(gt & 3);
+  if (blk >= nblocks) return;  // the 4 lanes of a block leave together
+  u32x2 bytes;
+  const float m = quantize_16(w, n, blk, sub, bytes);
+  *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
+  if (sub == 0) absmax[blk] = m;
+}
+
+// One workgroup per group of 256 blocks.
+__global__ __launch_bounds__(256) void double_quant_kernel(const float* __restrict__ absmax,
+                                                           int64_t nblocks,
+                                                           int8_t* __restrict__ qabsmax,
+                                                           float* __restrict__ c2) {
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int64_t b = (int64_t)blockIdx.x * kGroup + t;
+  const float a = (b < nblocks) ? absmax[b] : 0.0f;
+  float m = a;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float step = dq_step(m);
+  if (t == 0) c2[blockIdx.x] = step;
+  if (b < nblocks) qabsmax[b] = (int8_t)dq_code(a, step);
+}
+
+// Fused: one workgroup per DQ group (256 blocks = 16384 elements), four passes
+// of 64 blocks, then the second level from the absmax values kept in LDS.
+__global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __restrict__ w, int64_t n,
+                                                              int64_t nblocks,
+                                                              uint8_t* __restrict__ packed,
+                                                              int8_t* __restrict__ qabsmax,
+                                                              float* __restrict__ c2,
+                                                              float* __restrict__ absmax_out) {
+  __shared__ float amax[kGroup];
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  const int sub = t & 3;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int lb = pass * 64 + (t >> 2);
+    const int64_t blk = g * kGroup + lb;
+    float m = 0.0f;
+    if (blk < nblocks) {
+      u32x2 bytes;
+      m = quantize_16(w, n, blk, sub, bytes);
+      *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
+    }
+    if (sub == 0) amax[lb] = m;
+  }
+  __syncthreads();
+  const int64_t b = g * kGroup + t;
+  const float a = amax[t];
+  float m = a;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float step = dq_step(m);
+  if (t == 0) c2[g] = step;
+  if (b < nblocks) {
+    qabsmax[b] = (int8_t)dq_code(a, step);
+    if (absmax_out) absmax_out[b] = a;
+  }
+}
+
+// Standalone dequantisation to bf16: one packed dword (8 weights) per thread,
+// a 16-byte store.  n is a multiple of 64.
+__global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __restrict__ packed,
+                                                             const int8_t* __restrict__ qabsmax,
+                                                             const float* __restrict__ c2,
+                                                             int64_t ndwords,
+                                                             u32x4* __restrict__ out) {
+  __shared__ float cb[16];
+  if (threadIdx.x < 16) cb[threadIdx.x] = bits_to_float(kNF4Bits[threadIdx.x]);
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < ndwords; i += stride) {
+    const uint32_t p = __builtin_nontemporal_load(packed + i);
+    const int64_t b = i >> 3;  // 8 dwords per 64-block
+    const float ah = c2[b >> 8] * (float)qabsmax[b];
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float lo = cb[(p >> (8 * d)) & 15u] * ah;
+      const float hi = cb[(p >> (8 * d + 4)) & 15u] * ah;
+      o[d] = pack_bf16x2(lo, hi);
+    }
+    __builtin_nontemporal_store(o, out + i);
+  }
+}
+
+}  // namespace qlora

@@ -1,0 +1,168 @@
+/*
+ * qlora.h — C ABI of the MI355X (gfx950) QLoRA NF4 linear library (libqlora.so).
+ *
+ * What the library computes, and where it is defined:
+ *   * NF4 blockwise quantisation of a float32 weight: blocks of 64 consecutive
+ *     elements scaled by their absolute maximum, each element replaced by the
+ *     index of the nearest of 16 NormalFloat levels ("QLoRAの理論と実装",
+ *     disassemble-channel.com, §5-1 NF4: construction, and the three-step
+ *     quantise / dequantise process).
+ *   * Double Quantization of the per-block float32 absmax values: 8-bit codes in
+ *     groups of 256 blocks with one float32 second-level constant per group
+ *     (same page, §5-2 Double Quantization), dequantised in the order
+ *     W ≈ (c2 · c1^quant) · W^quant (Qiita explainer, "Double Quantization の仕組み").
+ *   * The QLoRA linear: Y = dequant(W_NF4)·X + (α/r)·B·(A·X), the 4-bit weight
+ *     decoded to BF16 right before the matmul (same page, "QLoRAの計算フロー";
+ *     Qiita explainer, storage/compute split), and its backward: gradients for
+ *     A and B only ("逆伝播と勾配の流れ") plus the input gradient through the
+ *     frozen weight (arXiv 2305.14314 summary, papers.plutine.com).
+ *
+ * Conventions (every entry point):
+ *   * Pointers are DEVICE pointers unless marked (host).  Every device pointer
+ *     must be 16-byte aligned.  The caller owns every buffer; the library never
+ *     allocates, frees or keeps a pointer past the call.
+ *   * `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; no call synchronises.
+ *   * Arguments are validated on the host before anything is enqueued.  On any
+ *     error status nothing is launched and no output is touched.  A failed
+ *     launch returns QLORA_ERR_LAUNCH.  Faults during execution surface at the
+ *     caller's next synchronisation of the stream.
+ *   * Inputs must be finite; non-finite input gives unspecified output.
+ *   * bf16 tensors are passed as raw 16-bit patterns (qlora_bf16).
+ *   * Weight layout: W is [n_out][k_in] row-major (the layer computes
+ *     Y = X·Wᵀ with tokens as rows); quantisation blocks run along k_in.
+ *   * Calls are reentrant; concurrent calls on different streams are safe.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_ABI_VERSION 1
+#define QLORA_BLOCKSIZE 64   /* first-level block (NF4), elements */
+#define QLORA_DQ_GROUP 256   /* second-level group, blocks */
+#define QLORA_MAX_RANK 256
+
+typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = 1,        /* a required pointer is NULL */
+  QLORA_ERR_SHAPE = 2,       /* a size is negative, out of range or not a required multiple */
+  QLORA_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
+  QLORA_ERR_UNSUPPORTED = 4, /* blocksize != 64, group != 256, r outside [1, 256] */
+  QLORA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than qlora_workspace_size() */
+  QLORA_ERR_DEVICE = 6,      /* no device, or the current device is not gfx950 */
+  QLORA_ERR_LAUNCH = 7       /* a kernel launch failed */
+} qlora_status;
+
+/* Non-owning view of one frozen NF4 + Double-Quantized weight W[n_out][k_in].
+ *   packed  : n_out*k_in/2 bytes; byte t = idx[2t] | idx[2t+1] << 4 (flat order)
+ *   qabsmax : n_out*k_in/64 second-level codes, values in [0, 127]
+ *   c2      : ceil(n_out*k_in/64/256) float32 second-level constants
+ *   k_in % 64 == 0 and n_out % 8 == 0 for the linear entry points. */
+typedef struct {
+  const uint8_t *packed;
+  const int8_t *qabsmax;
+  const float *c2;
+  int64_t n_out;
+  int64_t k_in;
+} qlora_nf4_weight;
+
+/* ---- quantisation ------------------------------------------------------- */
+
+/* First level ("QLoRAの理論と実装", §5-1, steps 1 and 2).  For each block of 64
+ * consecutive elements of the flat w[0..n) (the tail zero-padded):
+ *   absmax[b] = max |w| over the block (exact);
+ *   idx       = nearest NF4 level to the exact quotient w / absmax[b], a tie
+ *               going to the lower index; an all-zero block and every padded
+ *               slot get index 8 (the exact-zero level).
+ * Outputs: packed[ceil(n/64)*32] bytes (two indices per byte, even element in
+ * the low nibble) and absmax[ceil(n/64)] float32.  n >= 0; blocksize must be 64. */
+qlora_status qlora_quantize_nf4(const float *w, int64_t n, int32_t blocksize, uint8_t *packed,
+                                float *absmax, void *stream);
+
+/* Second level ("QLoRAの理論と実装", §5-2; Qiita explainer, DQ formula).  Groups of
+ * 256 consecutive blocks (the last may be short):
+ *   c2[g]    = RN32(max absmax over the group / 127)   (IEEE float32 division)
+ *   qabsmax  = integer in [0, 127] nearest to absmax / c2 (exact, tie to the
+ *              lower integer); 0 when c2 == 0.
+ * Inputs absmax[nblocks] (non-negative); outputs qabsmax[nblocks],
+ * c2[ceil(nblocks/256)].  group must be 256. */
+qlora_status qlora_double_quant(const float *absmax, int64_t nblocks, int32_t group,
+                                int8_t *qabsmax, float *c2, void *stream);
+
+/* Both levels in one pass over w.  Produces exactly the bytes that
+ * qlora_quantize_nf4 followed by qlora_double_quant produce.  absmax may be
+ * NULL (not written). */
+qlora_status qlora_quantize_nf4_dq(const float *w, int64_t n, uint8_t *packed, int8_t *qabsmax,
+                                   float *c2, float *absmax, void *stream);
+
+/* Dequantisation ("QLoRAの理論と実装", §5-1 step 3, in the DQ order):
+ *   â = RN32(c2[b/256] · qabsmax[b]);  out = RNE_bf16(RN32(c[idx] · â)).
+ * out[n_out*k_in] bf16, row-major.  Any n_out, k_in >= 0 with n_out*k_in % 64 == 0. */
+qlora_status qlora_dequantize_nf4(const qlora_nf4_weight *w /* host struct */, qlora_bf16 *out,
+                                  void *stream);
+
+/* ---- QLoRA linear ------------------------------------------------------- */
+
+/* Forward ("QLoRAの理論と実装", QLoRAの計算フロー, steps 1-4), s = RN32(alpha / r):
+ *   U = X·Aᵀ                       (bf16, [M][r], saved for the backward)
+ *   Y = RNE_bf16(X·Ŵᵀ + s·U·Bᵀ)    (fp32 accumulation; Ŵ decoded tile by tile,
+ *                                   never materialised)
+ * X [M][k_in], A [r][k_in], B [n_out][r], Y [M][n_out] bf16.  M >= 0.
+ * workspace: at least qlora_workspace_size(0, M, n_out, k_in, r) bytes. */
+qlora_status qlora_linear_fwd(const qlora_nf4_weight *w /* host struct */, const qlora_bf16 *X,
+                              int64_t M, const qlora_bf16 *A, const qlora_bf16 *B, int32_t r,
+                              float alpha, qlora_bf16 *Y, qlora_bf16 *U, void *workspace,
+                              size_t ws_bytes, void *stream);
+
+/* Backward ("QLoRAの理論と実装", 逆伝播と勾配の流れ; arXiv 2305.14314 summary):
+ *   V  = dY·B
+ *   dX = RNE_bf16(dY·Ŵ + s·V·A)   bf16 [M][k_in]
+ *   dA = s·Vᵀ·X                    fp32 [r][k_in]
+ *   dB = s·dYᵀ·U                   fp32 [n_out][r]   (U as saved by the forward)
+ * No gradient for the frozen weight.  workspace: at least
+ * qlora_workspace_size(1, M, n_out, k_in, r) bytes. */
+qlora_status qlora_linear_bwd(const qlora_nf4_weight *w /* host struct */, const qlora_bf16 *X,
+                              const qlora_bf16 *dY, int64_t M, const qlora_bf16 *A,
+                              const qlora_bf16 *B, int32_t r, float alpha, const qlora_bf16 *U,
+                              qlora_bf16 *dX, float *dA, float *dB, void *workspace,
+                              size_t ws_bytes, void *stream);
+
+/* The forward's two launches, callable on their own (the forward is exactly
+ * qlora_lora_down then qlora_nf4_matmul_fwd):
+ *   qlora_lora_down:      U = X·Aᵀ, bf16 [M][r]
+ *   qlora_nf4_matmul_fwd: Y = RNE_bf16(X·Ŵᵀ + s·U·Bᵀ)
+ * Same shapes, preconditions and workspace as qlora_linear_fwd. */
+qlora_status qlora_lora_down(const qlora_bf16 *X, int64_t M, int64_t k_in, const qlora_bf16 *A,
+                             int32_t r, qlora_bf16 *U, void *workspace, size_t ws_bytes,
+                             void *stream);
+qlora_status qlora_nf4_matmul_fwd(const qlora_nf4_weight *w /* host struct */,
+                                  const qlora_bf16 *X, int64_t M, const qlora_bf16 *U,
+                                  const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *Y,
+                                  void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of device workspace needed by op 0 (forward, also qlora_lora_down and
+ * qlora_nf4_matmul_fwd) or op 1 (backward).  Returns 0 for an invalid op. */
+size_t qlora_workspace_size(int32_t op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);
+
+/* (host) The 16 float32 NF4 levels the kernels use, ascending. */
+void qlora_nf4_codebook(float out[16]);
+
+/* (host) A static string naming a status. */
+const char *qlora_status_string(qlora_status s);
+
+/* (host) QLORA_ABI_VERSION of the built library. */
+int32_t qlora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

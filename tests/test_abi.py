@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before touching a device."""
+
+import ctypes
+import re
+
+import numpy as np
+import pytest
+
+import bit_nf4_quantized_blockwise_amd as q
+from oracle.codebook import nf4_codebook_f32
+
+OK, NULL, SHAPE, ALIGN, UNSUP, WS, DEV = 0, 1, 2, 3, 4, 5, 6
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+MIS = 0x10002
+
+
+@pytest.fixture(scope="module")
+def L():
+    return q.lib()
+
+
+def _header_functions():
+    txt = open(q.HEADER_PATH).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(q._SIGNATURES), set(names) ^ set(q._SIGNATURES)
+
+
+def test_abi_version_and_strings(L):
+    assert q.abi_version() == 1
+    for s in range(8):
+        assert q.status_string(s).startswith(q.STATUS[s])
+
+
+def test_codebook_matches_oracle_bitwise(L):
+    got = np.array(q.codebook(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), nf4_codebook_f32().view(np.uint32))
+
+
+def test_workspace_size(L):
+    assert q.workspace_size(0, 4096, 11008, 4096, 64) > 0
+    assert q.workspace_size(1, 4096, 11008, 4096, 64) > 0
+    assert q.workspace_size(2, 16, 64, 64, 8) == 0
+    assert q.workspace_size(0, 16, 64, 64, 0) == 0
+    assert q.workspace_size(0, 16, 64, 64, 257) == 0
+    assert q.workspace_size(0, 0, 64, 64, 8) >= 256
+
+
+def test_quantize_argument_errors(L):
+    f = L.qlora_quantize_nf4
+    assert f(FAKE, 100, 32, FAKE, FAKE, None) == UNSUP
+    assert f(FAKE, -1, 64, FAKE, FAKE, None) == SHAPE
+    assert f(None, 100, 64, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 100, 64, None, FAKE, None) == NULL
+    assert f(MIS, 100, 64, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 0, 64, None, None, None) == OK  # nothing to do
+    g = L.qlora_double_quant
+    assert g(FAKE, 10, 128, FAKE, FAKE, None) == UNSUP
+    assert g(FAKE, 10, 256, MIS, FAKE, None) == ALIGN
+    assert g(FAKE, -5, 256, FAKE, FAKE, None) == SHAPE
+    h = L.qlora_quantize_nf4_dq
+    assert h(FAKE, 10, FAKE, FAKE, None, None, None) == NULL
+    assert h(FAKE, 10, FAKE, FAKE, FAKE, MIS, None) == ALIGN
+
+
+def _weight(n_out=64, k_in=128, packed=FAKE):
+    return ctypes.byref(q.NF4Weight(packed, FAKE, FAKE, n_out, k_in))
+
+
+def test_linear_argument_errors(L):
+    f = L.qlora_linear_fwd
+    args = lambda **kw: dict(dict(w=_weight(), X=FAKE, M=16, A=FAKE, B=FAKE, r=8, alpha=16.0,
+                                  Y=FAKE, U=FAKE, ws=FAKE, wsb=1 << 30, st=None), **kw)
+    call = lambda d: f(*d.values())
+    assert call(args(r=0)) == UNSUP
+    assert call(args(r=257)) == UNSUP
+    assert call(args(M=-1)) == SHAPE
+    assert call(args(w=_weight(k_in=100))) == SHAPE
+    assert call(args(w=_weight(n_out=60))) == SHAPE
+    assert call(args(w=_weight(packed=None))) == NULL
+    assert call(args(w=_weight(packed=MIS))) == ALIGN
+    assert call(args(X=None)) == NULL
+    assert call(args(Y=MIS)) == ALIGN
+    assert call(args(ws=None)) == WS
+    assert call(args(wsb=16)) == WS
+    assert f(None, FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, 1 << 30, None) == NULL
+    b = L.qlora_linear_bwd
+    assert b(_weight(), FAKE, FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, None, FAKE,
+             1 << 30, None) == NULL
+    assert b(_weight(), FAKE, FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
+             None) == WS
+    d = L.qlora_dequantize_nf4
+    assert d(ctypes.byref(q.NF4Weight(FAKE, FAKE, FAKE, 3, 5)), FAKE, None) == SHAPE
+    assert d(ctypes.byref(q.NF4Weight(FAKE, FAKE, FAKE, 4, 16)), MIS, None) == ALIGN
+
+
+def test_valid_arguments_without_gpu_report_device(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert L.qlora_quantize_nf4(FAKE, 100, 64, FAKE, FAKE, None) == DEV
+    assert L.qlora_linear_fwd(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, 1 << 30,
+                              None) == DEV

@@ -1,0 +1,169 @@
+"""GPU parity of the quantiser, Double Quantization and dequantiser against the
+oracle: bit-exact on every byte, code and bf16 value."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle.codebook import nf4_codebook_f32, nf4_midpoints_f64
+from oracle.quant import block_absmax, dequantize_nf4, double_quant, quantize_nf4
+
+from support import bf16_bits, f32_bits, guarded, host, oracle_rows, oracle_weight, say, to_dev, u8
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("bit_nf4_quantized_blockwise_amd")
+
+
+def _gpu_all(flat):
+    """Both GPU routes: separate calls and the fused one (must agree bytewise)."""
+    w = to_dev(flat)
+    packed, absmax = q.quantize_nf4(w)
+    qa, c2 = q.double_quant(absmax)
+    fp, fq, fc2, fabs = q.quantize_nf4_dq(w, want_absmax=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(packed), u8(fp))
+    assert np.array_equal(u8(qa), u8(fq))
+    assert np.array_equal(f32_bits(c2), f32_bits(fc2))
+    assert np.array_equal(f32_bits(absmax), f32_bits(fabs))
+    return packed, absmax, qa, c2
+
+
+def _compare(flat, name):
+    say(f"[quant] {name}: n = {flat.size}")
+    packed, absmax, qa, c2 = _gpu_all(flat)
+    op, oa = quantize_nf4(flat)
+    oq, oc2 = double_quant(oa)
+    assert np.array_equal(f32_bits(absmax), oa.view(np.uint32)), "absmax"
+    gp = u8(packed)
+    bad = np.nonzero(gp != op)[0]
+    assert bad.size == 0, f"packed differs at {bad[:8]} ({bad.size} bytes)"
+    assert np.array_equal(u8(qa).view(np.int8), oq), "qabsmax"
+    assert np.array_equal(f32_bits(c2), oc2.view(np.uint32)), "c2"
+    return packed, qa, c2, op, oq, oc2
+
+
+def _blocks_with_scale(a, vals):
+    """Blocks of 64 whose first element is a (so absmax = a) and the rest vals."""
+    vals = np.asarray(vals, np.float32)
+    nb = -(-vals.size // 63)
+    flat = np.zeros(nb * 63, np.float32)
+    flat[:vals.size] = vals
+    blocks = np.zeros((nb, 64), np.float32)
+    blocks[:, 0] = a
+    blocks[:, 1:] = flat.reshape(nb, 63)
+    return blocks.ravel()
+
+
+def test_near_threshold_sweep_random_scales():
+    rng = np.random.default_rng(101)
+    mids = nf4_midpoints_f64()
+    parts = []
+    for a in rng.uniform(1e-4, 0.3, 600).astype(np.float32):
+        vals = []
+        for m in mids:
+            t = np.float32(m * float(a))
+            for k in range(-3, 4):
+                v = t
+                step = np.float32(np.inf) if k > 0 else np.float32(-np.inf)
+                for _ in range(abs(k)):
+                    v = np.nextafter(v, step)
+                vals.append(v)
+        parts.append(_blocks_with_scale(a, vals))
+    flat = np.concatenate(parts)
+    _compare(flat, "midpoints ± 3 ulp, 600 random scales")
+
+
+def test_unit_scale_dense_sweep_and_exact_ties():
+    mids = nf4_midpoints_f64()
+    vals = []
+    for m in mids:
+        base = np.float32(m)
+        bits = base.view(np.uint32)
+        # 4001 consecutive float32 values centred on the midpoint
+        off = np.arange(-2000, 2001, dtype=np.int64)
+        cand = (np.int64(bits) + off).astype(np.uint32).view(np.float32)
+        vals.append(cand)
+    rng = np.random.default_rng(102)
+    vals.append(rng.uniform(-1, 1, 400_000).astype(np.float32))
+    v = np.concatenate(vals)
+    v = v[np.abs(v) <= 1.0]
+    _compare(_blocks_with_scale(np.float32(1.0), v), "unit scale dense sweep")
+
+
+def test_random_weights_edge_blocks_ragged():
+    rng = np.random.default_rng(103)
+    n = 64 * 3000 + 37
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    w[rng.random(n) < 1e-3] = np.float32(0.16)
+    w[64 * 5:64 * 6] = 0.0                       # an all-zero block
+    w[64 * 7:64 * 8] = -0.0                      # negative zeros
+    w[64 * 9:64 * 10] *= np.float32(1e-36)       # tiny (subnormal products)
+    w[64 * 11:64 * 12] = np.float32(3e-41)       # subnormal inputs
+    w[64 * 13] = np.float32(-0.5)                # negative absmax
+    w[64 * 256 * 2:64 * 256 * 3] = 0.0          # an all-zero DQ group (c2 = 0)
+    packed, qa, c2, op, oq, oc2 = _compare(w, "random N(0, 0.02) with edge blocks")
+    # dequantiser: bf16 bit-exact (n must be a multiple of 64: drop the tail)
+    m = (n // 64) * 64
+    wq = q.NF4Tensor(packed, qa, c2, m // 64, 64)
+    out, check = guarded((m // 64, 64), torch.bfloat16, 7.0)
+    q.dequantize_nf4(wq, out=out)
+    ref = dequantize_nf4(op, oq, oc2, m)
+    assert np.array_equal(bf16_bits(out).ravel(), ref)
+    check()
+
+
+@pytest.mark.parametrize("n", [0, 1, 63, 64, 65, 16384, 16385])
+def test_small_and_empty_sizes(n):
+    rng = np.random.default_rng(104 + n)
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    if n == 0:
+        wt = torch.zeros(0, dtype=torch.float32, device="cuda")
+        p, a = q.quantize_nf4(wt)
+        qa, c2 = q.double_quant(a)
+        torch.cuda.synchronize()
+        assert p.numel() == 0 and qa.numel() == 0 and c2.numel() == 0
+        return
+    _compare(w, f"n = {n}")
+
+
+def test_single_linear_weight_full():
+    W = wl.SINGLE_LINEAR.inputs()["W"]
+    packed, qa, c2, op, oq, oc2 = _compare(W.ravel(), "single linear 4096x4096")
+    wq = q.NF4Tensor(packed, qa, c2, 4096, 4096)
+    out = q.dequantize_nf4(wq)
+    ref = dequantize_nf4(op, oq, oc2, W.size)
+    assert np.array_equal(bf16_bits(out).ravel(), ref)
+
+
+@pytest.mark.parametrize("matrix", [0, 4, 6])  # q 4096x4096, gate 4096->11008, down 11008->4096
+def test_llama7b_shapes_full(matrix):
+    W = wl.llama7b_weight(0, matrix)
+    say(f"[quant] llama7b layer 0 matrix {matrix}: {W.shape}")
+    wt = to_dev(W)
+    wq = q.quantize_weight(wt)
+    out = q.dequantize_nf4(wq)
+    o = oracle_weight(W)
+    assert np.array_equal(u8(wq.packed), o["packed"])
+    assert np.array_equal(u8(wq.qabsmax).view(np.int8), o["q"])
+    assert np.array_equal(f32_bits(wq.c2), o["c2"].view(np.uint32))
+    assert np.array_equal(bf16_bits(out), o["w_hat"])
+
+
+def test_llama7b_last_layer_sampled_groups():
+    """Another layer's matrices at full size, checked on sampled DQ groups."""
+    for matrix in range(7):
+        W = wl.llama7b_weight(31, matrix)
+        n_out, k_in = W.shape
+        wq = q.quantize_weight(to_dev(W))
+        out = q.dequantize_nf4(wq)
+        pk, qq, cc, ww = u8(wq.packed), u8(wq.qabsmax).view(np.int8), f32_bits(wq.c2), bf16_bits(out)
+        rng = np.random.default_rng(105 + matrix)
+        for r0 in rng.integers(0, n_out - 8, 3):
+            o = oracle_rows(W, int(r0), int(r0) + 8)
+            e0 = int(r0) * k_in
+            assert np.array_equal(pk[e0 // 2:e0 // 2 + o["packed"].size], o["packed"])
+            assert np.array_equal(qq[e0 // 64:e0 // 64 + o["q"].size], o["q"])
+            assert np.array_equal(cc[o["g0"]:o["g1"]], o["c2"].view(np.uint32))
+            assert np.array_equal(ww[int(r0):int(r0) + 8], o["w_hat"])
