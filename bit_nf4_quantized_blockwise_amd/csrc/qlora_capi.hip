@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstring>
 
 #include "qlora_kernels.h"
@@ -80,8 +81,28 @@ constexpr int SM_MT = 64, SM_NT = 256;      // NF4 GEMMs, few tokens (split-K)
 constexpr int SK_MT = 128, SK_NT = 64;      // skinny: U = X·Aᵀ, V = dY·B
 constexpr int TR_MT = 64, TR_NT = 256;      // token-reduction: dA, dB
 constexpr int64_t kBigM = 128;              // use the big tiles from this many tokens on
+constexpr int64_t kFewM = 16;               // up to this many tokens: the streaming GEMV
 
 bool use_big(int64_t M) { return M >= kBigM; }
+bool use_gemv(int64_t M) { return M <= kFewM; }
+
+struct GemvPlan {
+  int cpw, mg, ksplit, gx;
+};
+
+// 8 waves per workgroup, each wave CPW chunks of 128 k; tokens in groups of 8.
+GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K) {
+  GemvPlan p;
+  p.mg = M <= 8 ? 1 : 2;
+  const int64_t nch = ceil_div(K, 128);
+  const int64_t need = ceil_div(nch, 8);
+  const int cap = 8 / p.mg;
+  p.cpw = 1;
+  while (p.cpw < need && p.cpw < cap) p.cpw *= 2;
+  p.ksplit = (int)ceil_div(nch, 8 * (int64_t)p.cpw);
+  p.gx = (int)std::min<int64_t>(ceil_div(N, 16), 256);
+  return p;
+}
 
 // Forward workspace layout.
 struct FwdWs {
@@ -93,6 +114,13 @@ struct FwdWs {
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdWs w{};
   w.rp = rup(r, 8);
+  if (use_gemv(M)) {  // U written directly; partial sums only when K is split
+    const GemvPlan g = gemv_plan(M, N, K);
+    w.y_part = 0;
+    w.u_part = w.pad_u = w.pad_b = 0;
+    w.total = std::max<size_t>(g.ksplit > 1 ? align256((size_t)g.ksplit * M * N * 4) : 0, 256);
+    return w;
+  }
   w.pu = plan(M, r, K, SK_MT, SK_NT, true);
   const int64_t ldu = (int64_t)w.pu.tiles_n * SK_NT;
   size_t off = 0;
@@ -168,6 +196,14 @@ qlora_status run_reduce(const float* part, int64_t part_stride, int nsplit, int6
 
 constexpr ReduceOut kNoOut{nullptr, nullptr, 0, 0};
 
+// s·x is exact in bf16 for every bf16 x when s is a power of two (no
+// overflow / underflow at the magnitudes of the adapter factors).
+int needs_split(float s) {
+  int e = 0;
+  const float m = std::frexp(s, &e);
+  return (m == 0.5f || m == -0.5f) ? 0 : 1;
+}
+
 qlora_status validate_weight(const qlora_nf4_weight* w) {
   QCHECK(w != nullptr, QLORA_ERR_NULL);
   QCHECK(w->n_out >= 0 && w->k_in >= 0, QLORA_ERR_SHAPE);
@@ -195,6 +231,11 @@ qlora_status lora_down_impl(const uint16_t* X, int64_t M, int64_t K, const uint1
                             uint16_t* U, uint16_t* Upad, int64_t rp, char* ws, const FwdWs& L,
                             hipStream_t st) {
   if (M == 0) return QLORA_OK;
+  if (use_gemv(M)) {
+    hipLaunchKernelGGL(lora_down_small_kernel, dim3((unsigned)r), dim3(256), 0, st, X, (int)M, K,
+                       A, (int)r, U);
+    return launched();
+  }
   GemmArgs g{};
   g.a = X; g.lda = K; g.rows = M; g.cols = r; g.red = K;
   g.b = A; g.ldb = K;
@@ -211,16 +252,55 @@ qlora_status lora_down_impl(const uint16_t* X, int64_t M, int64_t K, const uint1
                     ReduceOut{Upad, nullptr, rp, 0}, kNoOut, st);
 }
 
+template <int CPW, int MG>
+void launch_gemv(const GemvArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((nf4_gemv_kernel<CPW, MG>), grid, dim3(512), 0, st, a);
+}
+
+// Few-token forward: U (pitch r) and B (pitch r) are read as given.
+qlora_status gemv_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* U,
+                       const uint16_t* B, int32_t r, float s, uint16_t* Y, char* ws,
+                       hipStream_t st) {
+  const int64_t N = w->n_out, K = w->k_in;
+  const GemvPlan p = gemv_plan(M, N, K);
+  GemvArgs a{};
+  a.x = X; a.M = (int32_t)M; a.K = K; a.N = N;
+  a.packed = w->packed; a.qabsmax = w->qabsmax; a.c2 = w->c2;
+  a.u = U; a.r = r; a.b = B; a.s = s;
+  a.y = Y; a.part = reinterpret_cast<float*>(ws); a.ksplit = p.ksplit;
+  const dim3 grid((unsigned)p.gx, (unsigned)p.ksplit);
+  if (p.mg == 1) {
+    switch (p.cpw) {
+      case 1: launch_gemv<1, 1>(a, grid, st); break;
+      case 2: launch_gemv<2, 1>(a, grid, st); break;
+      case 4: launch_gemv<4, 1>(a, grid, st); break;
+      default: launch_gemv<8, 1>(a, grid, st); break;
+    }
+  } else {
+    switch (p.cpw) {
+      case 1: launch_gemv<1, 2>(a, grid, st); break;
+      case 2: launch_gemv<2, 2>(a, grid, st); break;
+      default: launch_gemv<4, 2>(a, grid, st); break;
+    }
+  }
+  qlora_status e = launched();
+  if (e != QLORA_OK || p.ksplit == 1) return e;
+  return run_reduce(a.part, M * N, p.ksplit, M, N, M, N, N, 1.0f, ReduceOut{Y, nullptr, N, 0},
+                    ReduceOut{nullptr, nullptr, 0, 0}, st);
+}
+
 qlora_status matmul_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M,
                              const uint16_t* Upro, int64_t ldu, const uint16_t* Bpro, int64_t ldb,
                              int32_t r, float s, uint16_t* Y, char* ws, const FwdWs& L,
                              hipStream_t st) {
   if (M == 0) return QLORA_OK;
   const int64_t N = w->n_out, K = w->k_in;
+  if (use_gemv(M)) return gemv_impl(w, X, M, Upro, Bpro, r, s, Y, ws, st);
   GemmArgs g{};
   g.a = X; g.lda = K; g.rows = M; g.cols = N; g.red = K;
   g.packed = w->packed; g.qabsmax = w->qabsmax; g.c2 = w->c2; g.w_kin = K;
   g.pl = Upro; g.ldpl = ldu; g.pr = Bpro; g.ldpr = ldb; g.rl = r; g.s = s;
+  g.s_split = needs_split(s);
   if (use_big(M)) {
     g.out_bf16 = Y; g.ldo = N;
     return run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_COLS, true, O_BF16>(
@@ -333,7 +413,7 @@ qlora_status qlora_dequantize_nf4(const qlora_nf4_weight* w, qlora_bf16* out, vo
   s = check_device();
   if (s != QLORA_OK) return s;
   const int64_t ndw = n / 8;
-  hipLaunchKernelGGL(dequantize_nf4_kernel, dim3(grid_for(ndw, 256, 1 << 20)), dim3(256), 0,
+  hipLaunchKernelGGL(dequantize_nf4_kernel, dim3(grid_for(ndw, 1024, 1 << 20)), dim3(256), 0,
                      as_stream(stream), reinterpret_cast<const uint32_t*>(w->packed), w->qabsmax,
                      w->c2, ndw, reinterpret_cast<u32x4*>(out));
   return launched();
@@ -350,9 +430,11 @@ qlora_status qlora_lora_down(const qlora_bf16* X, int64_t M, int64_t k_in, const
   ALIGNED_OR_NULL(U);
   // the forward's layout, with n_out taken as 8 (only the U region is used)
   const FwdWs L = fwd_ws(M, 8, k_in, r);
-  QCHECK(workspace != nullptr && aligned16(workspace), QLORA_ERR_WORKSPACE);
-  QCHECK(ws_bytes >= L.u_part + align256((size_t)L.pu.nsplit * M * L.pu.tiles_n * SK_NT * 4),
-         QLORA_ERR_WORKSPACE);
+  if (!use_gemv(M)) {
+    QCHECK(workspace != nullptr && aligned16(workspace), QLORA_ERR_WORKSPACE);
+    QCHECK(ws_bytes >= L.u_part + align256((size_t)L.pu.nsplit * M * L.pu.tiles_n * SK_NT * 4),
+           QLORA_ERR_WORKSPACE);
+  }
   qlora_status s = check_device();
   if (s != QLORA_OK) return s;
   return lora_down_impl(X, M, k_in, A, r, U, nullptr, 0, static_cast<char*>(workspace), L,
@@ -378,7 +460,7 @@ qlora_status qlora_nf4_matmul_fwd(const qlora_nf4_weight* w, const qlora_bf16* X
   const uint16_t* up = U;
   const uint16_t* bp = B;
   int64_t ld = r;
-  if (r % 8 != 0) {
+  if (r % 8 != 0 && !use_gemv(M)) {
     uint16_t* Up = reinterpret_cast<uint16_t*>(ws + L.pad_u);
     uint16_t* Bp = reinterpret_cast<uint16_t*>(ws + L.pad_b);
     hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(M * L.rp)), dim3(256), 0, st, U, (int64_t)r,
@@ -411,7 +493,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const qlora_bf16* X, in
   if (s != QLORA_OK) return s;
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = as_stream(stream);
-  const bool pad = r % 8 != 0;
+  const bool pad = r % 8 != 0 && !use_gemv(M);
   uint16_t* Up = pad ? reinterpret_cast<uint16_t*>(ws + L.pad_u) : nullptr;
   s = lora_down_impl(X, M, w->k_in, A, r, U, Up, L.rp, ws, L, st);
   if (s != QLORA_OK) return s;
@@ -501,6 +583,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const qlora_bf16* X, co
     g.a = dY; g.lda = N; g.rows = M; g.cols = K; g.red = N;
     g.packed = w->packed; g.qabsmax = w->qabsmax; g.c2 = w->c2; g.w_kin = K;
     g.pl = V; g.ldpl = L.rp; g.pr = At; g.ldpr = L.rp; g.rl = r; g.s = sc;
+    g.s_split = needs_split(sc);
     if (use_big(M)) {
       g.out_bf16 = dX; g.ldo = K;
       s = run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_RED, true, O_BF16>(

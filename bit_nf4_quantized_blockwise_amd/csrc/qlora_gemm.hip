@@ -35,35 +35,86 @@ namespace {
 
 constexpr int KT = 64;
 constexpr int ROWB = KT * 2;  // bytes per LDS row
+constexpr int kOOB = 0x7ffffff0;         // a buffer offset past every range: loads return 0
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
 
 __device__ inline int swz(int row, int chunk) { return (row * ROWB) + ((chunk ^ (row & 7)) << 4); }
 
+// A raw buffer resource: loads at offsets outside [0, bytes) return zero, so
+// ragged tiles need no branches.
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ inline void init(const void* base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+    r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+  }
+  __device__ inline u32x4 ld16(int off) const {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ inline uint32_t ld4(int off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ inline uint32_t ld1(int off) const {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+  }
+};
+
 // ---- A-style loader: [rows][ld] bf16, reduction contiguous ---------------------
+// Thread t moves 16-byte chunks id = t + 256 i: row id / 8, chunk id % 8.
 template <int T_ROWS>
 struct RowTile {
   static constexpr int PER_T = T_ROWS * 8 / 256;
   static_assert(PER_T >= 1, "tile too small");
   u32x4 r[PER_T];
+  Buf buf;
+  int voff;      // byte offset of chunk i = 0 from the tile's first row
+  int rstride;   // bytes between chunk i and i + 1 (32 rows)
 
-  __device__ inline void load(const uint16_t* __restrict__ p, int64_t ld, int64_t nrows,
-                              int64_t nred, int64_t row0, int64_t k0, int tid) {
+  __device__ inline void init(const uint16_t* p, int64_t ld, int64_t nrows, int64_t row0,
+                              int tid) {
+    buf.init(p + row0 * ld, (nrows - row0) * ld * 2);
+    voff = (tid >> 3) * (int)ld * 2 + (tid & 7) * 16;
+    rstride = 32 * (int)ld * 2;
+  }
+  __device__ inline void load(int64_t k0, int64_t nred, int tid) {
+    const bool ok = k0 + (tid & 7) * 8 < nred;
+    const int base = ok ? voff + (int)k0 * 2 : kOOB;
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 3, c = id & 7;
-      const int64_t gr = row0 + row, gk = k0 + c * 8;
-      if (gr < nrows && gk < nred)
-        r[i] = *reinterpret_cast<const u32x4*>(p + gr * ld + gk);
-      else
-        r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < PER_T; ++i) r[i] = buf.ld16(ok ? base + i * rstride : kOOB);
   }
   __device__ inline void store(char* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int id = tid + 256 * i;
-      const int row = id >> 3, c = id & 7;
-      *reinterpret_cast<u32x4*>(lds + swz(row, c)) = r[i];
+      *reinterpret_cast<u32x4*>(lds + swz(id >> 3, id & 7)) = r[i];
+    }
+  }
+  // Quarter q of store(): chunks i with i % 4 == q (all of them when PER_T < 4
+  // and q == 0).
+  __device__ inline void store_part(char* lds, int tid, int q) const {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      if (i % 4 != q) continue;
+      const int id = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(lds + swz(id >> 3, id & 7)) = r[i];
+    }
+  }
+  // Stores RNE_bf16(s·v) (part 0) or RNE_bf16(s·v − part 0) (part 1) for the
+  // eight bf16 values v of each chunk: s·v ≈ part 0 + part 1 to ~2^-16.
+  __device__ inline void store_scaled(char* lds, int tid, float s, int part) const {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float a = bits_to_float(r[i][d] << 16) * s;
+        const float b = bits_to_float(r[i][d] & 0xffff0000u) * s;
+        uint32_t h = pack_bf16x2(a, b);
+        if (part) h = pack_bf16x2(a - bits_to_float(h << 16), b - bits_to_float(h & 0xffff0000u));
+        o[d] = h;
+      }
+      const int id = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(lds + swz(id >> 3, id & 7)) = o;
     }
   }
 };
@@ -86,25 +137,34 @@ template <int NT>
 struct RcTile {
   static_assert(NT == 256, "RC loader assumes 256 columns");
   u32x4 r[8];
-  __device__ inline void load(const uint16_t* __restrict__ p, int64_t ld, int64_t nred,
-                              int64_t ncols, int64_t red0, int64_t col0, int tid) {
+  __device__ inline void load(const uint16_t* p, int64_t ld, int64_t nred, int64_t ncols,
+                              int64_t red0, int64_t col0, int tid) {
+    Buf b;
+    b.init(p + red0 * ld, (nred - red0) * ld * 2);
     const int rb = tid >> 5, cb = tid & 31;
     const int64_t gc = col0 + cb * 8;
+    const int base = (gc < ncols) ? (rb * 8) * (int)ld * 2 + (int)gc * 2 : kOOB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t gr = red0 + rb * 8 + i;
-      if (gr < nred && gc < ncols)
-        r[i] = *reinterpret_cast<const u32x4*>(p + gr * ld + gc);
-      else
-        r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 8; ++i) r[i] = b.ld16(gc < ncols ? base + i * (int)ld * 2 : kOOB);
   }
   __device__ inline void store(char* lds, int tid) const {
-    const int rb = tid >> 5, cb = tid & 31;
-    u32x4 o[8];
-    transpose8x8(r, o);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = o[c];
+    for (int q = 0; q < 4; ++q) store_part(lds, tid, q);
+  }
+  // Quarter q: output columns 2q and 2q + 1 of this thread's 8x8 sub-block,
+  // each the 8 reduction values of one source column (an 8x8 transpose).
+  __device__ inline void store_part(char* lds, int tid, int q) const {
+    const int rb = tid >> 5, cb = tid & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 2 * q + h;
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        o[d] = __builtin_amdgcn_perm(r[2 * d + 1][c >> 1], r[2 * d][c >> 1], sel);
+      *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = o;
+    }
   }
 };
 
@@ -125,37 +185,43 @@ struct Nf4ColsTile {
   static constexpr int TPR = 256 / NT;        // threads per W row: 1 (NT=256) or 2 (NT=128)
   static constexpr int DW = 8 / TPR;          // packed dwords per thread
   static_assert(NT == 256 || NT == 128, "NF4 column loader: NT in {128, 256}");
-  uint32_t p[DW];
+  u32x4 p[DW / 4];
   float ah;
+  Buf pk, qa, c2;
+  int row_off, q_off;
+  int64_t gblk0;  // global block index of this thread's row at k = 0
 
-  __device__ inline void load(const GemmArgs& g, int64_t n0, int64_t k0, int tid) {
+  __device__ inline void init(const GemmArgs& g, int64_t n0, int tid) {
     const int row = tid / TPR, part = tid % TPR;
-    const int64_t n = n0 + row;
-    if (n < g.cols) {
-      const int64_t e0 = n * g.w_kin + k0 + part * (64 / TPR);
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(g.packed + (e0 >> 1));
-      if constexpr (DW == 8) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(src);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(src + 4);
-        p[0] = a[0]; p[1] = a[1]; p[2] = a[2]; p[3] = a[3];
-        p[4] = b[0]; p[5] = b[1]; p[6] = b[2]; p[7] = b[3];
-      } else {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(src);
-        p[0] = a[0]; p[1] = a[1]; p[2] = a[2]; p[3] = a[3];
-      }
-      const int64_t blk = (n * g.w_kin + k0) >> 6;
-      ah = g.c2[blk >> 8] * (float)g.qabsmax[blk];
-    } else {
+    const int64_t bpr = g.w_kin >> 6;  // blocks per W row
+    pk.init(g.packed + n0 * (g.w_kin >> 1), (g.cols - n0) * (g.w_kin >> 1));
+    qa.init(g.qabsmax + n0 * bpr, (g.cols - n0) * bpr);
+    c2.init(g.c2, ((g.cols * bpr + 255) >> 8) * 4);
+    row_off = row * (int)(g.w_kin >> 1) + part * 16 * (DW / 4);
+    q_off = row * (int)bpr;
+    gblk0 = (n0 + row) * bpr;
+  }
+  __device__ inline void load(int64_t k0, int64_t kend) {
+    const int kb = (int)(k0 >> 6);
+    const bool ok = k0 < kend;  // uniform: tiles past this split's range read as zero
 #pragma unroll
-      for (int d = 0; d < DW; ++d) p[d] = 0x88888888u;
-      ah = 0.0f;
-    }
+    for (int d = 0; d < DW / 4; ++d) p[d] = pk.ld16(ok ? row_off + (int)(k0 >> 1) + 16 * d : kOOB);
+    const uint32_t q = qa.ld1(ok ? q_off + kb : kOOB);
+    const float s2 = bits_to_float(c2.ld4((int)(((gblk0 + kb) >> 8) * 4)));
+    ah = s2 * (float)q;
   }
   __device__ inline void store(char* lds, int tid, const float* cb) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_part(lds, tid, cb, q);
+  }
+  // Quarter q: packed dwords d with d % 4 == q (8 weights -> one 16-byte chunk each).
+  __device__ inline void store_part(char* lds, int tid, const float* cb, int q) const {
     const int row = tid / TPR, part = tid % TPR;
 #pragma unroll
-    for (int d = 0; d < DW; ++d)
-      *reinterpret_cast<u32x4*>(lds + swz(row, part * DW + d)) = dequant8(p[d], ah, cb);
+    for (int d = 0; d < DW; ++d) {
+      if (d % 4 != q) continue;
+      *reinterpret_cast<u32x4*>(lds + swz(row, part * DW + d)) = dequant8(p[d >> 2][d & 3], ah, cb);
+    }
   }
 };
 
@@ -166,32 +232,50 @@ struct Nf4RedTile {
   static_assert(NT == 256, "NF4 reduction-major loader assumes 256 columns");
   uint32_t p[8];
   float ah[8];
+  Buf c2;
+  int64_t k;  // first W column of this thread
 
-  __device__ inline void load(const GemmArgs& g, int64_t r0, int64_t c0, int tid) {
-    const int rb = tid >> 5, cb = tid & 31;
-    const int64_t k = c0 + cb * 8;
+  __device__ inline void init(const GemmArgs& g, int64_t c0, int tid) {
+    k = c0 + (tid & 31) * 8;
+    c2.init(g.c2, ((g.red * (g.w_kin >> 6) + 255) >> 8) * 4);
+  }
+  __device__ inline void load(const GemmArgs& g, int64_t r0, int64_t rend, int tid) {
+    const int rb = tid >> 5;
+    const int64_t bpr = g.w_kin >> 6;
+    Buf pk, qa;
+    pk.init(g.packed + r0 * (g.w_kin >> 1), (rend - r0) * (g.w_kin >> 1));
+    qa.init(g.qabsmax + r0 * bpr, (rend - r0) * bpr);
+    const bool ok = k < g.cols;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t n = r0 + rb * 8 + i;
-      if (n < g.red && k < g.cols) {
-        const int64_t e = n * g.w_kin + k;
-        p[i] = *reinterpret_cast<const uint32_t*>(g.packed + (e >> 1));
-        const int64_t blk = e >> 6;
-        ah[i] = g.c2[blk >> 8] * (float)g.qabsmax[blk];
-      } else {
-        p[i] = 0x88888888u;
-        ah[i] = 0.0f;
-      }
+      const int n = rb * 8 + i;
+      p[i] = pk.ld4(ok ? n * (int)(g.w_kin >> 1) + (int)(k >> 1) : kOOB);
+      const int lb = n * (int)bpr + (int)(k >> 6);
+      const uint32_t q = qa.ld1(ok ? lb : kOOB);
+      const float s2 = bits_to_float(c2.ld4((int)((((r0 + n) * bpr + (k >> 6)) >> 8) * 4)));
+      ah[i] = s2 * (float)q;
     }
   }
   __device__ inline void store(char* lds, int tid, const float* cbk) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_part(lds, tid, cbk, q);
+  }
+  // Quarter q: output columns c = 2q, 2q + 1 — W column k + c decoded from
+  // nibble c of each of the 8 W rows (the transpose falls out of the lookup).
+  __device__ inline void store_part(char* lds, int tid, const float* cbk, int q) const {
     const int rb = tid >> 5, cb = tid & 31;
-    u32x4 rows[8], cols[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rows[i] = dequant8(p[i], ah[i], cbk);
-    transpose8x8(rows, cols);
+    for (int h = 0; h < 2; ++h) {
+      const int c = 2 * q + h;
+      u32x4 o;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = cols[c];
+      for (int d = 0; d < 4; ++d) {
+        const float lo = cbk[(p[2 * d] >> (4 * c)) & 15u] * ah[2 * d];
+        const float hi = cbk[(p[2 * d + 1] >> (4 * c)) & 15u] * ah[2 * d + 1];
+        o[d] = pack_bf16x2(lo, hi);
+      }
+      *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = o;
+    }
   }
 };
 
@@ -210,13 +294,26 @@ struct Mma {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   }
-  __device__ inline void scale(float s) {
+  struct Frags {
+    bf16x8 a[FM], b[FN];
+  };
+  __device__ inline void load_frags(Frags& f, const char* As, const char* Bs, int wm, int wn,
+                                    int lane, int ks) const {
+    const int lr = lane & 31, lh = lane >> 5;
+    const int chunk = ks * 2 + lh;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      f.a[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * WTM + i * 32 + lr, chunk));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * WTN + j * 32 + lr, chunk));
+  }
+  __device__ inline void mfma(const Frags& f) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] *= s;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   }
   // One 64-deep K tile from LDS.
   __device__ inline void run(const char* As, const char* Bs, int wm, int wn, int lane) {
@@ -276,62 +373,106 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   mma.zero();
 
   if constexpr (PROLOGUE) {
+    // acc = s · L·Rᵀ over the rank dimension.  s is applied to L while it is
+    // staged (two bf16 parts when s·L is not exact in one), never to acc.
     if (blockIdx.y == 0 && g.rl > 0) {
-      for (int64_t j0 = 0; j0 < g.rl; j0 += KT) {
-        RowTile<MT> lt;
-        RowTile<NT> rt;
-        lt.load(g.pl, g.ldpl, g.rows, g.rl, row0, j0, tid);
-        rt.load(g.pr, g.ldpr, g.cols, g.rl, col0, j0, tid);
-        lt.store(As(0), tid);
+      RowTile<MT> lt;
+      RowTile<NT> rt;
+      lt.init(g.pl, g.ldpl, g.rows, row0, tid);
+      rt.init(g.pr, g.ldpr, g.cols, col0, tid);
+      // one flat loop over (rank chunk, part): nested loops around the MFMAs
+      // make the register allocator spill the accumulators
+      const int nparts = 1 + g.s_split;
+      const int nsteps = (int)((g.rl + KT - 1) / KT) * nparts;
+      for (int st = 0; st < nsteps; ++st) {
+        const int64_t j0 = (int64_t)(st / nparts) * KT;
+        const int part = st % nparts;
+        lt.load(j0, g.rl, tid);
+        rt.load(j0, g.rl, tid);
+        lt.store_scaled(As(0), tid, g.s, part);
         rt.store(Bs(0), tid);
         __syncthreads();
         mma.run(As(0), Bs(0), wm, wn, lane);
         __syncthreads();
       }
-      mma.scale(g.s);
     }
   }
 
-  RowTile<MT> at;
   using BTile = typename std::conditional<
       BMODE == B_NF4_COLS, Nf4ColsTile<NT>,
       typename std::conditional<BMODE == B_NF4_RED, Nf4RedTile<NT>,
                                 typename std::conditional<BMODE == B_BF16_RC, RcTile<NT>,
                                                           RowTile<NT>>::type>::type>::type;
-  BTile bt;
+  // Two register sets: while the MFMAs consume one LDS stage, the tile loaded
+  // one half-iteration earlier is decoded into the other stage and the next
+  // tile is in flight from memory.
+  RowTile<MT> a0, a1;
+  BTile b0, b1;
+  a0.init(g.a, g.lda, g.rows, row0, tid);
+  a1.init(g.a, g.lda, g.rows, row0, tid);
+  if constexpr (BMODE == B_NF4_COLS || BMODE == B_NF4_RED) {
+    b0.init(g, col0, tid);
+    b1.init(g, col0, tid);
+  } else if constexpr (BMODE == B_BF16_CR) {
+    b0.init(g.b, g.ldb, g.cols, col0, tid);
+    b1.init(g.b, g.ldb, g.cols, col0, tid);
+  }
+  const int64_t kend = min(g.red, (int64_t)kt_end * KT);  // this split's reduction bound
 
-  auto load_tiles = [&](int kt) {
+  auto load_tiles = [&](RowTile<MT>& at, BTile& bt, int kt) {
     const int64_t k0 = (int64_t)kt * KT;
-    at.load(g.a, g.lda, g.rows, g.red, row0, k0, tid);
+    at.load(k0, kend, tid);
     if constexpr (BMODE == B_NF4_COLS) {
-      bt.load(g, col0, k0, tid);
+      bt.load(k0, kend);
     } else if constexpr (BMODE == B_NF4_RED) {
-      bt.load(g, k0, col0, tid);
+      bt.load(g, k0, kend, tid);
     } else if constexpr (BMODE == B_BF16_RC) {
-      bt.load(g.b, g.ldb, g.red, g.cols, k0, col0, tid);
+      bt.load(g.b, g.ldb, kend, g.cols, k0, col0, tid);
     } else {
-      bt.load(g.b, g.ldb, g.cols, g.red, col0, k0, tid);
+      bt.load(k0, kend, tid);
     }
   };
-  auto store_tiles = [&](int st) {
-    at.store(As(st), tid);
+  auto store_part = [&](const RowTile<MT>& at, const BTile& bt, int st, int q) {
+    at.store_part(As(st), tid, q);
     if constexpr (BMODE == B_NF4_COLS || BMODE == B_NF4_RED)
-      bt.store(Bs(st), tid, cb);
+      bt.store_part(Bs(st), tid, cb, q);
     else
-      bt.store(Bs(st), tid);
+      bt.store_part(Bs(st), tid, q);
+  };
+  using MmaT = Mma<MT, NT, WM, WN>;
+  // One K tile of MFMAs from stage `cur`, with a quarter of the next tile's
+  // decode + LDS writes (into stage cur ^ 1) after each 64-deep quarter of
+  // MFMAs; fragments are read one quarter ahead.  sched_barrier keeps the
+  // compiler from regrouping the quarters.
+  auto step = [&](int cur, const RowTile<MT>& at, const BTile& bt) {
+    typename MmaT::Frags f0, f1;
+    mma.load_frags(f0, As(cur), Bs(cur), wm, wn, lane, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      typename MmaT::Frags& fc = (ks & 1) ? f1 : f0;
+      typename MmaT::Frags& fn = (ks & 1) ? f0 : f1;
+      if (ks < 3) mma.load_frags(fn, As(cur), Bs(cur), wm, wn, lane, ks + 1);
+      mma.mfma(fc);
+      store_part(at, bt, cur ^ 1, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   if (kt_begin < kt_end) {
     __syncthreads();  // codebook visible
-    load_tiles(kt_begin);
-    store_tiles(0);
+    load_tiles(a0, b0, kt_begin);
+    load_tiles(a1, b1, kt_begin + 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_part(a0, b0, 0, q);
     __syncthreads();
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const int cur = (kt - kt_begin) & 1;
-      const bool more = kt + 1 < kt_end;
-      if (more) load_tiles(kt + 1);
-      mma.run(As(cur), Bs(cur), wm, wn, lane);
-      if (more) store_tiles(cur ^ 1);
+    // Branch-free: tiles past kt_end load as zeros, so an odd count ends with
+    // one MFMA pass over a zero tile.
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
+      load_tiles(a0, b0, kt + 2);
+      step(0, a1, b1);
+      __syncthreads();
+      load_tiles(a1, b1, kt + 3);
+      step(1, a0, b0);
       __syncthreads();
     }
   }

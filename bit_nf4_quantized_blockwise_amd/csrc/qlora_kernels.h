@@ -25,6 +25,7 @@ struct GemmArgs {
   int64_t ldpr;
   int32_t rl;
   float s;
+  int32_t s_split;     // 1: stage s·L as two bf16 parts (s·L not exact in bf16)
   uint16_t* out_bf16;  // O_BF16: [rows][ldo]
   float* out_f32;      // O_F32: [split][rows][ldo] partial sums
   int64_t ldo;
@@ -40,8 +41,30 @@ struct ReduceOut {
   int32_t transposed;  // write out[col][row] instead of out[row][col]
 };
 
+struct GemvArgs {
+  const uint16_t* x;  // [M][K] bf16
+  int32_t M;
+  int64_t K, N;
+  const uint8_t* packed;  // W[N][K] NF4 + DQ
+  const int8_t* qabsmax;
+  const float* c2;
+  const uint16_t* u;  // [M][r] bf16, pitch r
+  int32_t r;
+  const uint16_t* b;  // [N][r] bf16, pitch r
+  float s;
+  uint16_t* y;   // [M][N] bf16 (ksplit == 1)
+  float* part;   // [ksplit][M][N] (ksplit > 1; split 0 carries the adapter term)
+  int32_t ksplit;
+};
+
 template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE>
 __global__ void gemm_kernel(GemmArgs g);
+
+template <int CPW, int MG>
+__global__ void nf4_gemv_kernel(GemvArgs g);
+
+__global__ void lora_down_small_kernel(const uint16_t* x, int M, int64_t K, const uint16_t* a,
+                                       int r, uint16_t* u);
 
 __global__ void quantize_nf4_kernel(const float* w, int64_t n, int64_t nblocks, uint8_t* packed,
                                     float* absmax);

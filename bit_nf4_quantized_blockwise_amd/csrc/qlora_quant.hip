@@ -52,13 +52,6 @@ __device__ inline float rd32_mul(double m, float a) {
   return f;
 }
 
-__device__ inline uint32_t nf4_index(float w, const float (&T)[15]) {
-  uint32_t idx = 0;
-#pragma unroll
-  for (int i = 0; i < 15; ++i) idx += (w > T[i]) ? 1u : 0u;
-  return idx;
-}
-
 // Second-level code: integer in [0, 127] nearest to a / step, tie to the lower.
 __device__ inline int dq_code(float a, float step) {
   if (!(step > 0.0f)) return 0;
@@ -77,10 +70,38 @@ __device__ inline float dq_step(float gmax) {
   return (float)((double)gmax / 127.0);
 }
 
+// Bucket table for the exact decision.  With x = w / a in [-1, 1], bucket
+// j = floor((x + 1) · 32) (clamped to 63) spans [j/32 − 1, (j+1)/32 − 1).
+// kBucketMargin exceeds the error of the float32 quotient w · RN(1/a) by orders
+// of magnitude and, because consecutive midpoints are more than 0.088 apart,
+// a bucket widened by the margin on both sides still holds at most one
+// midpoint.  first[j] = #{i : m_i < j/32 − 1 − margin}: the exact index is
+// first[j] or first[j] + 1, decided by one exact compare w > T_first[j].
+constexpr double kBucketMargin = 1.0 / 1024.0;
+
+struct BucketTable {
+  uint8_t first[64];
+};
+
+constexpr BucketTable make_buckets() {
+  BucketTable t{};
+  for (int j = 0; j < 64; ++j) {
+    const double lo = j / 32.0 - 1.0 - kBucketMargin;
+    int c = 0;
+    for (int i = 0; i < 15; ++i) c += (kMid.m[i] < lo) ? 1 : 0;
+    t.first[j] = (uint8_t)c;
+  }
+  return t;
+}
+
+constexpr BucketTable kBuckets = make_buckets();
+
+constexpr int kTStride = 17;  // floats per block in the LDS threshold table (bank spread)
+
 // One lane handles 16 consecutive elements; 4 lanes form one 64-block.
-// Loads the 16 elements (zero beyond n), returns the block absmax (all 4
-// lanes agree) and the packed 8 bytes of this lane.
+// T: this block's 16-entry threshold row in LDS (T[15] = +inf); bk: bucket table.
 __device__ inline float quantize_16(const float* __restrict__ w, int64_t n, int64_t blk, int sub,
+                                    float* __restrict__ T, const uint8_t* __restrict__ bk,
                                     u32x2& out_bytes) {
   const int64_t base = blk * kBlock + (int64_t)sub * 16;
   float v[16];
@@ -104,17 +125,33 @@ __device__ inline float quantize_16(const float* __restrict__ w, int64_t n, int6
   m = fmaxf(m, __shfl_xor(m, 1));
   m = fmaxf(m, __shfl_xor(m, 2));
 
+  // the 4 lanes of the block write its 15 thresholds (+ the +inf sentinel)
+#pragma unroll
+  for (int i = sub; i < 16; i += 4) T[i] = (i < 15) ? rd32_mul(kMid.m[i], m) : __builtin_inff();
+  // the block's 4 lanes share one wave, whose LDS accesses complete in order;
+  // the barrier only keeps the compiler from moving the reads above the writes
+  __builtin_amdgcn_wave_barrier();
+
   uint32_t lo = 0x88888888u, hi = 0x88888888u;  // all-zero block: every index 8
   if (m > 0.0f) {
-    float T[15];
-#pragma unroll
-    for (int i = 0; i < 15; ++i) T[i] = rd32_mul(kMid.m[i], m);
+    // the estimate only picks a bucket; a power-of-two rescale keeps 1/m finite
+    // for subnormal block maxima without changing any ratio
+    const float sc = (m < 0x1p-64f) ? 0x1p64f : 1.0f;
+    const float inv = 1.0f / (m * sc);
     lo = 0u;
     hi = 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lo |= nf4_index(v[j], T) << (4 * j);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) hi |= nf4_index(v[8 + j], T) << (4 * j);
+    for (int j = 0; j < 16; ++j) {
+      const float x = (v[j] * sc) * inv;
+      int b = (int)__builtin_fmaf(x, 32.0f, 32.0f);
+      b = b < 0 ? 0 : (b > 63 ? 63 : b);
+      const int k0 = bk[b];
+      const uint32_t idx = (uint32_t)k0 + ((v[j] > T[k0]) ? 1u : 0u);
+      if (j < 8)
+        lo |= idx << (4 * j);
+      else
+        hi |= idx << (4 * (j - 8));
+    }
   }
   out_bytes = u32x2{lo, hi};
   return m;
@@ -127,12 +164,17 @@ __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restri
                                                            int64_t nblocks,
                                                            uint8_t* __restrict__ packed,
                                                            float* __restrict__ absmax) {
-  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float thr[64 * kTStride];
+  __shared__ uint8_t bk[64];
+  const int t = threadIdx.x;
+  if (t < 64) bk[t] = kBuckets.first[t];
+  __syncthreads();
+  const int64_t gt = (int64_t)blockIdx.x * 256 + t;
   const int64_t blk = gt >> 2;
   const int sub = (int)(gt & 3);
   if (blk >= nblocks) return;  // the 4 lanes of a block leave together
   u32x2 bytes;
-  const float m = quantize_16(w, n, blk, sub, bytes);
+  const float m = quantize_16(w, n, blk, sub, thr + (t >> 2) * kTStride, bk, bytes);
   *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
   if (sub == 0) absmax[blk] = m;
 }
@@ -167,7 +209,11 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
                                                               float* __restrict__ absmax_out) {
   __shared__ float amax[kGroup];
   __shared__ float red[4];
+  __shared__ float thr[64 * kTStride];
+  __shared__ uint8_t bk[64];
   const int t = threadIdx.x;
+  if (t < 64) bk[t] = kBuckets.first[t];
+  __syncthreads();
   const int64_t g = blockIdx.x;
   const int sub = t & 3;
 #pragma unroll 1
@@ -177,7 +223,7 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
     float m = 0.0f;
     if (blk < nblocks) {
       u32x2 bytes;
-      m = quantize_16(w, n, blk, sub, bytes);
+      m = quantize_16(w, n, blk, sub, thr + (t >> 2) * kTStride, bk, bytes);
       *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
     }
     if (sub == 0) amax[lb] = m;
@@ -199,8 +245,10 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
   }
 }
 
-// Standalone dequantisation to bf16: one packed dword (8 weights) per thread,
-// a 16-byte store.  n is a multiple of 64.
+// Standalone dequantisation to bf16.  A workgroup decodes 1024 consecutive
+// packed dwords (8192 weights); lane t takes dwords t, t + 256, t + 512,
+// t + 768, so every load (4 B per lane) and every store (16 B per lane) is
+// contiguous across the wave.  n is a multiple of 64.
 __global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __restrict__ packed,
                                                              const int8_t* __restrict__ qabsmax,
                                                              const float* __restrict__ c2,
@@ -209,19 +257,29 @@ __global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __r
   __shared__ float cb[16];
   if (threadIdx.x < 16) cb[threadIdx.x] = bits_to_float(kNF4Bits[threadIdx.x]);
   __syncthreads();
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < ndwords; i += stride) {
-    const uint32_t p = __builtin_nontemporal_load(packed + i);
-    const int64_t b = i >> 3;  // 8 dwords per 64-block
-    const float ah = c2[b >> 8] * (float)qabsmax[b];
-    u32x4 o;
+  const int64_t stride = (int64_t)gridDim.x * 1024;
+  for (int64_t base = (int64_t)blockIdx.x * 1024; base < ndwords; base += stride) {
+    uint32_t p[4];
+    float ah[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const float lo = cb[(p >> (8 * d)) & 15u] * ah;
-      const float hi = cb[(p >> (8 * d + 4)) & 15u] * ah;
-      o[d] = pack_bf16x2(lo, hi);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x + 256 * u;
+      p[u] = (i < ndwords) ? __builtin_nontemporal_load(packed + i) : 0u;
+      const int64_t b = (i < ndwords ? i : 0) >> 3;  // 8 dwords per 64-block
+      ah[u] = c2[b >> 8] * (float)qabsmax[b];
     }
-    __builtin_nontemporal_store(o, out + i);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x + 256 * u;
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float lo = cb[(p[u] >> (8 * d)) & 15u] * ah[u];
+        const float hi = cb[(p[u] >> (8 * d + 4)) & 15u] * ah[u];
+        o[d] = pack_bf16x2(lo, hi);
+      }
+      if (i < ndwords) __builtin_nontemporal_store(o, out + i);
+    }
   }
 }
 
