@@ -87,7 +87,7 @@ bool use_big(int64_t M) { return M >= kBigM; }
 bool use_gemv(int64_t M) { return M <= kFewM; }
 
 struct GemvPlan {
-  int cpw, mg, ksplit, gx;
+  int cpw, mg, ksplit, gx, groups;
 };
 
 // 8 waves per workgroup, each wave CPW chunks of 128 k; tokens in groups of 8.
@@ -100,7 +100,11 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K) {
   p.cpw = 1;
   while (p.cpw < need && p.cpw < cap) p.cpw *= 2;
   p.ksplit = (int)ceil_div(nch, 8 * (int64_t)p.cpw);
-  p.gx = (int)std::min<int64_t>(ceil_div(N, 16), 256);
+  // column groups (16 outputs each) per workgroup: enough that one workgroup
+  // per CU covers N, at most 8
+  const int64_t ncg = ceil_div(N, 16);
+  p.groups = (int)std::min<int64_t>(8, std::max<int64_t>(1, ceil_div(ncg, 256)));
+  p.gx = (int)ceil_div(ncg, p.groups);
   return p;
 }
 
@@ -174,13 +178,13 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   return w;
 }
 
-template <int MT, int NT, int WM, int WN, int BM, bool PRO, int OM>
+template <int MT, int NT, int WM, int WN, int BM, bool PRO, int OM, int AM = A_DIRECT>
 qlora_status run_gemm(GemmArgs g, const Plan& p, hipStream_t st) {
   g.tiles_m = p.tiles_m;
   g.tiles_n = p.tiles_n;
   g.kt_per_split = p.kt_per_split;
   dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.nsplit);
-  hipLaunchKernelGGL((gemm_kernel<MT, NT, WM, WN, BM, PRO, OM>), grid, dim3(256), 0, st, g);
+  hipLaunchKernelGGL((gemm_kernel<MT, NT, WM, WN, BM, PRO, OM, AM>), grid, dim3(256), 0, st, g);
   return launched();
 }
 
@@ -252,9 +256,23 @@ qlora_status lora_down_impl(const uint16_t* X, int64_t M, int64_t K, const uint1
                     ReduceOut{Upad, nullptr, rp, 0}, kNoOut, st);
 }
 
+template <int CPW, int MG, int G>
+void launch_gemv_g(const GemvArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((nf4_gemv_kernel<CPW, MG, G>), grid, dim3(512), 0, st, a);
+}
+
 template <int CPW, int MG>
-void launch_gemv(const GemvArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((nf4_gemv_kernel<CPW, MG>), grid, dim3(512), 0, st, a);
+void launch_gemv(const GemvArgs& a, dim3 grid, int groups, hipStream_t st) {
+  switch (groups) {
+    case 1: launch_gemv_g<CPW, MG, 1>(a, grid, st); break;
+    case 2: launch_gemv_g<CPW, MG, 2>(a, grid, st); break;
+    case 3: launch_gemv_g<CPW, MG, 3>(a, grid, st); break;
+    case 4: launch_gemv_g<CPW, MG, 4>(a, grid, st); break;
+    case 5: launch_gemv_g<CPW, MG, 5>(a, grid, st); break;
+    case 6: launch_gemv_g<CPW, MG, 6>(a, grid, st); break;
+    case 7: launch_gemv_g<CPW, MG, 7>(a, grid, st); break;
+    default: launch_gemv_g<CPW, MG, 8>(a, grid, st); break;
+  }
 }
 
 // Few-token forward: U (pitch r) and B (pitch r) are read as given.
@@ -271,16 +289,16 @@ qlora_status gemv_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, 
   const dim3 grid((unsigned)p.gx, (unsigned)p.ksplit);
   if (p.mg == 1) {
     switch (p.cpw) {
-      case 1: launch_gemv<1, 1>(a, grid, st); break;
-      case 2: launch_gemv<2, 1>(a, grid, st); break;
-      case 4: launch_gemv<4, 1>(a, grid, st); break;
-      default: launch_gemv<8, 1>(a, grid, st); break;
+      case 1: launch_gemv<1, 1>(a, grid, p.groups, st); break;
+      case 2: launch_gemv<2, 1>(a, grid, p.groups, st); break;
+      case 4: launch_gemv<4, 1>(a, grid, p.groups, st); break;
+      default: launch_gemv<8, 1>(a, grid, p.groups, st); break;
     }
   } else {
     switch (p.cpw) {
-      case 1: launch_gemv<1, 2>(a, grid, st); break;
-      case 2: launch_gemv<2, 2>(a, grid, st); break;
-      default: launch_gemv<4, 2>(a, grid, st); break;
+      case 1: launch_gemv<1, 2>(a, grid, p.groups, st); break;
+      case 2: launch_gemv<2, 2>(a, grid, p.groups, st); break;
+      default: launch_gemv<4, 2>(a, grid, p.groups, st); break;
     }
   }
   qlora_status e = launched();
@@ -303,7 +321,7 @@ qlora_status matmul_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64
   g.s_split = needs_split(s);
   if (use_big(M)) {
     g.out_bf16 = Y; g.ldo = N;
-    return run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_COLS, true, O_BF16>(
+    return run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_COLS, true, O_BF16, A_LDS>(
         g, plan(M, N, K, BIG_MT, BIG_NT, false), st);
   }
   g.out_f32 = reinterpret_cast<float*>(ws + L.y_part);

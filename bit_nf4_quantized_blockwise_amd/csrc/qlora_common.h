@@ -31,11 +31,31 @@ constexpr uint32_t kNF4Bits[16] = {
 __host__ __device__ inline float bits_to_float(uint32_t b) { return __builtin_bit_cast(float, b); }
 __host__ __device__ inline uint32_t float_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32;
+// `lo` lands in the low half.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{lo, hi}, bf16x2));
+}
+
+// Decode 8 NF4 codes (one packed dword, element 2t in the low nibble of byte t)
+// with block scale ah into 4 dwords of bf16 pairs: RNE_bf16(RN32(c[idx] * ah)).
+// cb is the 16-entry float codebook in LDS; the nibbles are spread to byte
+// offsets (4 * idx) once per dword so that each lookup costs one extract.
+__device__ inline u32x4 decode8(uint32_t p, float ah, const float* cb) {
+  const uint32_t ev = (p << 2) & 0x3c3c3c3cu;  // 4 * idx of elements 0, 2, 4, 6
+  const uint32_t od = (p >> 2) & 0x3c3c3c3cu;  // 4 * idx of elements 1, 3, 5, 7
+  const char* base = reinterpret_cast<const char*>(cb);
+  u32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float lo = *reinterpret_cast<const float*>(base + ((ev >> (8 * d)) & 0xffu)) * ah;
+    const float hi = *reinterpret_cast<const float*>(base + ((od >> (8 * d)) & 0xffu)) * ah;
+    o[d] = pack_bf16x2(lo, hi);
+  }
+  return o;
 }
 
 __device__ inline float bf16_bits_to_float(uint32_t b16) { return bits_to_float(b16 << 16); }

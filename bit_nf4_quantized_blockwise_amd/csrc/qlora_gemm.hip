@@ -19,11 +19,12 @@
 // QLoRAの計算フロー step 1: Ŵ only exists transiently).
 //
 // Tiling: K-tile 64 (= one NF4 block along k_in), 256 threads = 4 wave64s in
-// a WM×WN grid, v_mfma_f32_32x32x16_bf16, fp32 accumulators, LDS double
-// buffer with the next tile's global loads in flight during the MFMAs.  LDS
-// rows are 128 B (64 bf16) split in eight 16-byte chunks, chunk c of row r
-// stored at c ^ (r & 7) so that the 32 rows of one MFMA operand read hit
-// distinct banks.
+// a WM×WN grid, v_mfma_f32_32x32x16_bf16, fp32 accumulators.  The A operand
+// goes from memory straight into MFMA registers; only the B tile (decoded
+// weight or adapter factor) is staged in LDS, double-buffered, with the next
+// tile decoded while the MFMAs of the current one run.  LDS rows are 128 B
+// (64 bf16) in eight 16-byte chunks, swizzled so that the MFMA operand reads
+// and every loader's stores are free of bank conflicts.
 
 #include <type_traits>
 
@@ -38,7 +39,12 @@ constexpr int ROWB = KT * 2;  // bytes per LDS row
 constexpr int kOOB = 0x7ffffff0;         // a buffer offset past every range: loads return 0
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
 
-__device__ inline int swz(int row, int chunk) { return (row * ROWB) + ((chunk ^ (row & 7)) << 4); }
+// chunk c of row r sits at position c ^ (r mod 8) ^ ((r / 8) mod 8): eight
+// consecutive rows (the MFMA operand reads and the row-wise stores) and eight
+// rows 8 apart (the transposing stores) both land on eight distinct positions.
+__device__ inline int swz(int row, int chunk) {
+  return (row * ROWB) + ((chunk ^ (row & 7) ^ ((row >> 3) & 7)) << 4);
+}
 
 // A raw buffer resource: loads at offsets outside [0, bytes) return zero, so
 // ragged tiles need no branches.
@@ -99,37 +105,7 @@ struct RowTile {
       *reinterpret_cast<u32x4*>(lds + swz(id >> 3, id & 7)) = r[i];
     }
   }
-  // Stores RNE_bf16(s·v) (part 0) or RNE_bf16(s·v − part 0) (part 1) for the
-  // eight bf16 values v of each chunk: s·v ≈ part 0 + part 1 to ~2^-16.
-  __device__ inline void store_scaled(char* lds, int tid, float s, int part) const {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      u32x4 o;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float a = bits_to_float(r[i][d] << 16) * s;
-        const float b = bits_to_float(r[i][d] & 0xffff0000u) * s;
-        uint32_t h = pack_bf16x2(a, b);
-        if (part) h = pack_bf16x2(a - bits_to_float(h << 16), b - bits_to_float(h & 0xffff0000u));
-        o[d] = h;
-      }
-      const int id = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(lds + swz(id >> 3, id & 7)) = o;
-    }
-  }
 };
-
-// 8x8 transpose of 16-bit elements: in[i] is row i (8 values along the
-// reduction-major source), out[c] = column c.
-__device__ inline void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      out[c][d] = __builtin_amdgcn_perm(in[2 * d + 1][c >> 1], in[2 * d][c >> 1], sel);
-  }
-}
 
 // ---- B_BF16_RC: source [red][cols] row-major, NT == 256 -------------------------
 // Thread t owns an 8(red) x 8(cols) sub-block: red rows 8*(t/32).., cols 8*(t%32)..
@@ -167,17 +143,6 @@ struct RcTile {
     }
   }
 };
-
-__device__ inline u32x4 dequant8(uint32_t p, float ah, const float* __restrict__ cb) {
-  u32x4 o;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const float lo = cb[(p >> (8 * d)) & 15u] * ah;
-    const float hi = cb[(p >> (8 * d + 4)) & 15u] * ah;
-    o[d] = pack_bf16x2(lo, hi);
-  }
-  return o;
-}
 
 // ---- B_NF4_COLS: tile = NT rows of W (output cols) x 64 k --------------------------
 template <int NT>
@@ -220,7 +185,7 @@ struct Nf4ColsTile {
 #pragma unroll
     for (int d = 0; d < DW; ++d) {
       if (d % 4 != q) continue;
-      *reinterpret_cast<u32x4*>(lds + swz(row, part * DW + d)) = dequant8(p[d >> 2][d & 3], ah, cb);
+      *reinterpret_cast<u32x4*>(lds + swz(row, part * DW + d)) = decode8(p[d >> 2][d & 3], ah, cb);
     }
   }
 };
@@ -268,16 +233,68 @@ struct Nf4RedTile {
     for (int h = 0; h < 2; ++h) {
       const int c = 2 * q + h;
       u32x4 o;
+      const char* base = reinterpret_cast<const char*>(cbk);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const float lo = cbk[(p[2 * d] >> (4 * c)) & 15u] * ah[2 * d];
-        const float hi = cbk[(p[2 * d + 1] >> (4 * c)) & 15u] * ah[2 * d + 1];
+        const uint32_t ilo = (c >= 1 ? p[2 * d] >> (4 * c - 2) : p[2 * d] << 2) & 0x3cu;
+        const uint32_t ihi = (c >= 1 ? p[2 * d + 1] >> (4 * c - 2) : p[2 * d + 1] << 2) & 0x3cu;
+        const float lo = *reinterpret_cast<const float*>(base + ilo) * ah[2 * d];
+        const float hi = *reinterpret_cast<const float*>(base + ihi) * ah[2 * d + 1];
         o[d] = pack_bf16x2(lo, hi);
       }
       *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = o;
     }
   }
 };
+
+// A operand straight from memory into MFMA registers (no LDS round trip).
+// Lane l of a wave holds row 32 i + l % 32 of the wave's rows and, for the
+// four 16-deep MFMA steps ks of a 64-deep K tile, the reduction values
+// k0 + 32 h + 8 ks .. + 7 with h = l / 32.  That is a permutation of k within
+// the tile; the B operand reads use the same one (an MFMA sums its k slots in
+// any order), so each lane's four loads of a row are 64 contiguous bytes.
+template <int FM>
+struct ARegs {
+  u32x4 r[FM][4];
+  Buf buf;
+  int voff;     // byte offset of this lane's row in row block 0, at its k half
+  int istride;  // bytes between row blocks i and i + 1 (32 rows)
+  int h;
+
+  __device__ inline void init(const uint16_t* p, int64_t ld, int64_t nrows, int64_t row0,
+                              int lane) {
+    buf.init(p + row0 * ld, (nrows - row0) * ld * 2);
+    h = lane >> 5;
+    voff = (lane & 31) * (int)ld * 2 + h * 64;
+    istride = 32 * (int)ld * 2;
+  }
+  // Step ks of the K tile at k0; reduction values at or past kend read as zero.
+  __device__ inline void load_ks(int64_t k0, int64_t kend, int ks) {
+    const bool ok = k0 + 32 * h + 8 * ks < kend;
+    const int off = voff + (int)k0 * 2 + ks * 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) r[i][ks] = buf.ld16(ok ? off + i * istride : kOOB);
+  }
+  __device__ inline void load(int64_t k0, int64_t kend) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) load_ks(k0, kend, ks);
+  }
+};
+
+// bf16 pairs of v scaled by s: RNE_bf16(s·v) (part 0) or RNE_bf16(s·v − part 0)
+// (part 1); s·v ≈ part 0 + part 1 to ~2^-16.
+__device__ inline u32x4 scale_part(const u32x4& v, float s, int part) {
+  u32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float a = bits_to_float(v[d] << 16) * s;
+    const float b = bits_to_float(v[d] & 0xffff0000u) * s;
+    uint32_t h = pack_bf16x2(a, b);
+    if (part) h = pack_bf16x2(a - bits_to_float(h << 16), b - bits_to_float(h & 0xffff0000u));
+    o[d] = h;
+  }
+  return o;
+}
 
 template <int MT, int NT, int WM, int WN>
 struct Mma {
@@ -294,60 +311,53 @@ struct Mma {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   }
-  struct Frags {
-    bf16x8 a[FM], b[FN];
-  };
-  __device__ inline void load_frags(Frags& f, const char* As, const char* Bs, int wm, int wn,
-                                    int lane, int ks) const {
-    const int lr = lane & 31, lh = lane >> 5;
-    const int chunk = ks * 2 + lh;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      f.a[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * WTM + i * 32 + lr, chunk));
+  // B fragments of step ks from an LDS tile, in the k order of ARegs.
+  __device__ inline void load_b(bf16x8 (&b)[FN], const char* Bs, int wn, int lane, int ks) const {
+    const int chunk = 4 * (lane >> 5) + ks;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * WTN + j * 32 + lr, chunk));
+      b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * WTN + j * 32 + (lane & 31), chunk));
   }
-  __device__ inline void mfma(const Frags& f) {
+  // A fragments of step ks from an LDS tile (same k order as ARegs).
+  __device__ inline void load_a(bf16x8 (&a)[FM], const char* As, int wm, int lane, int ks) const {
+    const int chunk = 4 * (lane >> 5) + ks;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * WTM + i * 32 + (lane & 31), chunk));
+  }
+  __device__ inline void mfma(const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
-  // One 64-deep K tile from LDS.
-  __device__ inline void run(const char* As, const char* Bs, int wm, int wn, int lane) {
-    const int lr = lane & 31, lh = lane >> 5;
+  __device__ inline void mfma(const u32x4 (&a)[FM][4], int ks, const bf16x8 (&b)[FN]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int chunk = ks * 2 + lh;
-      bf16x8 af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * WTM + i * 32 + lr;
-        af[i] = *reinterpret_cast<const bf16x8*>(As + swz(row, chunk));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wn * WTN + j * 32 + lr;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(row, chunk));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i][ks]),
+                                                            b[j], acc[i][j], 0, 0, 0);
   }
 };
 
 }  // namespace
 
-template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE>
+template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE, int AMODE>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   static_assert(WM * WN == 4, "4 waves");
-  __shared__ __attribute__((aligned(16))) char lds[2 * (MT + NT) * ROWB];
-  __shared__ float cb[16];
+  using MmaT = Mma<MT, NT, WM, WN>;
+  constexpr int FM = MmaT::FM, FN = MmaT::FN, WTM = MmaT::WTM, WTN = MmaT::WTN;
+  // LDS: the 16-entry codebook at offset 0, then two stages of [A tile (when
+  // A is staged), B tile].
+  constexpr int CB_BYTES = 64;
+  constexpr int A_STAGE = AMODE == A_LDS ? MT * ROWB : 0;
+  constexpr int STAGE = A_STAGE + NT * ROWB;
+  __shared__ __attribute__((aligned(16))) char lds[CB_BYTES + 2 * STAGE];
+  float* cb = reinterpret_cast<float*>(lds);
+  auto As = [&](int st) { return lds + CB_BYTES + st * STAGE; };
+  auto Bs = [&](int st) { return lds + CB_BYTES + st * STAGE + A_STAGE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -357,42 +367,50 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     if (tid < 16) cb[tid] = bits_to_float(kNF4Bits[tid]);
   }
 
-  const int tile = blockIdx.x;
-  const int tm = tile % g.tiles_m, tn = tile / g.tiles_m;
+  // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+  // b mod 8).  Give each XCD a contiguous run of tiles in row-major order
+  // (N fastest), so the workgroups sharing an L2 share their A rows.
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = ntiles >> 3, rem = ntiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + slot;
+  const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
   const int64_t row0 = (int64_t)tm * MT, col0 = (int64_t)tn * NT;
+  const int64_t wrow0 = row0 + wm * WTM;  // this wave's first row
   const int nkt_total = (int)((g.red + KT - 1) / KT);
   const int kt_begin = blockIdx.y * g.kt_per_split;
   const int kt_end = min(nkt_total, kt_begin + g.kt_per_split);
 
-  // stage st: A tile at lds + st * STAGE, B tile right after it
-  constexpr int STAGE = (MT + NT) * ROWB;
-  auto As = [&](int st) { return lds + st * STAGE; };
-  auto Bs = [&](int st) { return lds + st * STAGE + MT * ROWB; };
-
-  Mma<MT, NT, WM, WN> mma;
+  MmaT mma;
   mma.zero();
 
   if constexpr (PROLOGUE) {
-    // acc = s · L·Rᵀ over the rank dimension.  s is applied to L while it is
-    // staged (two bf16 parts when s·L is not exact in one), never to acc.
+    // acc = s · L·Rᵀ over the rank dimension, L through registers (scaled by s
+    // there: two bf16 parts when s·L is not exact in one), R through LDS.
     if (blockIdx.y == 0 && g.rl > 0) {
-      RowTile<MT> lt;
+      ARegs<FM> la;
       RowTile<NT> rt;
-      lt.init(g.pl, g.ldpl, g.rows, row0, tid);
+      la.init(g.pl, g.ldpl, g.rows, wrow0, lane);
       rt.init(g.pr, g.ldpr, g.cols, col0, tid);
-      // one flat loop over (rank chunk, part): nested loops around the MFMAs
-      // make the register allocator spill the accumulators
-      const int nparts = 1 + g.s_split;
-      const int nsteps = (int)((g.rl + KT - 1) / KT) * nparts;
-      for (int st = 0; st < nsteps; ++st) {
-        const int64_t j0 = (int64_t)(st / nparts) * KT;
-        const int part = st % nparts;
-        lt.load(j0, g.rl, tid);
+      for (int64_t j0 = 0; j0 < g.rl; j0 += KT) {
+        la.load(j0, g.rl);
         rt.load(j0, g.rl, tid);
-        lt.store_scaled(As(0), tid, g.s, part);
         rt.store(Bs(0), tid);
         __syncthreads();
-        mma.run(As(0), Bs(0), wm, wn, lane);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 b[FN];
+          mma.load_b(b, Bs(0), wn, lane, ks);
+          u32x4 a[FM][4];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) a[i][ks] = scale_part(la.r[i][ks], g.s, 0);
+          mma.mfma(a, ks, b);
+          if (g.s_split) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i][ks] = scale_part(la.r[i][ks], g.s, 1);
+            mma.mfma(a, ks, b);
+          }
+        }
         __syncthreads();
       }
     }
@@ -403,13 +421,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       typename std::conditional<BMODE == B_NF4_RED, Nf4RedTile<NT>,
                                 typename std::conditional<BMODE == B_BF16_RC, RcTile<NT>,
                                                           RowTile<NT>>::type>::type>::type;
-  // Two register sets: while the MFMAs consume one LDS stage, the tile loaded
-  // one half-iteration earlier is decoded into the other stage and the next
-  // tile is in flight from memory.
-  RowTile<MT> a0, a1;
+  ARegs<(AMODE == A_DIRECT) ? FM : 1> a;
+  if constexpr (AMODE == A_DIRECT) a.init(g.a, g.lda, g.rows, wrow0, lane);
   BTile b0, b1;
-  a0.init(g.a, g.lda, g.rows, row0, tid);
-  a1.init(g.a, g.lda, g.rows, row0, tid);
   if constexpr (BMODE == B_NF4_COLS || BMODE == B_NF4_RED) {
     b0.init(g, col0, tid);
     b1.init(g, col0, tid);
@@ -419,9 +433,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
   const int64_t kend = min(g.red, (int64_t)kt_end * KT);  // this split's reduction bound
 
-  auto load_tiles = [&](RowTile<MT>& at, BTile& bt, int kt) {
+  auto load_b = [&](BTile& bt, int kt) {
     const int64_t k0 = (int64_t)kt * KT;
-    at.load(k0, kend, tid);
     if constexpr (BMODE == B_NF4_COLS) {
       bt.load(k0, kend);
     } else if constexpr (BMODE == B_NF4_RED) {
@@ -432,64 +445,115 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       bt.load(k0, kend, tid);
     }
   };
-  auto store_part = [&](const RowTile<MT>& at, const BTile& bt, int st, int q) {
-    at.store_part(As(st), tid, q);
+  auto store_b = [&](const BTile& bt, int st, int q) {
     if constexpr (BMODE == B_NF4_COLS || BMODE == B_NF4_RED)
       bt.store_part(Bs(st), tid, cb, q);
     else
       bt.store_part(Bs(st), tid, q);
   };
-  using MmaT = Mma<MT, NT, WM, WN>;
-  // One K tile of MFMAs from stage `cur`, with a quarter of the next tile's
-  // decode + LDS writes (into stage cur ^ 1) after each 64-deep quarter of
-  // MFMAs; fragments are read one quarter ahead.  sched_barrier keeps the
-  // compiler from regrouping the quarters.
-  auto step = [&](int cur, const RowTile<MT>& at, const BTile& bt) {
-    typename MmaT::Frags f0, f1;
-    mma.load_frags(f0, As(cur), Bs(cur), wm, wn, lane, 0);
+  // One K tile of MFMAs: A from registers, B from LDS stage `cur`.  After the
+  // MFMAs of each 16-deep step: that step's A registers are reloaded in place
+  // with tile kt_next, and a quarter of the next B tile is decoded into stage
+  // cur ^ 1.  B fragments are read one step ahead.  sched_barrier keeps the
+  // compiler from regrouping the steps.
+  auto step = [&](int cur, const BTile& bt_next, int kt_next) {
+    const int64_t kn = (int64_t)kt_next * KT;
+    bf16x8 f0[FN], f1[FN];
+    mma.load_b(f0, Bs(cur), wn, lane, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      typename MmaT::Frags& fc = (ks & 1) ? f1 : f0;
-      typename MmaT::Frags& fn = (ks & 1) ? f0 : f1;
-      if (ks < 3) mma.load_frags(fn, As(cur), Bs(cur), wm, wn, lane, ks + 1);
-      mma.mfma(fc);
-      store_part(at, bt, cur ^ 1, ks);
+      bf16x8(&fc)[FN] = (ks & 1) ? f1 : f0;
+      bf16x8(&fn)[FN] = (ks & 1) ? f0 : f1;
+      if (ks < 3) mma.load_b(fn, Bs(cur), wn, lane, ks + 1);
+      if constexpr (AMODE == A_DIRECT) {
+        mma.mfma(a.r, ks, fc);
+        a.load_ks(kn, kend, ks);
+      }
+      store_b(bt_next, cur ^ 1, ks);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (kt_begin < kt_end) {
-    __syncthreads();  // codebook visible
-    load_tiles(a0, b0, kt_begin);
-    load_tiles(a1, b1, kt_begin + 1);
+  if constexpr (AMODE == A_LDS) {
+    // A staged through LDS like B: global -> registers -> LDS, one tile ahead.
+    RowTile<MT> ra0, ra1;
+    ra0.init(g.a, g.lda, g.rows, row0, tid);
+    ra1.init(g.a, g.lda, g.rows, row0, tid);
+    auto stepl = [&](int cur, const RowTile<MT>& ra_next, const BTile& bt_next) {
+      bf16x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+      mma.load_a(fa0, As(cur), wm, lane, 0);
+      mma.load_b(fb0, Bs(cur), wn, lane, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store_part(a0, b0, 0, q);
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8(&ac)[FM] = (ks & 1) ? fa1 : fa0;
+        bf16x8(&an)[FM] = (ks & 1) ? fa0 : fa1;
+        bf16x8(&bc)[FN] = (ks & 1) ? fb1 : fb0;
+        bf16x8(&bn)[FN] = (ks & 1) ? fb0 : fb1;
+        if (ks < 3) {
+          mma.load_a(an, As(cur), wm, lane, ks + 1);
+          mma.load_b(bn, Bs(cur), wn, lane, ks + 1);
+        }
+        mma.mfma(ac, bc);
+        ra_next.store_part(As(cur ^ 1), tid, ks);
+        store_b(bt_next, cur ^ 1, ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (kt_begin < kt_end) {
+      __syncthreads();
+      ra0.load((int64_t)kt_begin * KT, kend, tid);
+      ra1.load((int64_t)(kt_begin + 1) * KT, kend, tid);
+      load_b(b0, kt_begin);
+      load_b(b1, kt_begin + 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ra0.store_part(As(0), tid, q);
+        store_b(b0, 0, q);
+      }
+      __syncthreads();
+      for (int kt = kt_begin; kt < kt_end; kt += 2) {
+        ra0.load((int64_t)(kt + 2) * KT, kend, tid);
+        load_b(b0, kt + 2);
+        stepl(0, ra1, b1);
+        __syncthreads();
+        ra1.load((int64_t)(kt + 3) * KT, kend, tid);
+        load_b(b1, kt + 3);
+        stepl(1, ra0, b0);
+        __syncthreads();
+      }
+    }
+  } else if (kt_begin < kt_end) {
+    __syncthreads();  // codebook visible, prologue done with stage 0
+    a.load((int64_t)kt_begin * KT, kend);
+    load_b(b0, kt_begin);
+    load_b(b1, kt_begin + 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_b(b0, 0, q);
     __syncthreads();
     // Branch-free: tiles past kt_end load as zeros, so an odd count ends with
     // one MFMA pass over a zero tile.
     for (int kt = kt_begin; kt < kt_end; kt += 2) {
-      load_tiles(a0, b0, kt + 2);
-      step(0, a1, b1);
+      load_b(b0, kt + 2);
+      step(0, b1, kt + 1);
       __syncthreads();
-      load_tiles(a1, b1, kt + 3);
-      step(1, a0, b0);
+      load_b(b1, kt + 3);
+      step(1, b0, kt + 2);
       __syncthreads();
     }
   }
 
   // Epilogue.  32x32 accumulator layout: lane l holds column l%32 and rows
   // 8*(e/4) + 4*(l/32) + e%4 for e = 0..15.
-  constexpr int WTM = MT / WM, WTN = NT / WN;
   const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < WTM / 32; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < WTN / 32; ++j) {
+    for (int j = 0; j < FN; ++j) {
       const int64_t col = col0 + wn * WTN + j * 32 + lr;
       if (col >= g.cols) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = row0 + wm * WTM + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+        const int64_t row = wrow0 + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
         if (row >= g.rows) continue;
         const float v = mma.acc[i][j][e];
         if constexpr (OMODE == O_BF16) {
@@ -502,14 +566,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 }
 
 // Instantiations used by the library.
-#define QLORA_GEMM(MT, NT, WM, WN, BM, PRO, OM) \
-  template __global__ void gemm_kernel<MT, NT, WM, WN, BM, PRO, OM>(GemmArgs);
+#define QLORA_GEMM(MT, NT, WM, WN, BM, PRO, OM, AM) \
+  template __global__ void gemm_kernel<MT, NT, WM, WN, BM, PRO, OM, AM>(GemmArgs);
 
-QLORA_GEMM(256, 256, 2, 2, B_NF4_COLS, true, O_BF16)   // forward, many tokens
-QLORA_GEMM(256, 256, 2, 2, B_NF4_RED, true, O_BF16)    // input gradient, many tokens
-QLORA_GEMM(64, 256, 1, 4, B_NF4_COLS, true, O_F32)     // forward, few tokens (split-K)
-QLORA_GEMM(64, 256, 1, 4, B_NF4_RED, true, O_F32)      // input gradient, few tokens
-QLORA_GEMM(128, 64, 4, 1, B_BF16_CR, false, O_F32)     // U = X·Aᵀ, V = dY·B (split-K)
-QLORA_GEMM(64, 256, 2, 2, B_BF16_RC, false, O_F32)     // dA, dB: reduction over tokens
+QLORA_GEMM(256, 256, 2, 2, B_NF4_COLS, true, O_BF16, A_LDS)     // forward, many tokens
+QLORA_GEMM(256, 256, 2, 2, B_NF4_RED, true, O_BF16, A_DIRECT)   // input gradient, many tokens
+QLORA_GEMM(64, 256, 1, 4, B_NF4_COLS, true, O_F32, A_DIRECT)    // forward, 17..127 tokens (split-K)
+QLORA_GEMM(64, 256, 1, 4, B_NF4_RED, true, O_F32, A_DIRECT)     // input gradient, 17..127 tokens
+QLORA_GEMM(128, 64, 4, 1, B_BF16_CR, false, O_F32, A_DIRECT)    // U = X·Aᵀ, V = dY·B (split-K)
+QLORA_GEMM(64, 256, 2, 2, B_BF16_RC, false, O_F32, A_DIRECT)    // dA, dB: reduction over tokens
 
 }  // namespace qlora

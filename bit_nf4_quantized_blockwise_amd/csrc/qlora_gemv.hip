@@ -21,7 +21,8 @@
 //     kb/64 + 1); the other entries are zero.  So C rows 0..7 hold the first
 //     block's partial sums and rows 8..15 the second's, and every lane scales
 //     the rows it holds by the scale of the block it loaded itself.
-// 8 waves split the reduction; partial sums meet in LDS once per 16 columns.
+// 8 waves split the reduction; each wave walks all of its workgroup's column
+// groups and the partial sums meet in LDS once, at the end.
 
 #include "qlora_kernels.h"
 
@@ -42,10 +43,10 @@ __device__ inline uint16_t bf16_rne_bits(float f) {
 
 }  // namespace
 
-template <int CPW, int MG>
+template <int CPW, int MG, int G>
 __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
-  __shared__ uint32_t lut[256 * 32];            // byte -> two bf16 levels, one copy per bank
-  __shared__ float red[2][8][MG][32][4];        // cross-wave partial sums, double-buffered
+  __shared__ uint32_t lut[256 * 32];        // byte -> two bf16 levels, one copy per bank
+  __shared__ float red[8][G][MG][32][4];    // per-wave partial sums, reduced once at the end
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
@@ -81,9 +82,18 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
   const int64_t ncg = (N + 15) / 16;
   const int64_t blocks_per_row = K >> 6;
   const __amdgpu_buffer_rsrc_t c2r = make_rsrc(g.c2, ((N * blocks_per_row + 255) >> 8) * 4);
-  int it = 0;
-  for (int64_t cg = blockIdx.x; cg < ncg; cg += gridDim.x, ++it) {
-    const int64_t n0 = cg * 16;
+  const int64_t cg0 = (int64_t)blockIdx.x * G;
+
+  // Every wave walks all G column groups of the workgroup on its own slice
+  // of the reduction; no workgroup barrier until the end, so the waves drift
+  // apart and one wave's loads overlap another's MFMAs.
+  floatx4 acc[G][MG];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) acc[gi][mg] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int64_t n0 = (cg0 + gi) * 16;
+    if (n0 >= N) continue;  // uniform
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.packed + n0 * (K >> 1), (N - n0) * (K >> 1));
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(g.qabsmax + n0 * blocks_per_row,
                                                 (N - n0) * blocks_per_row);
@@ -101,9 +111,6 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
           float, __builtin_amdgcn_raw_buffer_load_b32(c2r, (int)((gb >> 8) * 4), 0, 0));
       ah[c] = c2v * (float)qv;
     }
-    floatx4 acc[MG];
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg) acc[mg] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       floatx4 cb[MG];
@@ -124,89 +131,158 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mg][i] += ah[c] * cb[mg][i];
+        for (int i = 0; i < 4; ++i) acc[gi][mg][i] += ah[c] * cb[mg][i];
     }
-    // rows r and r + 8 hold the same token for the two blocks of each chunk
+  }
+  // rows r and r + 8 hold the same token for the two blocks of each chunk
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mg][i] += __shfl_xor(acc[mg][i], 32);
-    const int buf = it & 1;
-    if (lane < 32) {
+      for (int i = 0; i < 4; ++i) acc[gi][mg][i] += __shfl_xor(acc[gi][mg][i], 32);
+  if (lane < 32) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[buf][w][mg][lane][i] = acc[mg][i];
-    }
-    __syncthreads();
-    if (tid < 128 * MG) {
-      const int mg = tid >> 7, t = tid & 127, tok8 = t >> 4, col = t & 15;
-      float v = 0.0f;
+        for (int i = 0; i < 4; ++i) red[w][gi][mg][lane][i] = acc[gi][mg][i];
+  }
+  __syncthreads();
+  for (int o = tid; o < G * MG * 128; o += 512) {
+    const int gi = o / (MG * 128), mg = (o / 128) % MG, t = o & 127;
+    const int tok8 = t >> 4, col = t & 15;
+    float v = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < 8; ++ww) v += red[buf][ww][mg][col + 16 * (tok8 >> 2)][tok8 & 3];
-      const int tok = tok8 + 8 * mg;
-      const int64_t n = n0 + col;
-      if (tok < M && n < N) {
-        if (blockIdx.y == 0) {
-          float l = 0.0f;
-          for (int jr = 0; jr < g.r; ++jr)
-            l += bf16_bits_to_float(g.u[(int64_t)tok * g.r + jr]) *
-                 bf16_bits_to_float(g.b[n * g.r + jr]);
-          v += g.s * l;
-        }
-        if (g.ksplit == 1)
-          g.y[(int64_t)tok * N + n] = bf16_rne_bits(v);
-        else
-          g.part[((int64_t)blockIdx.y * M + tok) * N + n] = v;
+    for (int ww = 0; ww < 8; ++ww) v += red[ww][gi][mg][col + 16 * (tok8 >> 2)][tok8 & 3];
+    const int tok = tok8 + 8 * mg;
+    const int64_t n = (cg0 + gi) * 16 + col;
+    if (tok < M && n < N) {
+      if (blockIdx.y == 0) {
+        float l = 0.0f;
+        for (int jr = 0; jr < g.r; ++jr)
+          l += bf16_bits_to_float(g.u[(int64_t)tok * g.r + jr]) *
+               bf16_bits_to_float(g.b[n * g.r + jr]);
+        v += g.s * l;
       }
+      if (g.ksplit == 1)
+        g.y[(int64_t)tok * N + n] = bf16_rne_bits(v);
+      else
+        g.part[((int64_t)blockIdx.y * M + tok) * N + n] = v;
     }
   }
 }
 
 // U[m][j] = Σ_k X[m][k] · A[j][k] for M <= 16 tokens: one workgroup per rank
-// index j, 16-byte loads along k, fixed-order reduction.
+// index j; every load issued up front, then a fixed-order reduction through
+// LDS (no shuffle chains).
 __global__ __launch_bounds__(256) void lora_down_small_kernel(const uint16_t* __restrict__ x, int M,
                                                               int64_t K, const uint16_t* __restrict__ a,
                                                               int r, uint16_t* __restrict__ u) {
-  __shared__ float red[4][16];
+  __shared__ float red[16][257];
   const int j = blockIdx.x, tid = threadIdx.x;
   float acc[16];
 #pragma unroll
   for (int m = 0; m < 16; ++m) acc[m] = 0.0f;
-  for (int64_t k = (int64_t)tid * 8; k < K; k += 256 * 8) {
-    const u32x4 av = *reinterpret_cast<const u32x4*>(a + (int64_t)j * K + k);
+  for (int64_t k0 = (int64_t)tid * 8; k0 < K; k0 += 4 * 256 * 8) {
+    u32x4 av[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t k = k0 + (int64_t)s * 256 * 8;
+      av[s] = k < K ? *reinterpret_cast<const u32x4*>(a + (int64_t)j * K + k) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-      if (m < M) {
+      if (m >= M) continue;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t k = k0 + (int64_t)s * 256 * 8;
+        if (k >= K) continue;
         const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + k);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          acc[m] += bf16_bits_to_float(xv[d] & 0xffffu) * bf16_bits_to_float(av[d] & 0xffffu);
-          acc[m] += bf16_bits_to_float(xv[d] >> 16) * bf16_bits_to_float(av[d] >> 16);
+          acc[m] += bits_to_float(xv[d] << 16) * bits_to_float(av[s][d] << 16);
+          acc[m] += bits_to_float(xv[d] & 0xffff0000u) * bits_to_float(av[s][d] & 0xffff0000u);
         }
       }
     }
   }
 #pragma unroll
-  for (int m = 0; m < 16; ++m)
+  for (int m = 0; m < 16; ++m) red[m][tid] = acc[m];
+  __syncthreads();
+  {  // 256 threads: (m, part) sums 16 entries
+    const int m = tid >> 4, part = tid & 15;
+    float v = 0.0f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc[m] += __shfl_xor(acc[m], o);
-  if ((tid & 63) == 0)
-#pragma unroll
-    for (int m = 0; m < 16; ++m) red[tid >> 6][m] = acc[m];
+    for (int i = 0; i < 16; ++i) v += red[m][part * 16 + i];
+    __syncthreads();
+    red[m][part] = v;
+  }
   __syncthreads();
   if (tid < M) {
-    const float v = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v += red[tid][i];
     u[(int64_t)tid * r + j] = bf16_rne_bits(v);
   }
 }
 
-template __global__ void nf4_gemv_kernel<1, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 1>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 2>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 3>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 4>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 5>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 6>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 7>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 8>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 1>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 2>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 3>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 4>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 5>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 6>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 7>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 8>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 1>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 2>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 3>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 4>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 5>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 6>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 7>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 8>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 1>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 2>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 3>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 4>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 5>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 6>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 7>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 8>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 1>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 2>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 3>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 4>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 5>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 6>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 7>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 8>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 1>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 2>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 3>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 4>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 5>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 6>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 7>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 8>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 1>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 2>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 3>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 4>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 5>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 6>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 7>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 8>(GemvArgs);
 
 }  // namespace qlora

@@ -8,6 +8,7 @@ namespace qlora {
 
 enum BMode { B_NF4_COLS = 0, B_NF4_RED = 1, B_BF16_CR = 2, B_BF16_RC = 3 };
 enum OMode { O_BF16 = 0, O_F32 = 1 };
+enum AMode { A_LDS = 0, A_DIRECT = 1 };  // A operand staged through LDS or loaded into registers
 
 struct GemmArgs {
   const uint16_t* a;  // [rows][lda], reduction contiguous
@@ -57,10 +58,10 @@ struct GemvArgs {
   int32_t ksplit;
 };
 
-template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE>
+template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE, int AMODE>
 __global__ void gemm_kernel(GemmArgs g);
 
-template <int CPW, int MG>
+template <int CPW, int MG, int G>
 __global__ void nf4_gemv_kernel(GemvArgs g);
 
 __global__ void lora_down_small_kernel(const uint16_t* x, int M, int64_t K, const uint16_t* a,

@@ -272,12 +272,7 @@ __global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __r
     for (int u = 0; u < 4; ++u) {
       const int64_t i = base + threadIdx.x + 256 * u;
       u32x4 o;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float lo = cb[(p[u] >> (8 * d)) & 15u] * ah[u];
-        const float hi = cb[(p[u] >> (8 * d + 4)) & 15u] * ah[u];
-        o[d] = pack_bf16x2(lo, hi);
-      }
+      o = decode8(p[u], ah[u], cb);
       if (i < ndwords) __builtin_nontemporal_store(o, out + i);
     }
   }
