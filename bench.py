@@ -25,6 +25,112 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+GEMM_SOURCES = ["qlora_gemm.hip", "qlora_common.h", "qlora_kernels.h"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_gemm_fwd_llama7b_mlp.txt")
+CALIB_BYTES = 512 << 20  # plain device copy used to scale the byte counters
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "bit_nf4_quantized_blockwise_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the forward dequant-GEMM from the committed
+    counter summary, or None if absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_pmc(fetch_csv, write_csv, out_path):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the forward dequant-GEMM,
+    each scaled by what the same counter reads for a device copy of
+    CALIB_BYTES, written as a short text summary."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("gemm" if "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0>" in name else
+                   "copy" if "copyBuffer" in name else None)
+            if key:
+                vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+                vals[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    kib = CALIB_BYTES / 1024.0
+    f_scale = kib / f["copy"]
+    w_scale = kib / w["copy"]
+    fetch_b = f["gemm"] * f_scale * 1024.0
+    write_b = w["gemm"] * w_scale * 1024.0
+    M, K, N, r = 4096, 4096, 11008, 64
+    algo = N * K // 2 + N * K // 64 + ((N * K // 64 + 255) // 256) * 4 + 2 * M * K \
+        + 2 * M * r + 2 * N * r + 2 * M * N
+    with open(out_path, "w") as fh:
+        fh.write("# HBM traffic of the forward dequant-GEMM (LLaMA-7B MLP: 4096 tokens, 4096 -> 11008,\n")
+        fh.write("# r = 64), from rocprofv3 FETCH_SIZE and WRITE_SIZE (two --pmc runs of\n")
+        fh.write("# `python3 bench.py --pmc-pass`), each scaled by the same counter on a device\n")
+        fh.write(f"# copy of {CALIB_BYTES} bytes.\n")
+        fh.write(f"kernel_source_sha256_16 = {gemm_source_hash()}\n")
+        fh.write(f"fetch_kib_per_launch_raw = {f['gemm']:.1f}\n")
+        fh.write(f"write_kib_per_launch_raw = {w['gemm']:.1f}\n")
+        fh.write(f"copy_fetch_kib_raw = {f['copy']:.1f}\n")
+        fh.write(f"copy_write_kib_raw = {w['copy']:.1f}\n")
+        fh.write(f"fetch_scale = {f_scale:.4f}\n")
+        fh.write(f"write_scale = {w_scale:.4f}\n")
+        fh.write(f"fetch_bytes_per_launch = {fetch_b:.0f}\n")
+        fh.write(f"write_bytes_per_launch = {write_b:.0f}\n")
+        fh.write(f"traffic_bytes_per_launch = {fetch_b + write_b:.0f}\n")
+        fh.write(f"algorithmic_bytes_per_launch = {algo}\n")
+        fh.write(f"traffic_over_algorithmic = {(fetch_b + write_b) / algo:.3f}\n")
+    print(open(out_path).read())
+
+
+def pmc_pass():
+    """Short run for counter collection: the forward dequant-GEMM a few times
+    and a device copy of CALIB_BYTES (the byte counters' calibration)."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    wlc = wl.LLAMA7B_MLP
+    inp = wlc.inputs(with_dy=False)
+    wq = q.quantize_weight(torch.from_numpy(inp["W"]).to(dev))
+    X, A, B = (inp[k].to(dev) for k in ("X", "A", "B"))
+    ws = torch.empty(q.workspace_size(0, wlc.M, wlc.n_out, wlc.k_in, wlc.r), dtype=torch.uint8,
+                     device=dev)
+    U = q.lora_down(X, A)
+    Y = torch.empty(wlc.M, wlc.n_out, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        q.nf4_matmul_fwd(wq, X, U, B, wlc.alpha, workspace=ws, Y=Y)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("pmc pass done", flush=True)
 
 
 def _events():
@@ -53,12 +159,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="time only the training step")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="only run the forward dequant-GEMM and a calibration copy (counters)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the build has no multi-GPU path "
               "(the linear shards by tokens with one all-reduce of dA, dB; not built)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_pass:
+        pmc_pass()
+        return
 
     import numpy as np
     import torch
@@ -179,13 +296,13 @@ def main():
                    "fwd_ms": ms_fwd, "bwd_ms": ms_bwd},
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_kernel<256,256,2,2,B_NF4_COLS,prologue,bf16> (forward dequant-GEMM)",
+            "kernel": "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0> (forward dequant-GEMM)",
             "achieved": gemm_tflops,
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gemm_tflops / BF16_PEAK_TFLOPS,
             "ms": ms_gemm,
-            "traffic": None,
+            "traffic": read_traffic(),
         },
         "rows": rows,
         "cpu_baseline": cpu,
