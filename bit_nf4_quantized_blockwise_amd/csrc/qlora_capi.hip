@@ -321,7 +321,7 @@ qlora_status matmul_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64
   g.s_split = needs_split(s);
   if (use_big(M)) {
     g.out_bf16 = Y; g.ldo = N;
-    return run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_COLS, true, O_BF16, A_LDS>(
+    return run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_COLS, true, O_BF16, A_DMA>(
         g, plan(M, N, K, BIG_MT, BIG_NT, false), st);
   }
   g.out_f32 = reinterpret_cast<float*>(ws + L.y_part);
@@ -604,7 +604,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const qlora_bf16* X, co
     g.s_split = needs_split(sc);
     if (use_big(M)) {
       g.out_bf16 = dX; g.ldo = K;
-      s = run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_RED, true, O_BF16>(
+      s = run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_RED, true, O_BF16, A_DMA>(
           g, plan(M, K, N, BIG_MT, BIG_NT, false), st);
       if (s != QLORA_OK) return s;
     } else {

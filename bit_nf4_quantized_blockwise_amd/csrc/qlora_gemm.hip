@@ -188,6 +188,34 @@ struct Nf4ColsTile {
       *reinterpret_cast<u32x4*>(lds + swz(row, part * DW + d)) = decode8(p[d >> 2][d & 3], ah, cb);
     }
   }
+  // The same quarter in two phases, so the codebook reads can be issued a
+  // quarter before their use: lookup() gathers c[idx] (fp32), finish() scales,
+  // rounds to bf16 and stores.
+  __device__ inline void lookup(int q, float (&v)[16], const float* cb) const {
+    const char* base = reinterpret_cast<const char*>(cb);
+#pragma unroll
+    for (int d = 0, n = 0; d < DW; ++d) {
+      if (d % 4 != q) continue;
+      const uint32_t w = p[d >> 2][d & 3];
+      const uint32_t ev = (w << 2) & 0x3c3c3c3cu, od = (w >> 2) & 0x3c3c3c3cu;
+#pragma unroll
+      for (int b = 0; b < 4; ++b, n += 2) {
+        v[n] = *reinterpret_cast<const float*>(base + ((ev >> (8 * b)) & 0xffu));
+        v[n + 1] = *reinterpret_cast<const float*>(base + ((od >> (8 * b)) & 0xffu));
+      }
+    }
+  }
+  __device__ inline void finish(int q, const float (&v)[16], char* lds, int tid) const {
+    const int row = tid / TPR, part = tid % TPR;
+#pragma unroll
+    for (int d = 0, n = 0; d < DW; ++d) {
+      if (d % 4 != q) continue;
+      u32x4 o;
+#pragma unroll
+      for (int b = 0; b < 4; ++b, n += 2) o[b] = pack_bf16x2(v[n] * ah, v[n + 1] * ah);
+      *reinterpret_cast<u32x4*>(lds + swz(row, part * DW + d)) = o;
+    }
+  }
 };
 
 // ---- B_NF4_RED: tile = 64 rows of W (reduction) x NT columns of W (output) -------
@@ -245,7 +273,71 @@ struct Nf4RedTile {
       *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = o;
     }
   }
+  __device__ inline void lookup(int q, float (&v)[16], const float* cbk) const {
+    const char* base = reinterpret_cast<const char*>(cbk);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 2 * q + h;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t ix = (c >= 1 ? p[i] >> (4 * c - 2) : p[i] << 2) & 0x3cu;
+        v[8 * h + i] = *reinterpret_cast<const float*>(base + ix);
+      }
+    }
+  }
+  __device__ inline void finish(int q, const float (&v)[16], char* lds, int tid) const {
+    const int rb = tid >> 5, cb = tid & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 2 * q + h;
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        o[d] = pack_bf16x2(v[8 * h + 2 * d] * ah[2 * d], v[8 * h + 2 * d + 1] * ah[2 * d + 1]);
+      *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = o;
+    }
+  }
 };
+
+// A tile staged by direct-to-LDS buffer loads (no VGPRs).  A wave-wide
+// 16-byte load writes lane l's data at LDS offset 16 l, i.e. 8 rows x 128 B;
+// the LDS swizzle is applied on the global side: the lane landing in chunk
+// position pc of row r fetches logical chunk pc ^ f(r).  The tile's MT / 8
+// such loads are split over the 4 waves.
+template <int MT>
+struct ADma {
+  static constexpr int PER_W = MT / 32;
+  Buf buf;
+  int vrow;    // byte offset of this lane's row in the wave's first load
+  int c16;     // 16 * (chunk position ^ row swizzle of the first load)
+  int jstep;   // bytes between the rows of consecutive loads (8 rows)
+
+  __device__ inline void init(const uint16_t* p, int64_t ld, int64_t nrows, int64_t row0,
+                              int wave, int lane) {
+    buf.init(p + row0 * ld, (nrows - row0) * ld * 2);
+    // Row of load j: (wave * PER_W + j) * 8 + lane / 8, so row & 7 = lane / 8 and
+    // (row / 8) & 7 = (wave * PER_W + j) & 7 = j & 7 when PER_W is a multiple of 8.
+    static_assert(PER_W % 8 == 0, "A tile loads must cover whole swizzle periods");
+    vrow = (wave * PER_W * 8 + (lane >> 3)) * (int)ld * 2;
+    c16 = ((lane & 7) ^ (lane >> 3)) << 4;
+    jstep = 8 * (int)ld * 2;
+  }
+  __device__ inline void issue(char* stage, int wave, int64_t k0, int64_t kend) const {
+    const int kb = (int)k0 * 2, kendb = (int)kend * 2;
+#pragma unroll
+    for (int j = 0; j < PER_W; ++j) {
+      const int cj = c16 ^ ((j & 7) << 4);
+      const int off = (kb + cj < kendb) ? vrow + j * jstep + kb + cj : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          buf.r, (__attribute__((address_space(3))) void*)(stage + (wave * PER_W + j) * 1024), 16,
+          off, 0, 0, 0);
+    }
+  }
+};
+
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left alone): the direct-to-LDS loads,
+// which no register dependency tracks, have landed.
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // A operand straight from memory into MFMA registers (no LDS round trip).
 // Lane l of a wave holds row 32 i + l % 32 of the wave's rows and, for the
@@ -352,7 +444,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   // LDS: the 16-entry codebook at offset 0, then two stages of [A tile (when
   // A is staged), B tile].
   constexpr int CB_BYTES = 64;
-  constexpr int A_STAGE = AMODE == A_LDS ? MT * ROWB : 0;
+  constexpr int A_STAGE = AMODE == A_DMA ? MT * ROWB : 0;
   constexpr int STAGE = A_STAGE + NT * ROWB;
   __shared__ __attribute__((aligned(16))) char lds[CB_BYTES + 2 * STAGE];
   float* cb = reinterpret_cast<float*>(lds);
@@ -474,51 +566,61 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   };
 
-  if constexpr (AMODE == A_LDS) {
-    // A staged through LDS like B: global -> registers -> LDS, one tile ahead.
-    RowTile<MT> ra0, ra1;
-    ra0.init(g.a, g.lda, g.rows, row0, tid);
-    ra1.init(g.a, g.lda, g.rows, row0, tid);
-    auto stepl = [&](int cur, const RowTile<MT>& ra_next, const BTile& bt_next) {
+  if constexpr (AMODE == A_DMA) {
+    // A by direct-to-LDS loads one tile ahead; B decoded from registers into
+    // the other stage while the MFMAs run, its codebook reads a quarter ahead.
+    ADma<MT> adma;
+    adma.init(g.a, g.lda, g.rows, row0, wave, lane);
+    constexpr bool kNf4 = BMODE == B_NF4_COLS;
+    auto stepd = [&](int cur, const BTile& bt_next) {
       bf16x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+      float lk0[16], lk1[16];
       mma.load_a(fa0, As(cur), wm, lane, 0);
       mma.load_b(fb0, Bs(cur), wn, lane, 0);
+      if constexpr (kNf4) bt_next.lookup(0, lk0, cb);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8(&ac)[FM] = (ks & 1) ? fa1 : fa0;
         bf16x8(&an)[FM] = (ks & 1) ? fa0 : fa1;
         bf16x8(&bc)[FN] = (ks & 1) ? fb1 : fb0;
         bf16x8(&bn)[FN] = (ks & 1) ? fb0 : fb1;
+        float(&lc)[16] = (ks & 1) ? lk1 : lk0;
+        float(&ln)[16] = (ks & 1) ? lk0 : lk1;
         if (ks < 3) {
           mma.load_a(an, As(cur), wm, lane, ks + 1);
           mma.load_b(bn, Bs(cur), wn, lane, ks + 1);
         }
         mma.mfma(ac, bc);
-        ra_next.store_part(As(cur ^ 1), tid, ks);
-        store_b(bt_next, cur ^ 1, ks);
+        if constexpr (kNf4) {
+          if (ks < 3) bt_next.lookup(ks + 1, ln, cb);
+          bt_next.finish(ks, lc, Bs(cur ^ 1), tid);
+        } else {
+          store_b(bt_next, cur ^ 1, ks);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (kt_begin < kt_end) {
-      __syncthreads();
-      ra0.load((int64_t)kt_begin * KT, kend, tid);
-      ra1.load((int64_t)(kt_begin + 1) * KT, kend, tid);
+      __syncthreads();  // codebook visible, prologue done with stage 0
+      adma.issue(As(0), wave, (int64_t)kt_begin * KT, kend);
       load_b(b0, kt_begin);
       load_b(b1, kt_begin + 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ra0.store_part(As(0), tid, q);
-        store_b(b0, 0, q);
-      }
+      for (int q = 0; q < 4; ++q) store_b(b0, 0, q);
+      wait_vmem_all();
       __syncthreads();
+      // Branch-free: tiles past kt_end load as zeros, so an odd count ends
+      // with one MFMA pass over a zero tile.
       for (int kt = kt_begin; kt < kt_end; kt += 2) {
-        ra0.load((int64_t)(kt + 2) * KT, kend, tid);
+        adma.issue(As(1), wave, (int64_t)(kt + 1) * KT, kend);
         load_b(b0, kt + 2);
-        stepl(0, ra1, b1);
+        stepd(0, b1);
+        wait_vmem_all();
         __syncthreads();
-        ra1.load((int64_t)(kt + 3) * KT, kend, tid);
+        adma.issue(As(0), wave, (int64_t)(kt + 2) * KT, kend);
         load_b(b1, kt + 3);
-        stepl(1, ra0, b0);
+        stepd(1, b0);
+        wait_vmem_all();
         __syncthreads();
       }
     }
@@ -569,8 +671,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #define QLORA_GEMM(MT, NT, WM, WN, BM, PRO, OM, AM) \
   template __global__ void gemm_kernel<MT, NT, WM, WN, BM, PRO, OM, AM>(GemmArgs);
 
-QLORA_GEMM(256, 256, 2, 2, B_NF4_COLS, true, O_BF16, A_LDS)     // forward, many tokens
-QLORA_GEMM(256, 256, 2, 2, B_NF4_RED, true, O_BF16, A_DIRECT)   // input gradient, many tokens
+QLORA_GEMM(256, 256, 2, 2, B_NF4_COLS, true, O_BF16, A_DMA)     // forward, many tokens
+QLORA_GEMM(256, 256, 2, 2, B_NF4_RED, true, O_BF16, A_DMA)     // input gradient, many tokens
 QLORA_GEMM(64, 256, 1, 4, B_NF4_COLS, true, O_F32, A_DIRECT)    // forward, 17..127 tokens (split-K)
 QLORA_GEMM(64, 256, 1, 4, B_NF4_RED, true, O_F32, A_DIRECT)     // input gradient, 17..127 tokens
 QLORA_GEMM(128, 64, 4, 1, B_BF16_CR, false, O_F32, A_DIRECT)    // U = X·Aᵀ, V = dY·B (split-K)

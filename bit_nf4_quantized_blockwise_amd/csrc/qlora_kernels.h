@@ -8,7 +8,8 @@ namespace qlora {
 
 enum BMode { B_NF4_COLS = 0, B_NF4_RED = 1, B_BF16_CR = 2, B_BF16_RC = 3 };
 enum OMode { O_BF16 = 0, O_F32 = 1 };
-enum AMode { A_LDS = 0, A_DIRECT = 1 };  // A operand staged through LDS or loaded into registers
+// A operand: staged in LDS by direct-to-LDS loads, or loaded into MFMA registers
+enum AMode { A_DMA = 0, A_DIRECT = 1 };
 
 struct GemmArgs {
   const uint16_t* a;  // [rows][lda], reduction contiguous
