@@ -45,6 +45,12 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9
 __device__ inline int swz(int row, int chunk) {
   return (row * ROWB) + ((chunk ^ (row & 7) ^ ((row >> 3) & 7)) << 4);
 }
+// The A tile is only written row-wise (by direct-to-LDS loads) and read as
+// MFMA operands, so the position depends on r mod 8 alone; a load of eight
+// rows then needs the same source chunk order for every row group.
+__device__ inline int swz_a(int row, int chunk) {
+  return (row * ROWB) + ((chunk ^ (row & 7)) << 4);
+}
 
 // A raw buffer resource: loads at offsets outside [0, bytes) return zero, so
 // ragged tiles need no branches.
@@ -151,7 +157,9 @@ struct Nf4ColsTile {
   static constexpr int DW = 8 / TPR;          // packed dwords per thread
   static_assert(NT == 256 || NT == 128, "NF4 column loader: NT in {128, 256}");
   u32x4 p[DW / 4];
-  float ah;
+  uint32_t qraw;  // DQ code of this thread's block
+  float s2;       // its group's second-level step
+  float ah;       // c2 · q, set by prep()
   Buf pk, qa, c2;
   int row_off, q_off;
   int64_t gblk0;  // global block index of this thread's row at k = 0
@@ -166,16 +174,18 @@ struct Nf4ColsTile {
     q_off = row * (int)bpr;
     gblk0 = (n0 + row) * bpr;
   }
+  // Issues the loads only; nothing here waits for them.
   __device__ inline void load(int64_t k0, int64_t kend) {
     const int kb = (int)(k0 >> 6);
     const bool ok = k0 < kend;  // uniform: tiles past this split's range read as zero
 #pragma unroll
     for (int d = 0; d < DW / 4; ++d) p[d] = pk.ld16(ok ? row_off + (int)(k0 >> 1) + 16 * d : kOOB);
-    const uint32_t q = qa.ld1(ok ? q_off + kb : kOOB);
-    const float s2 = bits_to_float(c2.ld4((int)(((gblk0 + kb) >> 8) * 4)));
-    ah = s2 * (float)q;
+    qraw = qa.ld1(ok ? q_off + kb : kOOB);
+    s2 = bits_to_float(c2.ld4((int)(((gblk0 + kb) >> 8) * 4)));
   }
-  __device__ inline void store(char* lds, int tid, const float* cb) const {
+  __device__ inline void prep() { ah = s2 * (float)qraw; }
+  __device__ inline void store(char* lds, int tid, const float* cb) {
+    prep();
 #pragma unroll
     for (int q = 0; q < 4; ++q) store_part(lds, tid, cb, q);
   }
@@ -190,14 +200,18 @@ struct Nf4ColsTile {
   }
   // The same quarter in two phases, so the codebook reads can be issued a
   // quarter before their use: lookup() gathers c[idx] (fp32), finish() scales,
-  // rounds to bf16 and stores.
+  // rounds to bf16 and stores.  The nibbles are first spread to byte offsets
+  // 4·idx (even elements in one dword, odd in another); the empty asm keeps
+  // the compiler from folding that back into a shift-and-mask per element, so
+  // each lookup address is a single byte extract.
   __device__ inline void lookup(int q, float (&v)[16], const float* cb) const {
     const char* base = reinterpret_cast<const char*>(cb);
 #pragma unroll
     for (int d = 0, n = 0; d < DW; ++d) {
       if (d % 4 != q) continue;
       const uint32_t w = p[d >> 2][d & 3];
-      const uint32_t ev = (w << 2) & 0x3c3c3c3cu, od = (w >> 2) & 0x3c3c3c3cu;
+      uint32_t ev = (w << 2) & 0x3c3c3c3cu, od = (w >> 2) & 0x3c3c3c3cu;
+      asm("" : "+v"(ev), "+v"(od));
 #pragma unroll
       for (int b = 0; b < 4; ++b, n += 2) {
         v[n] = *reinterpret_cast<const float*>(base + ((ev >> (8 * b)) & 0xffu));
@@ -223,8 +237,9 @@ struct Nf4ColsTile {
 template <int NT>
 struct Nf4RedTile {
   static_assert(NT == 256, "NF4 reduction-major loader assumes 256 columns");
-  uint32_t p[8];
-  float ah[8];
+  uint32_t p[8];     // packed dword of each of the 8 rows; after prep(): 4·idx of even nibbles
+  uint32_t od[8];    // after prep(): 4·idx of odd nibbles
+  uint32_t qraw[8];  // DQ codes; after prep() the block scales (float bits)
   Buf c2;
   int64_t k;  // first W column of this thread
 
@@ -232,6 +247,9 @@ struct Nf4RedTile {
     k = c0 + (tid & 31) * 8;
     c2.init(g.c2, ((g.red * (g.w_kin >> 6) + 255) >> 8) * 4);
   }
+  // Issues the loads only.  The DQ code and the step of each row are folded
+  // into the row's block scale by prep(), once they have arrived.
+  float s2[8];
   __device__ inline void load(const GemmArgs& g, int64_t r0, int64_t rend, int tid) {
     const int rb = tid >> 5;
     const int64_t bpr = g.w_kin >> 6;
@@ -244,45 +262,44 @@ struct Nf4RedTile {
       const int n = rb * 8 + i;
       p[i] = pk.ld4(ok ? n * (int)(g.w_kin >> 1) + (int)(k >> 1) : kOOB);
       const int lb = n * (int)bpr + (int)(k >> 6);
-      const uint32_t q = qa.ld1(ok ? lb : kOOB);
-      const float s2 = bits_to_float(c2.ld4((int)((((r0 + n) * bpr + (k >> 6)) >> 8) * 4)));
-      ah[i] = s2 * (float)q;
+      qraw[i] = qa.ld1(ok ? lb : kOOB);
+      s2[i] = bits_to_float(c2.ld4((int)((((r0 + n) * bpr + (k >> 6)) >> 8) * 4)));
     }
   }
-  __device__ inline void store(char* lds, int tid, const float* cbk) const {
+  __device__ inline void prep() {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store_part(lds, tid, cbk, q);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = p[i];
+      uint32_t e = (w << 2) & 0x3c3c3c3cu, o = (w >> 2) & 0x3c3c3c3cu;
+      asm("" : "+v"(e), "+v"(o));
+      p[i] = e;
+      od[i] = o;
+      qraw[i] = float_to_bits(s2[i] * (float)qraw[i]);
+    }
+  }
+  __device__ inline float ah(int i) const { return bits_to_float(qraw[i]); }
+  __device__ inline void store(char* lds, int tid, const float* cbk) {
+    prep();
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lookup(q, v, cbk);
+      finish(q, v, lds, tid);
+    }
+  }
+  __device__ inline void store_part(char* lds, int tid, const float* cbk, int q) const {
+    float v[16];
+    lookup(q, v, cbk);
+    finish(q, v, lds, tid);
   }
   // Quarter q: output columns c = 2q, 2q + 1 — W column k + c decoded from
   // nibble c of each of the 8 W rows (the transpose falls out of the lookup).
-  __device__ inline void store_part(char* lds, int tid, const float* cbk, int q) const {
-    const int rb = tid >> 5, cb = tid & 31;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 2 * q + h;
-      u32x4 o;
-      const char* base = reinterpret_cast<const char*>(cbk);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t ilo = (c >= 1 ? p[2 * d] >> (4 * c - 2) : p[2 * d] << 2) & 0x3cu;
-        const uint32_t ihi = (c >= 1 ? p[2 * d + 1] >> (4 * c - 2) : p[2 * d + 1] << 2) & 0x3cu;
-        const float lo = *reinterpret_cast<const float*>(base + ilo) * ah[2 * d];
-        const float hi = *reinterpret_cast<const float*>(base + ihi) * ah[2 * d + 1];
-        o[d] = pack_bf16x2(lo, hi);
-      }
-      *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = o;
-    }
-  }
   __device__ inline void lookup(int q, float (&v)[16], const float* cbk) const {
     const char* base = reinterpret_cast<const char*>(cbk);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 2 * q + h;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t ix = (c >= 1 ? p[i] >> (4 * c - 2) : p[i] << 2) & 0x3cu;
-        v[8 * h + i] = *reinterpret_cast<const float*>(base + ix);
-      }
+    for (int i = 0; i < 8; ++i) {
+      v[i] = *reinterpret_cast<const float*>(base + ((p[i] >> (8 * q)) & 0xffu));
+      v[8 + i] = *reinterpret_cast<const float*>(base + ((od[i] >> (8 * q)) & 0xffu));
     }
   }
   __device__ inline void finish(int q, const float (&v)[16], char* lds, int tid) const {
@@ -293,7 +310,7 @@ struct Nf4RedTile {
       u32x4 o;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
-        o[d] = pack_bf16x2(v[8 * h + 2 * d] * ah[2 * d], v[8 * h + 2 * d + 1] * ah[2 * d + 1]);
+        o[d] = pack_bf16x2(v[8 * h + 2 * d] * ah(2 * d), v[8 * h + 2 * d + 1] * ah(2 * d + 1));
       *reinterpret_cast<u32x4*>(lds + swz(cb * 8 + c, rb)) = o;
     }
   }
@@ -308,29 +325,37 @@ template <int MT>
 struct ADma {
   static constexpr int PER_W = MT / 32;
   Buf buf;
-  int vrow;    // byte offset of this lane's row in the wave's first load
-  int c16;     // 16 * (chunk position ^ row swizzle of the first load)
-  int jstep;   // bytes between the rows of consecutive loads (8 rows)
+  int voff;   // byte offset of this lane's 16 bytes in the wave's first load, at k = 0
+  int kc;     // 2 · (first k of this lane's chunk within the tile)
+  int jstep;  // bytes between the rows of consecutive loads (8 rows)
+  int lbase;  // LDS byte offset of the wave's first load within a stage (uniform)
 
   __device__ inline void init(const uint16_t* p, int64_t ld, int64_t nrows, int64_t row0,
                               int wave, int lane) {
     buf.init(p + row0 * ld, (nrows - row0) * ld * 2);
-    // Row of load j: (wave * PER_W + j) * 8 + lane / 8, so row & 7 = lane / 8 and
-    // (row / 8) & 7 = (wave * PER_W + j) & 7 = j & 7 when PER_W is a multiple of 8.
-    static_assert(PER_W % 8 == 0, "A tile loads must cover whole swizzle periods");
-    vrow = (wave * PER_W * 8 + (lane >> 3)) * (int)ld * 2;
-    c16 = ((lane & 7) ^ (lane >> 3)) << 4;
+    // Load j of this wave covers rows (wave · PER_W + j) · 8 + lane / 8, whose
+    // r mod 8 is lane / 8; the lane fetches the chunk that lands at its slot.
+    const int c = (lane & 7) ^ (lane >> 3);
+    kc = c * 16;
+    voff = (wave * PER_W * 8 + (lane >> 3)) * (int)ld * 2 + kc;
     jstep = 8 * (int)ld * 2;
+    lbase = __builtin_amdgcn_readfirstlane(wave) * PER_W * 1024;
   }
-  __device__ inline void issue(char* stage, int wave, int64_t k0, int64_t kend) const {
+  __device__ inline void issue(char* stage, int64_t k0, int64_t kend) const {
     const int kb = (int)k0 * 2, kendb = (int)kend * 2;
+    if (kb + KT * 2 <= kendb) {  // whole tile inside the reduction range (uniform)
 #pragma unroll
-    for (int j = 0; j < PER_W; ++j) {
-      const int cj = c16 ^ ((j & 7) << 4);
-      const int off = (kb + cj < kendb) ? vrow + j * jstep + kb + cj : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          buf.r, (__attribute__((address_space(3))) void*)(stage + (wave * PER_W + j) * 1024), 16,
-          off, 0, 0, 0);
+      for (int j = 0; j < PER_W; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            buf.r, (__attribute__((address_space(3))) void*)(stage + lbase + j * 1024), 16,
+            voff + (j * jstep + kb), 0, 0, 0);
+    } else {
+      const int off = kb + kc < kendb ? voff + kb : kOOB;
+#pragma unroll
+      for (int j = 0; j < PER_W; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            buf.r, (__attribute__((address_space(3))) void*)(stage + lbase + j * 1024), 16,
+            off == kOOB ? kOOB : off + j * jstep, 0, 0, 0);
     }
   }
 };
@@ -388,6 +413,22 @@ __device__ inline u32x4 scale_part(const u32x4& v, float s, int part) {
   return o;
 }
 
+// Scheduling pattern for one region of the main loop: each MFMA followed by
+// up to two LDS reads, one VMEM instruction and four VALU instructions, with
+// the LDS writes spread in.  One wave per SIMD issues in order, so VALU work
+// placed between MFMAs runs while the matrix core is busy instead of after it.
+template <int NMFMA>
+__device__ inline void interleave() {
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+  }
+}
+
 template <int MT, int NT, int WM, int WN>
 struct Mma {
   static constexpr int WTM = MT / WM, WTN = NT / WN;
@@ -415,7 +456,7 @@ struct Mma {
     const int chunk = 4 * (lane >> 5) + ks;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * WTM + i * 32 + (lane & 31), chunk));
+      a[i] = *reinterpret_cast<const bf16x8*>(As + swz_a(wm * WTM + i * 32 + (lane & 31), chunk));
   }
   __device__ inline void mfma(const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
 #pragma unroll
@@ -452,7 +493,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   auto Bs = [&](int st) { return lds + CB_BYTES + st * STAGE + A_STAGE; };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform; saying so keeps everything derived from it
+  // (tile corners, buffer resources, row offsets) in scalar registers.
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   if constexpr (BMODE == B_NF4_COLS || BMODE == B_NF4_RED) {
@@ -466,7 +509,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int per = ntiles >> 3, rem = ntiles & 7;
   const int tile = xcd * per + min(xcd, rem) + slot;
-  const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
+  // (The divisions expand to vector code; readfirstlane brings the results
+  // back to scalar registers, so buffer resources built from them are too.)
+  const int tm = __builtin_amdgcn_readfirstlane(tile / g.tiles_n);
+  const int tn = __builtin_amdgcn_readfirstlane(tile - tm * g.tiles_n);
   const int64_t row0 = (int64_t)tm * MT, col0 = (int64_t)tn * NT;
   const int64_t wrow0 = row0 + wm * WTM;  // this wave's first row
   const int nkt_total = (int)((g.red + KT - 1) / KT);
@@ -537,18 +583,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       bt.load(k0, kend, tid);
     }
   };
-  auto store_b = [&](const BTile& bt, int st, int q) {
-    if constexpr (BMODE == B_NF4_COLS || BMODE == B_NF4_RED)
+  // Quarter q of a B tile into stage st; the NF4 tiles fold their scales
+  // (prep) before the first quarter, once per load.
+  auto store_b = [&](BTile& bt, int st, int q) {
+    if constexpr (BMODE == B_NF4_COLS || BMODE == B_NF4_RED) {
+      if (q == 0) bt.prep();
       bt.store_part(Bs(st), tid, cb, q);
-    else
+    } else {
       bt.store_part(Bs(st), tid, q);
+    }
   };
   // One K tile of MFMAs: A from registers, B from LDS stage `cur`.  After the
   // MFMAs of each 16-deep step: that step's A registers are reloaded in place
   // with tile kt_next, and a quarter of the next B tile is decoded into stage
   // cur ^ 1.  B fragments are read one step ahead.  sched_barrier keeps the
   // compiler from regrouping the steps.
-  auto step = [&](int cur, const BTile& bt_next, int kt_next) {
+  auto step = [&](int cur, BTile& bt_next, int kt_next) {
     const int64_t kn = (int64_t)kt_next * KT;
     bf16x8 f0[FN], f1[FN];
     mma.load_b(f0, Bs(cur), wn, lane, 0);
@@ -567,61 +617,97 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   };
 
   if constexpr (AMODE == A_DMA) {
-    // A by direct-to-LDS loads one tile ahead; B decoded from registers into
-    // the other stage while the MFMAs run, its codebook reads a quarter ahead.
+    // A arrives by direct-to-LDS loads, B is decoded from registers into the
+    // stage not being read.  Per K tile (stage cur, B registers D holding
+    // the next tile, N the one after):
+    //   quarters 0-2: fragments of step ks+1 and the codebook reads of
+    //                 quarter ks+1 are issued, then the MFMAs of step ks run
+    //                 beside the scaling/rounding/stores of quarter ks;
+    //   quarter 3:    half the MFMAs beside the last quarter's decode, then the
+    //                 one barrier of the tile; after it the A loads of tile +2
+    //                 go to stage cur, D is reloaded with tile +3, and the first
+    //                 fragments of the next stage and codebook reads of N are
+    //                 issued before the second half of the MFMAs, which use
+    //                 registers only.
+    // The barrier needs this wave's A loads landed (vmcnt 0: they and the B
+    // loads issued with them are a whole tile old by then).
     ADma<MT> adma;
     adma.init(g.a, g.lda, g.rows, row0, wave, lane);
-    constexpr bool kNf4 = BMODE == B_NF4_COLS;
-    auto stepd = [&](int cur, const BTile& bt_next) {
-      bf16x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
-      float lk0[16], lk1[16];
-      mma.load_a(fa0, As(cur), wm, lane, 0);
-      mma.load_b(fb0, Bs(cur), wn, lane, 0);
-      if constexpr (kNf4) bt_next.lookup(0, lk0, cb);
+    bf16x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+    float lk0[16], lk1[16];
+    // Codebook reads a quarter ahead where registers allow (column tiles: one
+    // block per thread); the reduction-major tile, with eight block scales per
+    // thread, reads and finishes each quarter in place.
+    constexpr bool kAhead = BMODE == B_NF4_COLS;
+    auto lookup = [&](const BTile& bt, int q, float (&v)[16]) {
+      if constexpr (kAhead) bt.lookup(q, v, cb);
+    };
+    auto finish = [&](const BTile& bt, int q, const float (&v)[16], int st) {
+      if constexpr (kAhead)
+        bt.finish(q, v, Bs(st), tid);
+      else if constexpr (BMODE == B_NF4_RED)
+        bt.store_part(Bs(st), tid, cb, q);
+    };
+    auto mfma_half = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN], int h) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if ((i * FN + j) * 2 / (FM * FN) == h)
+            mma.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], mma.acc[i][j], 0, 0, 0);
+    };
+    auto stepd = [&](int cur, BTile& D, BTile& N, int kt) {
+      D.prep();
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks) {
         bf16x8(&ac)[FM] = (ks & 1) ? fa1 : fa0;
         bf16x8(&an)[FM] = (ks & 1) ? fa0 : fa1;
         bf16x8(&bc)[FN] = (ks & 1) ? fb1 : fb0;
         bf16x8(&bn)[FN] = (ks & 1) ? fb0 : fb1;
         float(&lc)[16] = (ks & 1) ? lk1 : lk0;
         float(&ln)[16] = (ks & 1) ? lk0 : lk1;
-        if (ks < 3) {
-          mma.load_a(an, As(cur), wm, lane, ks + 1);
-          mma.load_b(bn, Bs(cur), wn, lane, ks + 1);
-        }
+        mma.load_a(an, As(cur), wm, lane, ks + 1);
+        mma.load_b(bn, Bs(cur), wn, lane, ks + 1);
+        lookup(D, ks + 1, ln);
         mma.mfma(ac, bc);
-        if constexpr (kNf4) {
-          if (ks < 3) bt_next.lookup(ks + 1, ln, cb);
-          bt_next.finish(ks, lc, Bs(cur ^ 1), tid);
-        } else {
-          store_b(bt_next, cur ^ 1, ks);
-        }
+        finish(D, ks, lc, cur ^ 1);
+        interleave<FM * FN>();
         __builtin_amdgcn_sched_barrier(0);
       }
+      mfma_half(fa1, fb1, 0);
+      finish(D, 3, lk1, cur ^ 1);
+      interleave<FM * FN / 2>();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmem_all();
+      __syncthreads();
+      mma.load_a(fa0, As(cur ^ 1), wm, lane, 0);
+      mma.load_b(fb0, Bs(cur ^ 1), wn, lane, 0);
+      lookup(N, 0, lk0);
+      adma.issue(As(cur), (int64_t)(kt + 2) * KT, kend);
+      load_b(D, kt + 3);
+      mfma_half(fa1, fb1, 1);
+      interleave<FM * FN / 2>();
+      __builtin_amdgcn_sched_barrier(0);
     };
     if (kt_begin < kt_end) {
       __syncthreads();  // codebook visible, prologue done with stage 0
-      adma.issue(As(0), wave, (int64_t)kt_begin * KT, kend);
+      adma.issue(As(0), (int64_t)kt_begin * KT, kend);
+      adma.issue(As(1), (int64_t)(kt_begin + 1) * KT, kend);
       load_b(b0, kt_begin);
       load_b(b1, kt_begin + 1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) store_b(b0, 0, q);
+      load_b(b0, kt_begin + 2);
       wait_vmem_all();
       __syncthreads();
+      mma.load_a(fa0, As(0), wm, lane, 0);
+      mma.load_b(fb0, Bs(0), wn, lane, 0);
+      lookup(b1, 0, lk0);
       // Branch-free: tiles past kt_end load as zeros, so an odd count ends
       // with one MFMA pass over a zero tile.
       for (int kt = kt_begin; kt < kt_end; kt += 2) {
-        adma.issue(As(1), wave, (int64_t)(kt + 1) * KT, kend);
-        load_b(b0, kt + 2);
-        stepd(0, b1);
-        wait_vmem_all();
-        __syncthreads();
-        adma.issue(As(0), wave, (int64_t)(kt + 2) * KT, kend);
-        load_b(b1, kt + 3);
-        stepd(1, b0);
-        wait_vmem_all();
-        __syncthreads();
+        stepd(0, b1, b0, kt);
+        stepd(1, b0, b1, kt + 1);
       }
     }
   } else if (kt_begin < kt_end) {
@@ -647,6 +733,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   // Epilogue.  32x32 accumulator layout: lane l holds column l%32 and rows
   // 8*(e/4) + 4*(l/32) + e%4 for e = 0..15.
   const int lr = lane & 31, lh = lane >> 5;
+  const int64_t wcol0 = col0 + wn * WTN;
+  if (wrow0 + WTM <= g.rows && wcol0 + WTN <= g.cols) {
+    // Whole wave tile in range: the row and column of each store are a
+    // uniform base plus this lane's 32-bit offset.
+    const int loff = lh * 4 * (int)g.ldo + lr;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t ru = wrow0 + i * 32 + (e >> 2) * 8 + (e & 3);
+          const float v = mma.acc[i][j][e];
+          if constexpr (OMODE == O_BF16) {
+            uint16_t* o = g.out_bf16 + ru * g.ldo + wcol0 + j * 32;
+            o[loff] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+          } else {
+            float* o = g.out_f32 + (int64_t)blockIdx.y * g.part_stride + ru * g.ldo + wcol0 + j * 32;
+            o[loff] = v;
+          }
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
