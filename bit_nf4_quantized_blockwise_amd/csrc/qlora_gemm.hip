@@ -45,12 +45,6 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9
 __device__ inline int swz(int row, int chunk) {
   return (row * ROWB) + ((chunk ^ (row & 7) ^ ((row >> 3) & 7)) << 4);
 }
-// The A tile is only written row-wise (by direct-to-LDS loads) and read as
-// MFMA operands, so the position depends on r mod 8 alone; a load of eight
-// rows then needs the same source chunk order for every row group.
-__device__ inline int swz_a(int row, int chunk) {
-  return (row * ROWB) + ((chunk ^ (row & 7)) << 4);
-}
 
 // A raw buffer resource: loads at offsets outside [0, bytes) return zero, so
 // ragged tiles need no branches.
@@ -324,38 +318,34 @@ struct Nf4RedTile {
 template <int MT>
 struct ADma {
   static constexpr int PER_W = MT / 32;
+  static_assert(PER_W % 8 == 0, "A tile loads must cover whole swizzle periods");
   Buf buf;
-  int voff;   // byte offset of this lane's 16 bytes in the wave's first load, at k = 0
-  int kc;     // 2 · (first k of this lane's chunk within the tile)
+  int vrow;   // byte offset of this lane's row in the wave's first load
+  int c16;    // 16 · ((lane mod 8) ^ (lane / 8)): chunk of the first load
   int jstep;  // bytes between the rows of consecutive loads (8 rows)
   int lbase;  // LDS byte offset of the wave's first load within a stage (uniform)
 
   __device__ inline void init(const uint16_t* p, int64_t ld, int64_t nrows, int64_t row0,
                               int wave, int lane) {
     buf.init(p + row0 * ld, (nrows - row0) * ld * 2);
-    // Load j of this wave covers rows (wave · PER_W + j) · 8 + lane / 8, whose
-    // r mod 8 is lane / 8; the lane fetches the chunk that lands at its slot.
-    const int c = (lane & 7) ^ (lane >> 3);
-    kc = c * 16;
-    voff = (wave * PER_W * 8 + (lane >> 3)) * (int)ld * 2 + kc;
+    // Load j of this wave covers rows (wave · PER_W + j) · 8 + lane / 8: r mod 8
+    // is lane / 8 and (r / 8) mod 8 is j mod 8, so the lane fetches logical
+    // chunk (lane mod 8) ^ (lane / 8) ^ (j mod 8) to land at its slot.
+    vrow = (wave * PER_W * 8 + (lane >> 3)) * (int)ld * 2;
+    c16 = ((lane & 7) ^ (lane >> 3)) << 4;
     jstep = 8 * (int)ld * 2;
-    lbase = __builtin_amdgcn_readfirstlane(wave) * PER_W * 1024;
+    lbase = wave * PER_W * 1024;
   }
   __device__ inline void issue(char* stage, int64_t k0, int64_t kend) const {
     const int kb = (int)k0 * 2, kendb = (int)kend * 2;
-    if (kb + KT * 2 <= kendb) {  // whole tile inside the reduction range (uniform)
+    const bool full = kb + KT * 2 <= kendb;  // whole tile inside the reduction range (uniform)
 #pragma unroll
-      for (int j = 0; j < PER_W; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            buf.r, (__attribute__((address_space(3))) void*)(stage + lbase + j * 1024), 16,
-            voff + (j * jstep + kb), 0, 0, 0);
-    } else {
-      const int off = kb + kc < kendb ? voff + kb : kOOB;
-#pragma unroll
-      for (int j = 0; j < PER_W; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            buf.r, (__attribute__((address_space(3))) void*)(stage + lbase + j * 1024), 16,
-            off == kOOB ? kOOB : off + j * jstep, 0, 0, 0);
+    for (int j = 0; j < PER_W; ++j) {
+      const int cj = c16 ^ ((j & 7) << 4);
+      const int off = vrow + cj + (kb + j * jstep);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          buf.r, (__attribute__((address_space(3))) void*)(stage + lbase + j * 1024), 16,
+          full || kb + cj < kendb ? off : kOOB, 0, 0, 0);
     }
   }
 };
@@ -456,7 +446,7 @@ struct Mma {
     const int chunk = 4 * (lane >> 5) + ks;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(As + swz_a(wm * WTM + i * 32 + (lane & 31), chunk));
+      a[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * WTM + i * 32 + (lane & 31), chunk));
   }
   __device__ inline void mfma(const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
 #pragma unroll
