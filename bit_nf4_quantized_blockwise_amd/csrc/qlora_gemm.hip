@@ -310,6 +310,85 @@ struct Nf4RedTile {
   }
 };
 
+// ---- B_NF4_RED, row-major staging (NT = 256) ---------------------------------
+// The tile is 64 W rows (the reduction) x 256 W columns (the output), kept in
+// LDS in W's own layout: row n holds its 256 columns in 512 bytes, the 16-byte
+// chunk c at position c ^ 4 (n mod 4).  Thread t decodes one NF4 block: row
+// t / 4, columns 64 (t mod 4) .. +64, exactly as the column tile does, and the
+// MFMA reads its operand through the transposing LDS loads.
+__device__ inline int swz_rows(int n, int chunk) { return n * 512 + ((chunk ^ ((n & 3) << 2)) << 4); }
+
+struct Nf4RowsTile {
+  u32x4 p[2];
+  uint32_t qraw;
+  float s2, ah;
+  Buf c2;
+  int n, b;      // row within the tile, block within the row
+  int64_t col;   // first W column of this thread's block
+
+  __device__ inline void init(const GemmArgs& g, int64_t c0, int tid) {
+    n = tid >> 2;
+    b = tid & 3;
+    col = c0 + 64 * b;
+    c2.init(g.c2, ((g.red * (g.w_kin >> 6) + 255) >> 8) * 4);
+  }
+  // Issues the loads only: W row r0 + n; rows at or past rend and columns
+  // past the matrix read as zero.
+  __device__ inline void load(const GemmArgs& g, int64_t r0, int64_t rend) {
+    const int64_t bpr = g.w_kin >> 6;
+    Buf pk, qa;
+    pk.init(g.packed + r0 * (g.w_kin >> 1), (rend - r0) * (g.w_kin >> 1));
+    qa.init(g.qabsmax + r0 * bpr, (rend - r0) * bpr);
+    const bool ok = col < g.cols;
+    const int off = n * (int)(g.w_kin >> 1) + (int)(col >> 1);
+    p[0] = pk.ld16(ok ? off : kOOB);
+    p[1] = pk.ld16(ok ? off + 16 : kOOB);
+    qraw = qa.ld1(ok ? n * (int)bpr + (int)(col >> 6) : kOOB);
+    s2 = bits_to_float(c2.ld4((int)((((r0 + n) * bpr + (col >> 6)) >> 8) * 4)));
+  }
+  __device__ inline void prep() { ah = s2 * (float)qraw; }
+  // Quarter q: packed dwords q and q + 4 (chunks q and q + 4 of the block).
+  __device__ inline void lookup(int q, float (&v)[16], const float* cb) const {
+    const char* base = reinterpret_cast<const char*>(cb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d = q + 4 * h;
+      const uint32_t w = p[d >> 2][d & 3];
+      uint32_t ev = (w << 2) & 0x3c3c3c3cu, od = (w >> 2) & 0x3c3c3c3cu;
+      asm("" : "+v"(ev), "+v"(od));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * h + 2 * e] = *reinterpret_cast<const float*>(base + ((ev >> (8 * e)) & 0xffu));
+        v[8 * h + 2 * e + 1] = *reinterpret_cast<const float*>(base + ((od >> (8 * e)) & 0xffu));
+      }
+    }
+  }
+  __device__ inline void finish(int q, const float (&v)[16], char* lds, int) const {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[8 * h + 2 * e] * ah, v[8 * h + 2 * e + 1] * ah);
+      *reinterpret_cast<u32x4*>(lds + swz_rows(n, 8 * b + q + 4 * h)) = o;
+    }
+  }
+  __device__ inline void store_part(char* lds, int tid, const float* cb, int q) const {
+    float v[16];
+    lookup(q, v, cb);
+    finish(q, v, lds, tid);
+  }
+  // Whole tile at once (pipeline fill).
+  __device__ inline void store(char* lds, const float* cb) {
+    prep();
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lookup(q, v, cb);
+      finish(q, v, lds, 0);
+    }
+  }
+};
+
 // A tile staged by direct-to-LDS buffer loads (no VGPRs).  A wave-wide
 // 16-byte load writes lane l's data at LDS offset 16 l, i.e. 8 rows x 128 B;
 // the LDS swizzle is applied on the global side: the lane landing in chunk
@@ -441,6 +520,34 @@ struct Mma {
     for (int j = 0; j < FN; ++j)
       b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * WTN + j * 32 + (lane & 31), chunk));
   }
+  // B fragments of step ks from a row-major tile (see Nf4RowsTile), through
+  // ds_read_b64_tr_b16.  In each group of 16 lanes that instruction hands
+  // lane 4a + b element b of the 8-byte rows fetched by lanes a, a + 4,
+  // a + 8, a + 12.  So lane r of a group fetches row n0 + r / 4, columns
+  // 4 (r mod 4) .. +3 of its 16-column slice, and every lane ends up with four
+  // consecutive rows (the reduction) of one column; two loads give the eight
+  // rows 32 (lane / 32) + 8 ks .. +7, the A operand's k order.  tb[j] is the
+  // lane's byte offset for column block j at ks = 0 (from tr_base).
+  __device__ inline void load_b_tr(bf16x8 (&b)[FN], const char* Bs, const int (&tb)[FN], int ks) const {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      typedef short s4 __attribute__((ext_vector_type(4)));
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s4*)(Bs + tb[j] + (8 * ks) * 512));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s4*)(Bs + tb[j] + (8 * ks + 4) * 512));
+      b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+  __device__ inline void tr_base(int (&tb)[FN], int wn, int lane) const {
+    const int r = lane & 15;
+    const int n = 32 * (lane >> 5) + (r >> 2);  // row at ks = 0; + 8 ks (+ 4) keeps n mod 4
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int chunk = (wn * WTN + j * 32 + 16 * ((lane >> 4) & 1)) / 8 + ((r & 3) >> 1);
+      tb[j] = swz_rows(n, chunk) + 8 * (r & 1);
+    }
+  }
   // A fragments of step ks from an LDS tile (same k order as ARegs).
   __device__ inline void load_a(bf16x8 (&a)[FM], const char* As, int wm, int lane, int ks) const {
     const int chunk = 4 * (lane >> 5) + ks;
@@ -544,9 +651,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   }
 
+  constexpr bool kRows = BMODE == B_NF4_RED && AMODE == A_DMA;  // row-major B, transposed reads
   using BTile = typename std::conditional<
       BMODE == B_NF4_COLS, Nf4ColsTile<NT>,
-      typename std::conditional<BMODE == B_NF4_RED, Nf4RedTile<NT>,
+      typename std::conditional<BMODE == B_NF4_RED,
+                                typename std::conditional<kRows, Nf4RowsTile, Nf4RedTile<NT>>::type,
                                 typename std::conditional<BMODE == B_BF16_RC, RcTile<NT>,
                                                           RowTile<NT>>::type>::type>::type;
   ARegs<(AMODE == A_DIRECT) ? FM : 1> a;
@@ -565,6 +674,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     const int64_t k0 = (int64_t)kt * KT;
     if constexpr (BMODE == B_NF4_COLS) {
       bt.load(k0, kend);
+    } else if constexpr (kRows) {
+      bt.load(g, k0, kend);
     } else if constexpr (BMODE == B_NF4_RED) {
       bt.load(g, k0, kend, tid);
     } else if constexpr (BMODE == B_BF16_RC) {
@@ -628,14 +739,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     // Codebook reads a quarter ahead where registers allow (column tiles: one
     // block per thread); the reduction-major tile, with eight block scales per
     // thread, reads and finishes each quarter in place.
-    constexpr bool kAhead = BMODE == B_NF4_COLS;
+    constexpr bool kAhead = BMODE == B_NF4_COLS || kRows;
+    int tb[FN];
+    if constexpr (kRows) mma.tr_base(tb, wn, lane);
+    auto load_bf = [&](bf16x8 (&f)[FN], int st, int ks) {
+      if constexpr (kRows)
+        mma.load_b_tr(f, Bs(st), tb, ks);
+      else
+        mma.load_b(f, Bs(st), wn, lane, ks);
+    };
     auto lookup = [&](const BTile& bt, int q, float (&v)[16]) {
       if constexpr (kAhead) bt.lookup(q, v, cb);
     };
     auto finish = [&](const BTile& bt, int q, const float (&v)[16], int st) {
       if constexpr (kAhead)
         bt.finish(q, v, Bs(st), tid);
-      else if constexpr (BMODE == B_NF4_RED)
+      else if constexpr (BMODE == B_NF4_RED && !kRows)
         bt.store_part(Bs(st), tid, cb, q);
     };
     auto mfma_half = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN], int h) {
@@ -657,7 +776,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         float(&lc)[16] = (ks & 1) ? lk1 : lk0;
         float(&ln)[16] = (ks & 1) ? lk0 : lk1;
         mma.load_a(an, As(cur), wm, lane, ks + 1);
-        mma.load_b(bn, Bs(cur), wn, lane, ks + 1);
+        load_bf(bn, cur, ks + 1);
         lookup(D, ks + 1, ln);
         mma.mfma(ac, bc);
         finish(D, ks, lc, cur ^ 1);
@@ -671,7 +790,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       wait_vmem_all();
       __syncthreads();
       mma.load_a(fa0, As(cur ^ 1), wm, lane, 0);
-      mma.load_b(fb0, Bs(cur ^ 1), wn, lane, 0);
+      load_bf(fb0, cur ^ 1, 0);
       lookup(N, 0, lk0);
       adma.issue(As(cur), (int64_t)(kt + 2) * KT, kend);
       load_b(D, kt + 3);
@@ -691,7 +810,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       wait_vmem_all();
       __syncthreads();
       mma.load_a(fa0, As(0), wm, lane, 0);
-      mma.load_b(fb0, Bs(0), wn, lane, 0);
+      load_bf(fb0, 0, 0);
       lookup(b1, 0, lk0);
       // Branch-free: tiles past kt_end load as zeros, so an odd count ends
       // with one MFMA pass over a zero tile.
