@@ -98,7 +98,9 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t need = ceil_div(nch, 8);
   const int cap = 8 / p.mg;
   p.cpw = 1;
-  while (p.cpw < need && p.cpw < cap) p.cpw *= 2;
+  // multi-chunk runs read the DQ codes as dwords: rows of a multiple of 4 blocks
+  if ((K / 64) % 4 == 0)
+    while (p.cpw < need && p.cpw < cap) p.cpw *= 2;
   p.ksplit = (int)ceil_div(nch, 8 * (int64_t)p.cpw);
   // column groups (16 outputs each) per workgroup: enough that one workgroup
   // per CU covers N, at most 8
@@ -258,7 +260,9 @@ qlora_status lora_down_impl(const uint16_t* X, int64_t M, int64_t K, const uint1
 
 template <int CPW, int MG, int G>
 void launch_gemv_g(const GemvArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((nf4_gemv_kernel<CPW, MG, G>), grid, dim3(512), 0, st, a);
+  // dword reads of the DQ codes need 4-byte aligned runs: even CPW (and rows
+  // a multiple of 4 blocks long, which the plan checks)
+  hipLaunchKernelGGL((nf4_gemv_kernel<CPW, MG, G, (CPW > 1)>), grid, dim3(512), 0, st, a);
 }
 
 template <int CPW, int MG>

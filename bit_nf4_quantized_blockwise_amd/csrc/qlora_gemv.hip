@@ -43,19 +43,23 @@ __device__ inline uint16_t bf16_rne_bits(float f) {
 
 }  // namespace
 
-template <int CPW, int MG, int G>
+template <int CPW, int MG, int G, bool QV>
 __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
-  __shared__ uint32_t lut[256 * 32];        // byte -> two bf16 levels, one copy per bank
+  // byte e -> the two bf16 levels of its nibbles, 64 copies: entry e of lane
+  // l at byte 256 e + 4 l, so a lookup address is one v_perm of the packed
+  // dword and the lane's offset, and the 64 lanes hit 64 different banks.
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 64];
   __shared__ float red[8][G][MG][32][4];    // per-wave partial sums, reduced once at the end
+  __shared__ uint16_t ush[16 * 256];         // U rows for the adapter term (M <= 16, r <= 256)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
 
-  for (int i = tid; i < 256 * 32; i += 512) {
-    const int e = i >> 5;
-    const float lo = bits_to_float(kNF4Bits[e & 15]);
-    const float hi = bits_to_float(kNF4Bits[e >> 4]);
-    lut[i] = (uint32_t)bf16_rne_bits(lo) | ((uint32_t)bf16_rne_bits(hi) << 16);
+  for (int i = tid; i < 256 * 16; i += 512) {
+    const int e = i >> 4;
+    const uint32_t v = (uint32_t)bf16_rne_bits(bits_to_float(kNF4Bits[e & 15])) |
+                       ((uint32_t)bf16_rne_bits(bits_to_float(kNF4Bits[e >> 4])) << 16);
+    *reinterpret_cast<u32x4*>(&lut[i * 4]) = u32x4{v, v, v, v};
   }
 
   const int64_t K = g.K, N = g.N;
@@ -78,7 +82,8 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
       }
   __syncthreads();
 
-  const uint32_t* lutl = lut + (lane & 31);
+  const char* lutb = reinterpret_cast<const char*>(lut);
+  const uint32_t lane4 = (uint32_t)lane * 4;
   const int64_t ncg = (N + 15) / 16;
   const int64_t blocks_per_row = K >> 6;
   const __amdgpu_buffer_rsrc_t c2r = make_rsrc(g.c2, ((N * blocks_per_row + 255) >> 8) * 4);
@@ -86,52 +91,98 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
 
   // Every wave walks all G column groups of the workgroup on its own slice
   // of the reduction; no workgroup barrier until the end, so the waves drift
-  // apart and one wave's loads overlap another's MFMAs.
+  // apart and one wave's loads overlap another's MFMAs.  Within a wave the
+  // weight loads run one column group ahead: as soon as chunk c of group gi
+  // has been turned into MFMA operands, its registers are reloaded with
+  // chunk c of group gi + 1, so eight 16-byte loads per lane stay in flight.
+  const int64_t nw0 = cg0 * 16;  // first W row of this workgroup
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.packed + nw0 * (K >> 1), (N - nw0) * (K >> 1));
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(g.qabsmax + nw0 * blocks_per_row,
+                                              (N - nw0) * blocks_per_row);
+  u32x4 pk[CPW];
+  auto load = [&](int gi, int c) {
+    const int64_t kq = (chunk0 + c) * 128 + 32 * qd;
+    const int64_t nl = (int64_t)gi * 16 + c16;  // W row relative to nw0
+    const int off = (int)((nl * K + kq) >> 1);
+    pk[c] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, kq < K ? off : 0x7ffffff0, 0, 0));
+  };
+  // Block scales of one column group: the lane's chunks c = 0..CPW-1 use
+  // blocks b0 + 2c + (qd >= 2) of its row, so its DQ codes are the 2·CPW
+  // bytes from b0 (fetched as dwords when the row pitch in blocks is a
+  // multiple of 4, else byte by byte), and they span at most two DQ groups.
+  // Bytes past a row's end belong to the next row; they only ever scale
+  // partial sums that are zero (weights past K meet zero tokens).
+  constexpr int QW = (2 * CPW + 3) / 4;
+  struct Scales {
+    uint32_t q[QW];
+    uint32_t c2a, c2b;
+    int sw;  // first byte of the run that falls in the second DQ group
+  };
+  auto load_scales = [&](int gi, Scales& sc) {
+    const int64_t nl = (int64_t)gi * 16 + c16;
+    const int b0 = (int)(nl * blocks_per_row + 2 * chunk0);  // relative to row nw0
+    if constexpr (QV) {
+#pragma unroll
+      for (int i = 0; i < QW; ++i) sc.q[i] = __builtin_amdgcn_raw_buffer_load_b32(qr, b0 + 4 * i, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < QW; ++i) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          v |= __builtin_amdgcn_raw_buffer_load_b8(qr, b0 + 4 * i + t, 0, 0) << (8 * t);
+        sc.q[i] = v;
+      }
+    }
+    const int64_t gb = nw0 * blocks_per_row + b0;
+    sc.sw = 256 - (int)(gb & 255);
+    sc.c2a = __builtin_amdgcn_raw_buffer_load_b32(c2r, (int)((gb >> 8) * 4), 0, 0);
+    sc.c2b = __builtin_amdgcn_raw_buffer_load_b32(c2r, (int)((gb >> 8) * 4) + 4, 0, 0);
+  };
+  auto scale_of = [&](const Scales& sc, int c) {
+    const int i = 2 * c + (qd >> 1);  // byte within the lane's run
+    const uint32_t q = (sc.q[(2 * c) >> 2] >> (8 * (i & 3))) & 0xffu;
+    return __builtin_bit_cast(float, i >= sc.sw ? sc.c2b : sc.c2a) * (float)q;
+  };
+  Scales sA, sB;
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) load(0, c);
+  load_scales(0, sA);
   floatx4 acc[G][MG];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
+    Scales& sc = (gi & 1) ? sB : sA;
+    if (gi + 1 < G) load_scales(gi + 1, (gi & 1) ? sA : sB);
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) acc[gi][mg] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int64_t n0 = (cg0 + gi) * 16;
-    if (n0 >= N) continue;  // uniform
-    const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.packed + n0 * (K >> 1), (N - n0) * (K >> 1));
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(g.qabsmax + n0 * blocks_per_row,
-                                                (N - n0) * blocks_per_row);
-    u32x4 pk[CPW];
-    float ah[CPW];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int64_t kq = (chunk0 + c) * 128 + 32 * qd;
-      const int off = (int)((c16 * K + kq) >> 1);
-      pk[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
-      const int64_t lb = (c16 * K + kq) >> 6;  // block index relative to row n0
-      const uint32_t qv = __builtin_amdgcn_raw_buffer_load_b8(qr, (int)lb, 0, 0);
-      const int64_t gb = n0 * blocks_per_row + lb;
-      const float c2v = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(c2r, (int)((gb >> 8) * 4), 0, 0));
-      ah[c] = c2v * (float)qv;
-    }
+      u32x4 bop[4];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t p = pk[c][j];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          bop[j][t] = *reinterpret_cast<const uint32_t*>(
+              lutb + __builtin_amdgcn_perm(p, lane4, 0x0c0c0400u + (t << 8)));
+      }
+      if (gi + 1 < G) load(gi + 1, c);  // rows past N read as zero
       floatx4 cb[MG];
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg) cb[mg] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t p = pk[c][j];
-        u32x4 bop;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) bop[t] = lutl[((p >> (8 * t)) & 0xffu) * 32];
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg)
           cb[mg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[mg][c][j]),
-                                                           __builtin_bit_cast(bf16x8, bop), cb[mg],
+                                                           __builtin_bit_cast(bf16x8, bop[j]), cb[mg],
                                                            0, 0, 0);
-      }
+      const float ah = scale_of(sc, c);
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[gi][mg][i] += ah[c] * cb[mg][i];
+        for (int i = 0; i < 4; ++i) acc[gi][mg][i] += ah * cb[mg][i];
     }
   }
   // rows r and r + 8 hold the same token for the two blocks of each chunk
@@ -149,6 +200,19 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[w][gi][mg][lane][i] = acc[gi][mg][i];
   }
+  // Adapter term (split 0 only): the workgroup's G·16 rows of B and the M
+  // rows of U are staged in LDS (B where the table was), so each output's
+  // rank-r dot product reads LDS instead of issuing r dependent global loads.
+  const bool lora = blockIdx.y == 0 && g.r > 0;
+  uint16_t* bsh = reinterpret_cast<uint16_t*>(lut);  // [G·16][r]; r <= 256 fits the table
+  __syncthreads();  // every wave is done with the table
+  if (lora) {
+    for (int i = tid; i < G * 16 * g.r; i += 512) {
+      const int64_t n = nw0 + i / g.r;
+      bsh[i] = n < N ? g.b[n * g.r + i % g.r] : (uint16_t)0;
+    }
+    for (int i = tid; i < M * g.r; i += 512) ush[i] = g.u[i];
+  }
   __syncthreads();
   for (int o = tid; o < G * MG * 128; o += 512) {
     const int gi = o / (MG * 128), mg = (o / 128) % MG, t = o & 127;
@@ -159,11 +223,11 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
     const int tok = tok8 + 8 * mg;
     const int64_t n = (cg0 + gi) * 16 + col;
     if (tok < M && n < N) {
-      if (blockIdx.y == 0) {
+      if (lora) {
+        const uint16_t* ur = ush + tok * g.r;
+        const uint16_t* br = bsh + (n - nw0) * g.r;
         float l = 0.0f;
-        for (int jr = 0; jr < g.r; ++jr)
-          l += bf16_bits_to_float(g.u[(int64_t)tok * g.r + jr]) *
-               bf16_bits_to_float(g.b[n * g.r + jr]);
+        for (int jr = 0; jr < g.r; ++jr) l += bf16_bits_to_float(ur[jr]) * bf16_bits_to_float(br[jr]);
         v += g.s * l;
       }
       if (g.ksplit == 1)
@@ -228,61 +292,61 @@ __global__ __launch_bounds__(256) void lora_down_small_kernel(const uint16_t* __
   }
 }
 
-template __global__ void nf4_gemv_kernel<1, 1, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 1, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 1, 3>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 1, 4>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 1, 5>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 1, 6>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 1, 7>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 1, 8>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1, 3>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1, 4>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1, 5>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1, 6>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1, 7>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 1, 8>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1, 3>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1, 4>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1, 5>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1, 6>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1, 7>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 1, 8>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1, 3>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1, 4>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1, 5>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1, 6>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1, 7>(GemvArgs);
-template __global__ void nf4_gemv_kernel<8, 1, 8>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2, 3>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2, 4>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2, 5>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2, 6>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2, 7>(GemvArgs);
-template __global__ void nf4_gemv_kernel<1, 2, 8>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2, 3>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2, 4>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2, 5>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2, 6>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2, 7>(GemvArgs);
-template __global__ void nf4_gemv_kernel<2, 2, 8>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2, 1>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2, 2>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2, 3>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2, 4>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2, 5>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2, 6>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2, 7>(GemvArgs);
-template __global__ void nf4_gemv_kernel<4, 2, 8>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 1, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 2, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 3, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 4, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 5, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 6, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 7, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 1, 8, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 1, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 2, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 3, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 4, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 5, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 6, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 7, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 1, 8, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 1, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 2, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 3, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 4, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 5, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 6, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 7, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 1, 8, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 1, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 2, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 3, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 4, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 5, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 6, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 7, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<8, 1, 8, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 1, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 2, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 3, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 4, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 5, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 6, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 7, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<1, 2, 8, false>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 1, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 2, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 3, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 4, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 5, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 6, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 7, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<2, 2, 8, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 1, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 2, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 3, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 4, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 5, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 6, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 7, true>(GemvArgs);
+template __global__ void nf4_gemv_kernel<4, 2, 8, true>(GemvArgs);
 
 }  // namespace qlora

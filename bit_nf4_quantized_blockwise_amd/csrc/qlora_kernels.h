@@ -62,7 +62,7 @@ struct GemvArgs {
 template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE, int AMODE>
 __global__ void gemm_kernel(GemmArgs g);
 
-template <int CPW, int MG, int G>
+template <int CPW, int MG, int G, bool QV>
 __global__ void nf4_gemv_kernel(GemvArgs g);
 
 __global__ void lora_down_small_kernel(const uint16_t* x, int M, int64_t K, const uint16_t* a,
