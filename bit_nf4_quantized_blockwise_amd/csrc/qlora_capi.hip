@@ -90,18 +90,20 @@ struct GemvPlan {
   int cpw, mg, ksplit, gx, groups;
 };
 
-// 8 waves per workgroup, each wave CPW chunks of 128 k; tokens in groups of 8.
+// kGemvWaves waves per workgroup, each wave CPW chunks of 128 k; tokens in
+// groups of 8 (MG groups).  The token operands live in registers, CPW · MG
+// chunks' worth: at most 8 (two waves per SIMD at 256 registers).
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K) {
   GemvPlan p;
   p.mg = M <= 8 ? 1 : 2;
   const int64_t nch = ceil_div(K, 128);
-  const int64_t need = ceil_div(nch, 8);
+  const int64_t need = ceil_div(nch, kGemvWaves);
   const int cap = 8 / p.mg;
   p.cpw = 1;
   // multi-chunk runs read the DQ codes as dwords: rows of a multiple of 4 blocks
   if ((K / 64) % 4 == 0)
     while (p.cpw < need && p.cpw < cap) p.cpw *= 2;
-  p.ksplit = (int)ceil_div(nch, 8 * (int64_t)p.cpw);
+  p.ksplit = (int)ceil_div(nch, kGemvWaves * (int64_t)p.cpw);
   // column groups (16 outputs each) per workgroup: enough that one workgroup
   // per CU covers N, at most 8
   const int64_t ncg = ceil_div(N, 16);
@@ -262,7 +264,7 @@ template <int CPW, int MG, int G>
 void launch_gemv_g(const GemvArgs& a, dim3 grid, hipStream_t st) {
   // dword reads of the DQ codes need 4-byte aligned runs: even CPW (and rows
   // a multiple of 4 blocks long, which the plan checks)
-  hipLaunchKernelGGL((nf4_gemv_kernel<CPW, MG, G, (CPW > 1)>), grid, dim3(512), 0, st, a);
+  hipLaunchKernelGGL((nf4_gemv_kernel<CPW, MG, G, (CPW > 1)>), grid, dim3(64 * kGemvWaves), 0, st, a);
 }
 
 template <int CPW, int MG>

@@ -44,18 +44,19 @@ __device__ inline uint16_t bf16_rne_bits(float f) {
 }  // namespace
 
 template <int CPW, int MG, int G, bool QV>
-__global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
+__global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   // byte e -> the two bf16 levels of its nibbles, 64 copies: entry e of lane
   // l at byte 256 e + 4 l, so a lookup address is one v_perm of the packed
   // dword and the lane's offset, and the 64 lanes hit 64 different banks.
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 64];
-  __shared__ float red[8][G][MG][32][4];    // per-wave partial sums, reduced once at the end
+  __shared__ float red[kGemvWaves][G][MG][32][4];  // per-wave partial sums, reduced once at the end
   __shared__ uint16_t ush[16 * 256];         // U rows for the adapter term (M <= 16, r <= 256)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
 
-  for (int i = tid; i < 256 * 16; i += 512) {
+  constexpr int NT = 64 * kGemvWaves;
+  for (int i = tid; i < 256 * 16; i += NT) {
     const int e = i >> 4;
     const uint32_t v = (uint32_t)bf16_rne_bits(bits_to_float(kNF4Bits[e & 15])) |
                        ((uint32_t)bf16_rne_bits(bits_to_float(kNF4Bits[e >> 4])) << 16);
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
 
   const int64_t K = g.K, N = g.N;
   const int M = g.M;
-  const int64_t chunk0 = ((int64_t)blockIdx.y * 8 + w) * CPW;
+  const int64_t chunk0 = ((int64_t)blockIdx.y * kGemvWaves + w) * CPW;
 
   // Token operands for this wave's chunks, kept in registers for all columns.
   u32x4 xa[MG][CPW][4];
@@ -99,12 +100,21 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.packed + nw0 * (K >> 1), (N - nw0) * (K >> 1));
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(g.qabsmax + nw0 * blocks_per_row,
                                               (N - nw0) * blocks_per_row);
-  u32x4 pk[CPW];
-  auto load = [&](int gi, int c) {
+  // Weight chunks stream through a ring of D registers: step s = gi·CPW + c
+  // consumes slot s mod D and refills it with step s + D, so D 16-byte loads
+  // per lane stay in flight (two column groups ahead when the token operands
+  // leave room).
+  constexpr int RD = 1;
+  constexpr int D = CPW * RD;
+  constexpr int S = G * CPW;
+  u32x4 pk[D];
+  auto load = [&](int st) {
+    if (st >= S) return;
+    const int gi = st / CPW, c = st % CPW;
     const int64_t kq = (chunk0 + c) * 128 + 32 * qd;
     const int64_t nl = (int64_t)gi * 16 + c16;  // W row relative to nw0
     const int off = (int)((nl * K + kq) >> 1);
-    pk[c] = __builtin_bit_cast(
+    pk[st % D] = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, kq < K ? off : 0x7ffffff0, 0, 0));
   };
   // Block scales of one column group: the lane's chunks c = 0..CPW-1 use
@@ -147,27 +157,28 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
   };
   Scales sA, sB;
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) load(0, c);
+  for (int st = 0; st < D; ++st) load(st);  // rows past N read as zero
   load_scales(0, sA);
-  floatx4 acc[G][MG];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     Scales& sc = (gi & 1) ? sB : sA;
     if (gi + 1 < G) load_scales(gi + 1, (gi & 1) ? sA : sB);
+    floatx4 acc[MG];
 #pragma unroll
-    for (int mg = 0; mg < MG; ++mg) acc[gi][mg] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mg = 0; mg < MG; ++mg) acc[mg] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
+      const int st = gi * CPW + c;
       u32x4 bop[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t p = pk[c][j];
+        const uint32_t p = pk[st % D][j];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           bop[j][t] = *reinterpret_cast<const uint32_t*>(
               lutb + __builtin_amdgcn_perm(p, lane4, 0x0c0c0400u + (t << 8)));
       }
-      if (gi + 1 < G) load(gi + 1, c);  // rows past N read as zero
+      load(st + D);  // refills the slot just read; rows past N read as zero
       floatx4 cb[MG];
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg) cb[mg] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -182,23 +193,17 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[gi][mg][i] += ah * cb[mg][i];
+        for (int i = 0; i < 4; ++i) acc[mg][i] += ah * cb[mg][i];
     }
-  }
-  // rows r and r + 8 hold the same token for the two blocks of each chunk
-#pragma unroll
-  for (int gi = 0; gi < G; ++gi)
+    // rows r and r + 8 hold the same token for the two blocks of each chunk;
+    // the group's sums leave for LDS right away
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[gi][mg][i] += __shfl_xor(acc[gi][mg][i], 32);
-  if (lane < 32) {
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-      for (int mg = 0; mg < MG; ++mg)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[w][gi][mg][lane][i] = acc[gi][mg][i];
+      for (int i = 0; i < 4; ++i) {
+        acc[mg][i] += __shfl_xor(acc[mg][i], 32);
+        if (lane < 32) red[w][gi][mg][lane][i] = acc[mg][i];
+      }
   }
   // Adapter term (split 0 only): the workgroup's G·16 rows of B and the M
   // rows of U are staged in LDS (B where the table was), so each output's
@@ -207,19 +212,19 @@ __global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvArgs g) {
   uint16_t* bsh = reinterpret_cast<uint16_t*>(lut);  // [G·16][r]; r <= 256 fits the table
   __syncthreads();  // every wave is done with the table
   if (lora) {
-    for (int i = tid; i < G * 16 * g.r; i += 512) {
+    for (int i = tid; i < G * 16 * g.r; i += NT) {
       const int64_t n = nw0 + i / g.r;
       bsh[i] = n < N ? g.b[n * g.r + i % g.r] : (uint16_t)0;
     }
-    for (int i = tid; i < M * g.r; i += 512) ush[i] = g.u[i];
+    for (int i = tid; i < M * g.r; i += NT) ush[i] = g.u[i];
   }
   __syncthreads();
-  for (int o = tid; o < G * MG * 128; o += 512) {
+  for (int o = tid; o < G * MG * 128; o += NT) {
     const int gi = o / (MG * 128), mg = (o / 128) % MG, t = o & 127;
     const int tok8 = t >> 4, col = t & 15;
     float v = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < 8; ++ww) v += red[ww][gi][mg][col + 16 * (tok8 >> 2)][tok8 & 3];
+    for (int ww = 0; ww < kGemvWaves; ++ww) v += red[ww][gi][mg][col + 16 * (tok8 >> 2)][tok8 & 3];
     const int tok = tok8 + 8 * mg;
     const int64_t n = (cg0 + gi) * 16 + col;
     if (tok < M && n < N) {

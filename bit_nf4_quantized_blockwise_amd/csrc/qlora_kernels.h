@@ -62,6 +62,7 @@ struct GemvArgs {
 template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE, int AMODE>
 __global__ void gemm_kernel(GemmArgs g);
 
+constexpr int kGemvWaves = 8;   // waves per few-token GEMV workgroup (they split the reduction)
 template <int CPW, int MG, int G, bool QV>
 __global__ void nf4_gemv_kernel(GemvArgs g);
 
