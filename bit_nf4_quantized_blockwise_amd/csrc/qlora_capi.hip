@@ -16,7 +16,8 @@ using namespace qlora;
 namespace {
 
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_cus[kMaxDevices];  // compute units, once checked
 
 qlora_status check_device() {
   int dev = -1;
@@ -29,8 +30,19 @@ qlora_status check_device() {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QLORA_ERR_DEVICE;
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < kMaxDevices) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  if (dev < kMaxDevices) {
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  }
   return ok ? QLORA_OK : QLORA_ERR_DEVICE;
+}
+
+// Compute units of the current device (after check_device); 256 if unknown.
+int device_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  const int c = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return c > 0 ? c : 256;
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -422,7 +434,10 @@ qlora_status qlora_quantize_nf4_dq(const float* w, int64_t n, uint8_t* packed, i
   const int64_t nb = ceil_div(n, 64);
   const int64_t ng = ceil_div(nb, 256);
   QCHECK(ng <= 0x7fffffff, QLORA_ERR_SHAPE);
-  hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)ng), dim3(256), 0, as_stream(stream),
+  // four workgroups per CU stride over the groups (enough bytes in flight,
+  // and every workgroup overlaps its loads with its own arithmetic)
+  const int64_t grid = std::min<int64_t>(ng, 4 * (int64_t)device_cus());
+  hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
                      w, n, nb, packed, qabsmax, c2, absmax);
   return launched();
 }

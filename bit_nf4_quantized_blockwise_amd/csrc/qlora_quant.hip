@@ -71,7 +71,8 @@ __device__ inline float dq_step(float gmax) {
 }
 
 // Bucket table for the exact decision.  With x = w / a in [-1, 1], bucket
-// j = floor((x + 1) · 32) (clamped to 63) spans [j/32 − 1, (j+1)/32 − 1).
+// j = floor((x + 1) · 32) spans [j/32 − 1, (j+1)/32 − 1); j = 64 is x = 1 (the
+// estimate never leaves [0, 64], so no clamp is needed).
 // kBucketMargin exceeds the error of the float32 quotient w · RN(1/a) by orders
 // of magnitude and, because consecutive midpoints are more than 0.088 apart,
 // a bucket widened by the margin on both sides still holds at most one
@@ -79,13 +80,15 @@ __device__ inline float dq_step(float gmax) {
 // first[j] or first[j] + 1, decided by one exact compare w > T_first[j].
 constexpr double kBucketMargin = 1.0 / 1024.0;
 
+constexpr int kNBuckets = 65;
+
 struct BucketTable {
-  uint8_t first[64];
+  uint8_t first[kNBuckets];
 };
 
 constexpr BucketTable make_buckets() {
   BucketTable t{};
-  for (int j = 0; j < 64; ++j) {
+  for (int j = 0; j < kNBuckets; ++j) {
     const double lo = j / 32.0 - 1.0 - kBucketMargin;
     int c = 0;
     for (int i = 0; i < 15; ++i) c += (kMid.m[i] < lo) ? 1 : 0;
@@ -100,25 +103,9 @@ constexpr int kTStride = 17;  // floats per block in the LDS threshold table (ba
 
 // One lane handles 16 consecutive elements; 4 lanes form one 64-block.
 // T: this block's 16-entry threshold row in LDS (T[15] = +inf); bk: bucket table.
-__device__ inline float quantize_16(const float* __restrict__ w, int64_t n, int64_t blk, int sub,
-                                    float* __restrict__ T, const uint8_t* __restrict__ bk,
-                                    u32x2& out_bytes) {
-  const int64_t base = blk * kBlock + (int64_t)sub * 16;
-  float v[16];
-  if (base + 16 <= n) {
-    const floatx4* p = reinterpret_cast<const floatx4*>(w + base);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      floatx4 x = __builtin_nontemporal_load(p + j);
-      v[4 * j + 0] = x[0];
-      v[4 * j + 1] = x[1];
-      v[4 * j + 2] = x[2];
-      v[4 * j + 3] = x[3];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = (base + j < n) ? w[base + j] : 0.0f;
-  }
+// Block absmax (over the block's 4 lanes) and NF4 indices of 16 loaded values.
+__device__ inline float quantize_16v(const float (&v)[16], int sub, float* __restrict__ T,
+                                     const uint8_t* __restrict__ bk, u32x2& out_bytes) {
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
@@ -137,14 +124,15 @@ __device__ inline float quantize_16(const float* __restrict__ w, int64_t n, int6
     // the estimate only picks a bucket; a power-of-two rescale keeps 1/m finite
     // for subnormal block maxima without changing any ratio
     const float sc = (m < 0x1p-64f) ? 0x1p64f : 1.0f;
-    const float inv = 1.0f / (m * sc);
+    // 32 / (m·sc) to within a couple of ulp (v_rcp: the estimate only picks a
+    // bucket): b = trunc(32 x + 32) in one fma, and |x| <= 1 + 2^-21 keeps b
+    // in [0, 64]
+    const float k32 = 32.0f * __builtin_amdgcn_rcpf(m * sc);
     lo = 0u;
     hi = 0u;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float x = (v[j] * sc) * inv;
-      int b = (int)__builtin_fmaf(x, 32.0f, 32.0f);
-      b = b < 0 ? 0 : (b > 63 ? 63 : b);
+      const int b = (int)__builtin_fmaf(v[j] * sc, k32, 32.0f);
       const int k0 = bk[b];
       const uint32_t idx = (uint32_t)k0 + ((v[j] > T[k0]) ? 1u : 0u);
       if (j < 8)
@@ -157,6 +145,36 @@ __device__ inline float quantize_16(const float* __restrict__ w, int64_t n, int6
   return m;
 }
 
+// The 16 values of lane `sub` of block blk (zero past n).
+__device__ inline void load_16(const float* __restrict__ w, int64_t n, int64_t blk, int sub,
+                               float (&v)[16]) {
+  const int64_t base = blk * kBlock + (int64_t)sub * 16;
+  if (base + 16 <= n) {
+    const floatx4* p = reinterpret_cast<const floatx4*>(w + base);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // plain loads: the four lanes of a block read the same cache lines in
+      // four instructions, which only cached loads serve from one fetch
+      const floatx4 x = p[j];
+      v[4 * j + 0] = x[0];
+      v[4 * j + 1] = x[1];
+      v[4 * j + 2] = x[2];
+      v[4 * j + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = (base + j < n) ? w[base + j] : 0.0f;
+  }
+}
+
+__device__ inline float quantize_16(const float* __restrict__ w, int64_t n, int64_t blk, int sub,
+                                    float* __restrict__ T, const uint8_t* __restrict__ bk,
+                                    u32x2& out_bytes) {
+  float v[16];
+  load_16(w, n, blk, sub, v);
+  return quantize_16v(v, sub, T, bk, out_bytes);
+}
+
 }  // namespace
 
 // packed[nblocks*32], absmax[nblocks]; 64 blocks per 256-thread workgroup.
@@ -165,9 +183,9 @@ __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restri
                                                            uint8_t* __restrict__ packed,
                                                            float* __restrict__ absmax) {
   __shared__ float thr[64 * kTStride];
-  __shared__ uint8_t bk[64];
+  __shared__ uint8_t bk[kNBuckets];
   const int t = threadIdx.x;
-  if (t < 64) bk[t] = kBuckets.first[t];
+  if (t < kNBuckets) bk[t] = kBuckets.first[t];
   __syncthreads();
   const int64_t gt = (int64_t)blockIdx.x * 256 + t;
   const int64_t blk = gt >> 2;
@@ -210,38 +228,53 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
   __shared__ float amax[kGroup];
   __shared__ float red[4];
   __shared__ float thr[64 * kTStride];
-  __shared__ uint8_t bk[64];
+  __shared__ uint8_t bk[kNBuckets];
   const int t = threadIdx.x;
-  if (t < 64) bk[t] = kBuckets.first[t];
+  if (t < kNBuckets) bk[t] = kBuckets.first[t];
   __syncthreads();
-  const int64_t g = blockIdx.x;
   const int sub = t & 3;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int lb = pass * 64 + (t >> 2);
-    const int64_t blk = g * kGroup + lb;
-    float m = 0.0f;
-    if (blk < nblocks) {
-      u32x2 bytes;
-      m = quantize_16(w, n, blk, sub, thr + (t >> 2) * kTStride, bk, bytes);
-      *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
-    }
-    if (sub == 0) amax[lb] = m;
-  }
-  __syncthreads();
-  const int64_t b = g * kGroup + t;
-  const float a = amax[t];
-  float m = a;
+  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  // Workgroups stride over the groups; each group is four passes of 64
+  // blocks, and the next pass (of this group or the next one) is always in
+  // flight while the current one is quantized.
+  auto blk_of = [&](int64_t g, int pass) { return g * kGroup + pass * 64 + (t >> 2); };
+  float vA[16], vB[16];
+  int64_t g = blockIdx.x;
+  if (g < ngroups && blk_of(g, 0) < nblocks) load_16(w, n, blk_of(g, 0), sub, vA);
+  for (; g < ngroups; g += gridDim.x) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((t & 63) == 0) red[t >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float step = dq_step(m);
-  if (t == 0) c2[g] = step;
-  if (b < nblocks) {
-    qabsmax[b] = (int8_t)dq_code(a, step);
-    if (absmax_out) absmax_out[b] = a;
+    for (int pass = 0; pass < 4; ++pass) {
+      float(&cur)[16] = (pass & 1) ? vB : vA;
+      float(&nxt)[16] = (pass & 1) ? vA : vB;
+      const int64_t gn = pass < 3 ? g : g + gridDim.x;
+      const int64_t bn = blk_of(gn, (pass + 1) & 3);
+      if (gn < ngroups && bn < nblocks) load_16(w, n, bn, sub, nxt);
+      const int lb = pass * 64 + (t >> 2);
+      const int64_t blk = g * kGroup + lb;
+      float m = 0.0f;
+      if (blk < nblocks) {
+        u32x2 bytes;
+        m = quantize_16v(cur, sub, thr + (t >> 2) * kTStride, bk, bytes);
+        *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
+      }
+      if (sub == 0) amax[lb] = m;
+    }
+    __syncthreads();
+    const int64_t b = g * kGroup + t;
+    const float a = amax[t];
+    float m = a;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float step = dq_step(m);
+    if (t == 0) c2[g] = step;
+    if (b < nblocks) {
+      qabsmax[b] = (int8_t)dq_code(a, step);
+      if (absmax_out) absmax_out[b] = a;
+    }
+    __syncthreads();  // amax and red are rewritten by the next group
   }
 }
 
