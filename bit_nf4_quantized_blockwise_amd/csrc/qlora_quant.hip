@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __r
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t i = base + threadIdx.x + 256 * u;
-      p[u] = (i < ndwords) ? __builtin_nontemporal_load(packed + i) : 0u;
+      p[u] = (i < ndwords) ? packed[i] : 0u;
       const int64_t b = (i < ndwords ? i : 0) >> 3;  // 8 dwords per 64-block
       ah[u] = c2[b >> 8] * (float)qabsmax[b];
     }
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __r
       const int64_t i = base + threadIdx.x + 256 * u;
       u32x4 o;
       o = decode8(p[u], ah[u], cb);
-      if (i < ndwords) __builtin_nontemporal_store(o, out + i);
+      if (i < ndwords) out[i] = o;
     }
   }
 }
