@@ -600,16 +600,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 
   // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
-  // b mod 8).  Give each XCD a contiguous run of tiles in row-major order
-  // (N fastest), so the workgroups sharing an L2 share their A rows.
+  // b mod 8).  Give each XCD a contiguous run of tiles, in an order that
+  // walks 4 tile rows at a time (down the 4 rows, then the next column): the
+  // 32 workgroups an XCD runs at once then cover about 4 x 8 tiles and share
+  // both their A rows and their B columns through that XCD's L2.
   const int ntiles = g.tiles_m * g.tiles_n;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int per = ntiles >> 3, rem = ntiles & 7;
   const int tile = xcd * per + min(xcd, rem) + slot;
   // (The divisions expand to vector code; readfirstlane brings the results
   // back to scalar registers, so buffer resources built from them are too.)
-  const int tm = __builtin_amdgcn_readfirstlane(tile / g.tiles_n);
-  const int tn = __builtin_amdgcn_readfirstlane(tile - tm * g.tiles_n);
+  constexpr int GM = 4;
+  const int grp = __builtin_amdgcn_readfirstlane(tile / (GM * g.tiles_n));
+  const int gsz = min(g.tiles_m - grp * GM, GM);  // rows in this group
+  const int in = tile - grp * GM * g.tiles_n;
+  const int tm = __builtin_amdgcn_readfirstlane(grp * GM + in % gsz);
+  const int tn = __builtin_amdgcn_readfirstlane(in / gsz);
   const int64_t row0 = (int64_t)tm * MT, col0 = (int64_t)tn * NT;
   const int64_t wrow0 = row0 + wm * WTM;  // this wave's first row
   const int nkt_total = (int)((g.red + KT - 1) / KT);
