@@ -94,6 +94,9 @@ constexpr int SK_MT = 128, SK_NT = 64;      // skinny: U = X·Aᵀ, V = dY·B
 constexpr int TR_MT = 64, TR_NT = 256;      // token-reduction: dA, dB
 constexpr int64_t kBigM = 128;              // use the big tiles from this many tokens on
 constexpr int64_t kFewM = 16;               // up to this many tokens: the streaming GEMV
+// split-K target for the memory-bound rank-r products: one workgroup per CU
+// (more only multiplies the partial sums written and read back)
+constexpr int kSkinnyWgs = 256;
 
 bool use_big(int64_t M) { return M >= kBigM; }
 bool use_gemv(int64_t M) { return M <= kFewM; }
@@ -141,7 +144,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
     w.total = std::max<size_t>(g.ksplit > 1 ? align256((size_t)g.ksplit * M * N * 4) : 0, 256);
     return w;
   }
-  w.pu = plan(M, r, K, SK_MT, SK_NT, true);
+  w.pu = plan(M, r, K, SK_MT, SK_NT, true, kSkinnyWgs);
   const int64_t ldu = (int64_t)w.pu.tiles_n * SK_NT;
   size_t off = 0;
   w.u_part = off;
@@ -179,15 +182,15 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   w.ut = off; off += align256((size_t)r * w.Mp * 2);
   w.at = off; off += align256((size_t)K * w.rp * 2);
   w.part = off;
-  w.pv = plan(M, r, N, SK_MT, SK_NT, true);
+  w.pv = plan(M, r, N, SK_MT, SK_NT, true, kSkinnyWgs);
   size_t part = (size_t)w.pv.nsplit * M * ((size_t)w.pv.tiles_n * SK_NT) * 4;
   if (!use_big(M)) {
     w.pdx = plan(M, K, N, SM_MT, SM_NT, true);
     part = std::max(part, (size_t)w.pdx.nsplit * M * K * 4);
   }
-  w.pda = plan(r, K, M, TR_MT, TR_NT, true);
+  w.pda = plan(r, K, M, TR_MT, TR_NT, true, kSkinnyWgs);
   part = std::max(part, (size_t)w.pda.nsplit * r * K * 4);
-  w.pdb = plan(r, N, M, TR_MT, TR_NT, true);
+  w.pdb = plan(r, N, M, TR_MT, TR_NT, true, kSkinnyWgs);
   part = std::max(part, (size_t)w.pdb.nsplit * r * N * 4);
   off += align256(part);
   w.total = std::max<size_t>(off, 256);
@@ -209,6 +212,18 @@ qlora_status run_reduce(const float* part, int64_t part_stride, int nsplit, int6
                         ReduceOut o0, ReduceOut o1, hipStream_t st) {
   const int64_t total = rows_pad * cols_pad;
   if (total == 0) return QLORA_OK;
+  // four columns per thread when every row of partials and outputs stays
+  // 16-byte (partials) / 8-byte (bf16 rows) aligned
+  auto al = [](const ReduceOut& o) {
+    return o.transposed || ((o.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(o.bf16) & 7u) == 0 &&
+                            (reinterpret_cast<uintptr_t>(o.f32) & 15u) == 0);
+  };
+  if (cols_pad % 4 == 0 && ldp % 4 == 0 && part_stride % 4 == 0 &&
+      (reinterpret_cast<uintptr_t>(part) & 15u) == 0 && al(o0) && al(o1)) {
+    hipLaunchKernelGGL(reduce_partials4_kernel, dim3(grid_for(total / 4)), dim3(256), 0, st, part,
+                       part_stride, nsplit, rows, cols, rows_pad, cols_pad, ldp, scale, o0, o1);
+    return launched();
+  }
   hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid_for(total)), dim3(256), 0, st, part,
                      part_stride, nsplit, rows, cols, rows_pad, cols_pad, ldp, scale, o0, o1);
   return launched();
@@ -589,12 +604,15 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const qlora_bf16* X, co
   float* part = reinterpret_cast<float*>(ws + L.part);
 
   // adapter factors in the layouts the GEMMs read
-  hipLaunchKernelGGL(transpose_pad_kernel, dim3(grid_for(N * (int64_t)r)), dim3(256), 0, st, B,
-                     (int64_t)r, N, (int64_t)r, N, (int64_t)r, Bt, N);
-  hipLaunchKernelGGL(transpose_pad_kernel, dim3(grid_for(M * (int64_t)r)), dim3(256), 0, st, U,
-                     (int64_t)r, M, (int64_t)r, L.Mp, (int64_t)r, Ut, L.Mp);
-  hipLaunchKernelGGL(transpose_pad_kernel, dim3(grid_for(K * L.rp)), dim3(256), 0, st, A, K,
-                     (int64_t)r, K, L.rp, K, At, L.rp);
+  {
+    const TransposeJob jb{B, (int64_t)r, N, (int64_t)r, N, (int64_t)r, Bt, N};
+    const TransposeJob ju{U, (int64_t)r, M, (int64_t)r, L.Mp, (int64_t)r, Ut, L.Mp};
+    const TransposeJob ja{A, K, (int64_t)r, K, L.rp, K, At, L.rp};
+    const int64_t tiles = std::max({ceil_div(N, 64) * ceil_div(r, 64), ceil_div(L.Mp, 64) * ceil_div(r, 64),
+                                    ceil_div(L.rp, 64) * ceil_div(K, 64)});
+    hipLaunchKernelGGL(transpose_pad3_kernel, dim3((unsigned)std::min<int64_t>(tiles, 1024), 3),
+                       dim3(256), 0, st, jb, ju, ja);
+  }
   if ((s = launched()) != QLORA_OK) return s;
 
   // V = dY·B  -> V [M][rp] (zero-padded) and Vᵀ [r][Mp] (zero-padded), bf16
@@ -607,13 +625,20 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const qlora_bf16* X, co
     g.part_stride = M * g.ldo;
     if ((s = run_gemm<SK_MT, SK_NT, 4, 1, B_BF16_CR, false, O_F32>(g, L.pv, st)) != QLORA_OK)
       return s;
-    if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, L.rp, g.ldo, 1.0f,
-                        ReduceOut{V, nullptr, L.rp, 0}, kNoOut, st)) != QLORA_OK)
-      return s;
-    // Vᵀ from the same partials: rows_pad = Mp pads the token axis with zeros
-    if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, L.Mp, r, g.ldo, 1.0f,
-                        ReduceOut{Vt, nullptr, L.Mp, 1}, kNoOut, st)) != QLORA_OK)
-      return s;
+    if (L.rp == r && L.Mp == M) {  // no padding: V and Vᵀ from one pass over the partials
+      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, r, g.ldo, 1.0f,
+                          ReduceOut{V, nullptr, L.rp, 0}, ReduceOut{Vt, nullptr, L.Mp, 1}, st)) !=
+          QLORA_OK)
+        return s;
+    } else {
+      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, L.rp, g.ldo, 1.0f,
+                          ReduceOut{V, nullptr, L.rp, 0}, kNoOut, st)) != QLORA_OK)
+        return s;
+      // Vᵀ from the same partials: rows_pad = Mp pads the token axis with zeros
+      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, L.Mp, r, g.ldo, 1.0f,
+                          ReduceOut{Vt, nullptr, L.Mp, 1}, kNoOut, st)) != QLORA_OK)
+        return s;
+    }
   }
 
   // dX = dY·Ŵ + s·V·A

@@ -43,6 +43,14 @@ struct ReduceOut {
   int32_t transposed;  // write out[col][row] instead of out[row][col]
 };
 
+// out[c][r] = in[r][c] for r < R, c < C; zero for r in [R, Rp) or c in [C, Cp).
+struct TransposeJob {
+  const uint16_t* in;
+  int64_t ldi, R, C, Rp, Cp;
+  uint16_t* out;  // nullptr: no job
+  int64_t ldo;
+};
+
 struct GemvArgs {
   const uint16_t* x;  // [M][K] bf16
   int32_t M;
@@ -81,6 +89,11 @@ __global__ void reduce_partials_kernel(const float* part, int64_t part_stride, i
                                        int64_t rows, int64_t cols, int64_t rows_pad,
                                        int64_t cols_pad, int64_t ldp, float scale, ReduceOut o0,
                                        ReduceOut o1);
+__global__ void reduce_partials4_kernel(const float* part, int64_t part_stride, int32_t nsplit,
+                                       int64_t rows, int64_t cols, int64_t rows_pad,
+                                       int64_t cols_pad, int64_t ldp, float scale, ReduceOut o0,
+                                       ReduceOut o1);
+__global__ void transpose_pad3_kernel(TransposeJob j0, TransposeJob j1, TransposeJob j2);
 __global__ void transpose_pad_kernel(const uint16_t* in, int64_t ldi, int64_t R, int64_t C,
                                      int64_t Rp, int64_t Cp, uint16_t* out, int64_t ldo);
 __global__ void pad_cols_kernel(const uint16_t* in, int64_t ldi, int64_t R, int64_t C, int64_t Cp,
