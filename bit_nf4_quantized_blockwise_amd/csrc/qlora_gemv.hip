@@ -51,6 +51,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 64];
   __shared__ float red[kGemvWaves][G][MG][32][4];  // per-wave partial sums, reduced once at the end
   __shared__ uint16_t ush[16 * 256];         // U rows for the adapter term (M <= 16, r <= 256)
+  __shared__ float ured[kGemvWaves][MG][32][4];  // per-wave partial U when it is formed here
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
@@ -159,6 +160,42 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
 #pragma unroll
   for (int st = 0; st < D; ++st) load(st);  // rows past N read as zero
   load_scales(0, sA);
+
+  // U = X·Aᵀ (r <= 16) with the same operands: the rows of A stand in for a
+  // 16-column group of weights (already bf16, no table), each wave over its
+  // own slice of k; rows r and r + 8 of the result (the two blocks of a
+  // chunk) are folded and the waves summed at the end.
+  const bool form_u = g.a != nullptr;  // uniform
+  if (form_u) {
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(g.a, (int64_t)g.r * K * 2);
+    floatx4 ua[MG];
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) ua[mg] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int64_t kq = (chunk0 + c) * 128 + 32 * qd;
+      u32x4 av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        av[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       ar, kq + 8 * j < K ? (int)(((int64_t)c16 * K + kq + 8 * j) * 2) : 0x7ffffff0, 0, 0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg)
+          ua[mg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[mg][c][j]),
+                                                           __builtin_bit_cast(bf16x8, av[j]), ua[mg],
+                                                           0, 0, 0);
+    }
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ua[mg][i] += __shfl_xor(ua[mg][i], 32);
+        if (lane < 32) ured[w][mg][lane][i] = ua[mg][i];
+      }
+  }
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     Scales& sc = (gi & 1) ? sB : sA;
@@ -216,7 +253,20 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
       const int64_t n = nw0 + i / g.r;
       bsh[i] = n < N ? g.b[n * g.r + i % g.r] : (uint16_t)0;
     }
-    for (int i = tid; i < M * g.r; i += NT) ush[i] = g.u[i];
+    if (form_u) {
+      // U[tok][j] summed over the waves in a fixed order, rounded to bf16
+      // (the stored U the backward pass reads); workgroup 0 writes it out
+      for (int i = tid; i < M * g.r; i += NT) {
+        const int tok = i / g.r, j = i % g.r, mg = tok >> 3, t8 = tok & 7;
+        float v = 0.0f;
+        for (int ww = 0; ww < kGemvWaves; ++ww) v += ured[ww][mg][j + 16 * (t8 >> 2)][t8 & 3];
+        const uint16_t ub = bf16_rne_bits(v);
+        ush[i] = ub;
+        if (blockIdx.x == 0) g.u_out[i] = ub;
+      }
+    } else {
+      for (int i = tid; i < M * g.r; i += NT) ush[i] = g.u[i];
+    }
   }
   __syncthreads();
   for (int o = tid; o < G * MG * 128; o += NT) {

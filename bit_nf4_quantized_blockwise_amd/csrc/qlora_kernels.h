@@ -58,7 +58,10 @@ struct GemvArgs {
   const uint8_t* packed;  // W[N][K] NF4 + DQ
   const int8_t* qabsmax;
   const float* c2;
-  const uint16_t* u;  // [M][r] bf16, pitch r
+  const uint16_t* u;  // [M][r] bf16, pitch r (read when a == nullptr)
+  const uint16_t* a;  // [r][K] bf16: when set, U = X·Aᵀ is formed in the kernel (r <= 16,
+                      // one split) and written to u_out by workgroup 0
+  uint16_t* u_out;
   int32_t r;
   const uint16_t* b;  // [N][r] bf16, pitch r
   float s;
