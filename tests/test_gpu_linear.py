@@ -73,6 +73,10 @@ def _run_case(M, K, N, r, alpha, seed, bwd=True):
     (300, 192, 520, 8, 16.0),     # ragged in M and N, several tiles each way
     (513, 128, 1032, 72, 16.0),   # rank above 64: prologue over two 64-chunks
     (257, 448, 256, 64, 16.0),
+    (3, 8448, 64, 8, 16.0),       # few-token path split over k (partial sums + reduction)
+    (12, 4096, 40, 16, 32.0),     # few tokens in two groups of 8, U formed in the kernel
+    (6, 4096, 40, 32, 16.0),      # few tokens, rank too large to form U in the kernel
+    (2, 1088, 48, 8, 16.0),       # few tokens, byte-wise scale codes, k split in two
 ])
 def test_small_shapes(M, K, N, r, alpha):
     _run_case(M, K, N, r, alpha, seed=M + K + N + r)
