@@ -498,6 +498,15 @@ __device__ inline void interleave() {
   }
 }
 
+// One 32x32x16 step of acc[i][j] += (A rows i)·(B cols j), issued with the
+// operands swapped: the matrix core then produces the transposed block, so
+// that lane l holds output row l mod 32 and, for e = 4g + c, output column
+// 8g + 4 (l / 32) + c — four consecutive columns per group g, which the
+// epilogue stores as one 8- or 16-byte write.
+__device__ inline floatx16 mfma_t(const bf16x8& a, const bf16x8& b, const floatx16& acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
+}
+
 template <int MT, int NT, int WM, int WN>
 struct Mma {
   static constexpr int WTM = MT / WM, WTN = NT / WN;
@@ -560,15 +569,14 @@ struct Mma {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma_t(a[i], b[j], acc[i][j]);
   }
   __device__ inline void mfma(const u32x4 (&a)[FM][4], int ks, const bf16x8 (&b)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i][ks]),
-                                                            b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma_t(__builtin_bit_cast(bf16x8, a[i][ks]), b[j], acc[i][j]);
   }
 };
 
@@ -769,7 +777,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           if ((i * FN + j) * 2 / (FM * FN) == h)
-            mma.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], mma.acc[i][j], 0, 0, 0);
+            mma.acc[i][j] = mfma_t(a[i], b[j], mma.acc[i][j]);
     };
     auto stepd = [&](int cur, BTile& D, BTile& N, int kt) {
       D.prep();
@@ -845,42 +853,53 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   }
 
-  // Epilogue.  32x32 accumulator layout: lane l holds column l%32 and rows
-  // 8*(e/4) + 4*(l/32) + e%4 for e = 0..15.
+  // Epilogue (accumulator layout: see mfma_t).  Lane l owns row
+  // wrow0 + 32 i + l mod 32 of block i and, in column block j, the runs of
+  // four columns 32 j + 8 g + 4 (l / 32) .. +3.
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t wcol0 = col0 + wn * WTN;
-  if (wrow0 + WTM <= g.rows && wcol0 + WTN <= g.cols) {
-    // Whole wave tile in range: the row and column of each store are a
-    // uniform base plus this lane's 32-bit offset.
-    const int loff = lh * 4 * (int)g.ldo + lr;
+  if (wrow0 + WTM <= g.rows && wcol0 + WTN <= g.cols && (g.ldo & 3) == 0) {
+    // Whole wave tile in range, rows 8-byte aligned: one 8-byte (bf16) or
+    // 16-byte (fp32) store per run, at a constant offset from the row start.
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int64_t row = wrow0 + i * 32 + lr;
+      if constexpr (OMODE == O_BF16) {
+        uint16_t* o = g.out_bf16 + row * g.ldo + wcol0 + 4 * lh;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t ru = wrow0 + i * 32 + (e >> 2) * 8 + (e & 3);
-          const float v = mma.acc[i][j][e];
-          if constexpr (OMODE == O_BF16) {
-            uint16_t* o = g.out_bf16 + ru * g.ldo + wcol0 + j * 32;
-            o[loff] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-          } else {
-            float* o = g.out_f32 + (int64_t)blockIdx.y * g.part_stride + ru * g.ldo + wcol0 + j * 32;
-            o[loff] = v;
+          for (int q = 0; q < 4; ++q) {
+            const floatx16& c = mma.acc[i][j];
+            u32x2 v;
+            v[0] = pack_bf16x2(c[4 * q], c[4 * q + 1]);
+            v[1] = pack_bf16x2(c[4 * q + 2], c[4 * q + 3]);
+            *reinterpret_cast<u32x2*>(o + 32 * j + 8 * q) = v;
           }
-        }
+      } else {
+        float* o = g.out_f32 + (int64_t)blockIdx.y * g.part_stride + row * g.ldo + wcol0 + 4 * lh;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const floatx16& c = mma.acc[i][j];
+            *reinterpret_cast<floatx4*>(o + 32 * j + 8 * q) =
+                floatx4{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+          }
+      }
+    }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int64_t row = wrow0 + i * 32 + lr;
+    if (row >= g.rows) continue;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = col0 + wn * WTN + j * 32 + lr;
-      if (col >= g.cols) continue;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = wrow0 + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-        if (row >= g.rows) continue;
+        const int64_t col = wcol0 + j * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+        if (col >= g.cols) continue;
         const float v = mma.acc[i][j][e];
         if constexpr (OMODE == O_BF16) {
           g.out_bf16[row * g.ldo + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
@@ -888,7 +907,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
           g.out_f32[(int64_t)blockIdx.y * g.part_stride + row * g.ldo + col] = v;
         }
       }
-    }
+  }
 }
 
 // Instantiations used by the library.
