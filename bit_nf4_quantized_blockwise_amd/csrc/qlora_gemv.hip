@@ -41,6 +41,18 @@ __device__ inline uint16_t bf16_rne_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// kNF4Bits[i] for a per-lane i, as a tree of selects between literals (no
+// memory read).
+template <int LO, int N>
+__device__ inline uint32_t level_bits_tree(int i) {
+  if constexpr (N == 1) {
+    return kNF4Bits[LO];
+  } else {
+    return (i & (N / 2)) ? level_bits_tree<LO + N / 2, N / 2>(i) : level_bits_tree<LO, N / 2>(i);
+  }
+}
+__device__ inline uint32_t level_bits(int i) { return level_bits_tree<0, 16>(i); }
+
 }  // namespace
 
 template <int CPW, int MG, int G, bool QV>
@@ -57,18 +69,28 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   const int c16 = lane & 15, qd = lane >> 4;
 
   constexpr int NT = 64 * kGemvWaves;
-  for (int i = tid; i < 256 * 16; i += NT) {
-    const int e = i >> 4;
-    const uint32_t v = (uint32_t)bf16_rne_bits(bits_to_float(kNF4Bits[e & 15])) |
-                       ((uint32_t)bf16_rne_bits(bits_to_float(kNF4Bits[e >> 4])) << 16);
-    *reinterpret_cast<u32x4*>(&lut[i * 4]) = u32x4{v, v, v, v};
+  // Table fill: thread t writes entries e = t / 16 + (NT / 16) it (four
+  // copies each), whose low nibble t / 16 mod 16 is fixed and whose high
+  // nibble is t / 256 + (NT / 256) it; the levels come from literals.
+  static_assert(NT % 256 == 0 && 256 * 16 % NT == 0, "table fill");
+  {
+    const uint32_t lo = bf16_rne_bits(bits_to_float(level_bits((tid >> 4) & 15)));
+#pragma unroll
+    for (int it = 0; it < 256 * 16 / NT; ++it) {
+      const uint32_t hi = bf16_rne_bits(bits_to_float(level_bits((tid >> 8) + (NT / 256) * it)));
+      const uint32_t v = lo | (hi << 16);
+      *reinterpret_cast<u32x4*>(&lut[(tid + it * NT) * 4]) = u32x4{v, v, v, v};
+    }
   }
 
   const int64_t K = g.K, N = g.N;
   const int M = g.M;
   const int64_t chunk0 = ((int64_t)blockIdx.y * kGemvWaves + w) * CPW;
 
+  __syncthreads();
+
   // Token operands for this wave's chunks, kept in registers for all columns.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(g.x, (int64_t)M * K * 2);
   u32x4 xa[MG][CPW][4];
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg)
@@ -79,10 +101,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
         const int64_t k = (chunk0 + c) * 128 + 32 * qd + 8 * j;
         const int tok = (c16 & 7) + 8 * mg;
         const bool valid = ((c16 < 8) == (qd < 2)) && tok < M && k < K;
-        xa[mg][c][j] = valid ? *reinterpret_cast<const u32x4*>(g.x + (int64_t)tok * K + k)
-                             : u32x4{0u, 0u, 0u, 0u};
+        xa[mg][c][j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       xr, valid ? (int)(((int64_t)tok * K + k) * 2) : 0x7ffffff0, 0, 0));
       }
-  __syncthreads();
 
   const char* lutb = reinterpret_cast<const char*>(lut);
   const uint32_t lane4 = (uint32_t)lane * 4;
@@ -103,10 +125,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
                                               (N - nw0) * blocks_per_row);
   // Weight chunks stream through a ring of D registers: step s = gi·CPW + c
   // consumes slot s mod D and refills it with step s + D, so D 16-byte loads
-  // per lane stay in flight (two column groups ahead when the token operands
-  // leave room).
-  constexpr int RD = 1;
-  constexpr int D = CPW * RD;
+  // per lane stay in flight.  A register spill here would be worse than a
+  // shallower ring: reloading it waits (in issue order) for every weight load
+  // issued before it.
+  constexpr int D = CPW > 6 ? 6 : CPW;  // six in flight: eight make the widest variant spill
   constexpr int S = G * CPW;
   u32x4 pk[D];
   auto load = [&](int st) {
@@ -160,6 +182,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
 #pragma unroll
   for (int st = 0; st < D; ++st) load(st);  // rows past N read as zero
   load_scales(0, sA);
+
 
   // U = X·Aᵀ (r <= 16) with the same operands: the rows of A stand in for a
   // 16-column group of weights (already bf16, no table), each wave over its
@@ -249,9 +272,14 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   uint16_t* bsh = reinterpret_cast<uint16_t*>(lut);  // [G·16][r]; r <= 256 fits the table
   __syncthreads();  // every wave is done with the table
   if (lora) {
-    for (int i = tid; i < G * 16 * g.r; i += NT) {
-      const int64_t n = nw0 + i / g.r;
-      bsh[i] = n < N ? g.b[n * g.r + i % g.r] : (uint16_t)0;
+    const int nb = G * 16 * g.r;  // B rows nw0 .. nw0 + 16 G are contiguous
+    const int64_t bvalid = (N - nw0) * g.r;
+    if ((g.r & 7) == 0) {  // 16-byte pieces (B is 16-byte aligned)
+      for (int i = tid * 8; i < nb; i += NT * 8)
+        *reinterpret_cast<u32x4*>(bsh + i) =
+            i < bvalid ? *reinterpret_cast<const u32x4*>(g.b + nw0 * g.r + i) : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      for (int i = tid; i < nb; i += NT) bsh[i] = i < bvalid ? g.b[nw0 * g.r + i] : (uint16_t)0;
     }
     if (form_u) {
       // U[tok][j] summed over the waves in a fixed order, rounded to bf16
