@@ -88,9 +88,12 @@ def summarize_pmc(fetch_csv, write_csv, out_path):
         + 2 * M * r + 2 * N * r + 2 * M * N
     with open(out_path, "w") as fh:
         fh.write("# HBM traffic of the forward dequant-GEMM (LLaMA-7B MLP: 4096 tokens, 4096 -> 11008,\n")
-        fh.write("# r = 64), from rocprofv3 FETCH_SIZE and WRITE_SIZE (two --pmc runs of\n")
-        fh.write("# `python3 bench.py --pmc-pass`), each scaled by the same counter on a device\n")
-        fh.write(f"# copy of {CALIB_BYTES} bytes.\n")
+        fh.write("# r = 64), from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by the same counter\n")
+        fh.write(f"# on a device copy of {CALIB_BYTES} bytes.  Commands (from /tmp, TMPDIR=/tmp):\n")
+        fh.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_f> -o f -- python3 <repo>/bench.py --pmc-pass\n")
+        fh.write("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_w> -o w -- python3 <repo>/bench.py --pmc-pass\n")
+        fh.write("#   python3 <repo>/bench.py --summarize-pmc <dir_f>/f_counter_collection.csv "
+                 "<dir_w>/w_counter_collection.csv <this file>\n")
         fh.write(f"kernel_source_sha256_16 = {gemm_source_hash()}\n")
         fh.write(f"fetch_kib_per_launch_raw = {f['gemm']:.1f}\n")
         fh.write(f"write_kib_per_launch_raw = {w['gemm']:.1f}\n")
