@@ -42,6 +42,17 @@ class NF4Weight(ctypes.Structure):
     ]
 
 
+class AdamWTensor(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("m", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("param_bf16", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+    ]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -59,6 +70,9 @@ _SIGNATURES = {
     "qlora_lora_down": ([_P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P], _I32),
     "qlora_nf4_matmul_fwd": ([_W, _P, _I64, _P, _P, _I32, _F, _P, _P, _SZ, _P], _I32),
     "qlora_workspace_size": ([_I32, _I64, _I64, _I64, _I32], _SZ),
+    "qlora_adamw_step": ([ctypes.POINTER(AdamWTensor), _I32, _F, _F, _F, _F, _F, _I64, _F, _P, _P,
+                          _SZ, _P], _I32),
+    "qlora_adamw_workspace_size": ([_I32], _SZ),
     "qlora_nf4_codebook": ([_P], None),
     "qlora_status_string": ([_I32], ctypes.c_char_p),
     "qlora_abi_version": ([], _I32),
@@ -246,3 +260,41 @@ def linear_bwd(wq, X, dY, A, B, U, alpha, workspace=None, dX=None, dA=None, dB=N
                                   alpha, _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
                                   ws.numel(), _stream(dev)), "qlora_linear_bwd")
     return dX, dA, dB
+
+
+# ---- optimizer step on the adapter factors ------------------------------------
+
+def adamw_workspace_size(count):
+    return lib().qlora_adamw_workspace_size(count)
+
+
+def adamw_step(params, grads, ms, vs, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8,
+               weight_decay=0.001, max_grad_norm=0.3, params_bf16=None, grad_norm=None,
+               workspace=None):
+    """One 32-bit AdamW step over lists of float32 tensors (updated in place):
+    params (master weights), grads, ms, vs; params_bf16 (optional list, entries
+    may be None) receives the bf16 copies; grad_norm (optional float32 device
+    tensor of one element) the global gradient norm before clipping.  The
+    defaults are the page's training settings (lr 2e-4, weight decay 0.001,
+    max_grad_norm 0.3) and the usual AdamW betas and eps."""
+    n = len(params)
+    if not (len(grads) == len(ms) == len(vs) == n):
+        raise ValueError("params, grads, ms and vs must have the same length")
+    pbs = params_bf16 if params_bf16 is not None else [None] * n
+    arr = (AdamWTensor * max(n, 1))()
+    for i in range(n):
+        p = params[i]
+        for t in (grads[i], ms[i], vs[i]):
+            if t.numel() != p.numel():
+                raise ValueError(f"tensor {i}: sizes differ")
+        if pbs[i] is not None and pbs[i].numel() != p.numel():
+            raise ValueError(f"tensor {i}: bf16 copy size differs")
+        arr[i] = AdamWTensor(p.data_ptr(), grads[i].data_ptr(), ms[i].data_ptr(), vs[i].data_ptr(),
+                             pbs[i].data_ptr() if pbs[i] is not None else None, p.numel())
+    device = params[0].device if n else torch.device("cuda")
+    if workspace is None:
+        workspace = torch.empty(adamw_workspace_size(n), dtype=torch.uint8, device=device)
+    _check(lib().qlora_adamw_step(arr, n, lr, beta1, beta2, eps, weight_decay, step,
+                                  max_grad_norm, _ptr(grad_norm), _ptr(workspace),
+                                  workspace.numel(), _stream(device)),
+           "qlora_adamw_step")

@@ -704,4 +704,82 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const qlora_bf16* X, co
   return QLORA_OK;
 }
 
+size_t qlora_adamw_workspace_size(int32_t count) {
+  if (count < 0) return 0;
+  const int64_t groups = std::max<int64_t>(1, ceil_div(count, kAdamMaxTensors));
+  return std::max<size_t>(256, (size_t)groups * kAdamNormWgs * sizeof(double));
+}
+
+qlora_status qlora_adamw_step(const qlora_adamw_tensor* t, int32_t count, float lr, float beta1,
+                              float beta2, float eps, float weight_decay, int64_t step,
+                              float max_grad_norm, float* grad_norm, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  QCHECK(count >= 0 && step >= 1, QLORA_ERR_SHAPE);
+  QCHECK(count == 0 || t != nullptr, QLORA_ERR_NULL);
+  QCHECK(std::isfinite(lr) && lr >= 0.0f && std::isfinite(weight_decay) && weight_decay >= 0.0f,
+         QLORA_ERR_UNSUPPORTED);
+  QCHECK(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f, QLORA_ERR_UNSUPPORTED);
+  QCHECK(std::isfinite(eps) && eps > 0.0f && std::isfinite(max_grad_norm), QLORA_ERR_UNSUPPORTED);
+  for (int32_t i = 0; i < count; ++i) {
+    QCHECK(t[i].n >= 0, QLORA_ERR_SHAPE);
+    if (t[i].n == 0) continue;
+    QCHECK(t[i].param && t[i].grad && t[i].m && t[i].v, QLORA_ERR_NULL);
+    QCHECK(aligned16(t[i].param) && aligned16(t[i].grad) && aligned16(t[i].m) && aligned16(t[i].v),
+           QLORA_ERR_ALIGN);
+    QCHECK(t[i].param_bf16 == nullptr || aligned16(t[i].param_bf16), QLORA_ERR_ALIGN);
+  }
+  QCHECK(grad_norm == nullptr || aligned16(grad_norm), QLORA_ERR_ALIGN);
+  const bool clip = max_grad_norm > 0.0f;
+  const bool need_norm = clip || grad_norm != nullptr;
+  if (need_norm)
+    QCHECK(workspace != nullptr && aligned16(workspace) &&
+               ws_bytes >= qlora_adamw_workspace_size(count),
+           QLORA_ERR_WORKSPACE);
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  if (count == 0) return QLORA_OK;
+  hipStream_t st = as_stream(stream);
+
+  AdamHyper h{};
+  h.beta1 = beta1;
+  h.beta2 = beta2;
+  h.eps = eps;
+  h.decay = (float)(1.0 - (double)lr * (double)weight_decay);
+  h.step_size = (float)((double)lr / (1.0 - std::pow((double)beta1, (double)step)));
+  h.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow((double)beta2, (double)step)));
+  h.max_norm = max_grad_norm;
+  h.clip = clip ? 1 : 0;
+
+  const int groups = (int)ceil_div(count, kAdamMaxTensors);
+  auto list_of = [&](int gidx) {
+    AdamList L{};
+    const int first = gidx * kAdamMaxTensors;
+    L.count = std::min(kAdamMaxTensors, count - first);
+    int64_t u = 0;
+    for (int i = 0; i < L.count; ++i) {
+      const qlora_adamw_tensor& x = t[first + i];
+      L.t[i] = AdamTensor{x.param, x.grad, x.m, x.v, x.param_bf16, x.n, u};
+      u += ceil_div(x.n, 4);
+    }
+    L.units = u;
+    return L;
+  };
+  double* partials = static_cast<double*>(workspace);
+  if (need_norm) {
+    for (int gidx = 0; gidx < groups; ++gidx)
+      hipLaunchKernelGGL(adam_sqnorm_kernel, dim3(kAdamNormWgs), dim3(kAdamThreads), 0, st,
+                         list_of(gidx), partials + (size_t)gidx * kAdamNormWgs);
+    if ((s = launched()) != QLORA_OK) return s;
+  }
+  for (int gidx = 0; gidx < groups; ++gidx) {
+    const AdamList L = list_of(gidx);
+    const int grid = (int)std::min<int64_t>(std::max<int64_t>(1, ceil_div(L.units, kAdamThreads)),
+                                            8 * device_cus());
+    hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kAdamThreads), 0, st, L, h,
+                       need_norm ? partials : nullptr, need_norm ? groups * kAdamNormWgs : 0,
+                       gidx == 0 ? grad_norm : nullptr);
+  }
+  return launched();
+}
+
 }  // extern "C"

@@ -148,6 +148,44 @@ qlora_status qlora_nf4_matmul_fwd(const qlora_nf4_weight *w /* host struct */,
                                   const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *Y,
                                   void *workspace, size_t ws_bytes, void *stream);
 
+/* ---- optimizer step on the adapter factors ------------------------------ */
+
+/* One trainable tensor of the AdamW step.  param, m and v are float32 and
+ * updated in place; grad is read; param_bf16 (optional, may be NULL) receives
+ * RNE_bf16 of the updated param — the bf16 factor the linear computes with. */
+typedef struct {
+  float *param;
+  const float *grad;
+  float *m;
+  float *v;
+  qlora_bf16 *param_bf16;
+  int64_t n;
+} qlora_adamw_tensor;
+
+/* 32-bit AdamW over a list of tensors ("QLoRAの理論と実装", §5-3 Paged
+ * Optimizers: Adam's first and second moments in FP32, with the FP32 master
+ * weight 12 bytes per trainable parameter; the training example's
+ * paged_adamw_32bit with max_grad_norm).  AdamW as published (decoupled decay),
+ * t = step >= 1:
+ *   coef = min(1, max_grad_norm / (||g||_2 + 1e-6)), the norm over every element
+ *          of every tensor in the list (coef = 1 when max_grad_norm <= 0)
+ *   p <- p·(1 − lr·weight_decay);  m <- β1·m + (1−β1)·coef·g;
+ *   v <- β2·v + (1−β2)·(coef·g)²;  p <- p − lr/(1−β1^t) · m / (sqrt(v)/sqrt(1−β2^t) + eps)
+ * Arithmetic in float32 (the bias corrections in float64 on the host); the
+ * norm is a fixed-order float64 reduction, so repeated steps are bitwise
+ * equal.  grad_norm (optional device float) receives the norm before
+ * clipping.  workspace (at least qlora_adamw_workspace_size(count) bytes) is
+ * needed when max_grad_norm > 0 or grad_norm != NULL, else may be NULL.
+ * tensors is a host array; tensors with n == 0 may have NULL pointers.
+ * Requires 0 <= β1, β2 < 1, eps > 0, lr >= 0, weight_decay >= 0. */
+qlora_status qlora_adamw_step(const qlora_adamw_tensor *tensors /* host array */, int32_t count,
+                              float lr, float beta1, float beta2, float eps, float weight_decay,
+                              int64_t step, float max_grad_norm, float *grad_norm,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace qlora_adamw_step needs for `count` tensors (0 if count < 0). */
+size_t qlora_adamw_workspace_size(int32_t count);
+
 /* Bytes of device workspace needed by op 0 (forward, also qlora_lora_down and
  * qlora_nf4_matmul_fwd) or op 1 (backward).  Returns 0 for an invalid op. */
 size_t qlora_workspace_size(int32_t op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);

@@ -109,3 +109,36 @@ def test_valid_arguments_without_gpu_report_device(L):
     assert L.qlora_quantize_nf4(FAKE, 100, 64, FAKE, FAKE, None) == DEV
     assert L.qlora_linear_fwd(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, 1 << 30,
                               None) == DEV
+
+
+def test_adamw_argument_errors(L):
+    T = q.AdamWTensor
+    good = T(FAKE, FAKE, FAKE, FAKE, None, 8)
+    arr = (T * 2)(good, good)
+    f = L.qlora_adamw_step
+    args = dict(lr=2e-4, b1=0.9, b2=0.999, eps=1e-8, wd=0.001, step=1, clip=0.3)
+
+    def call(a=arr, n=2, ws=FAKE, wsb=1 << 20, gn=None, **kw):
+        p = dict(args, **kw)
+        return f(a, n, p["lr"], p["b1"], p["b2"], p["eps"], p["wd"], p["step"], p["clip"], gn, ws,
+                 wsb, None)
+
+    assert call(n=-1) == SHAPE
+    assert call(step=0) == SHAPE
+    assert call(b1=1.0) == UNSUP
+    assert call(b2=-0.1) == UNSUP
+    assert call(eps=0.0) == UNSUP
+    assert call(lr=-1.0) == UNSUP
+    assert call(wd=float("nan")) == UNSUP
+    assert call(ws=None) == WS                     # clipping needs the workspace
+    assert call(wsb=8) == WS
+    assert call(gn=MIS) == ALIGN
+    bad = (T * 1)(T(MIS, FAKE, FAKE, FAKE, None, 8))
+    assert call(a=bad, n=1) == ALIGN
+    bad = (T * 1)(T(FAKE, None, FAKE, FAKE, None, 8))
+    assert call(a=bad, n=1) == NULL
+    bad = (T * 1)(T(FAKE, FAKE, FAKE, FAKE, None, -1))
+    assert call(a=bad, n=1) == SHAPE
+    assert L.qlora_adamw_workspace_size(-1) == 0
+    assert L.qlora_adamw_workspace_size(0) >= 256
+    assert L.qlora_adamw_workspace_size(200) >= 5 * 256 * 8

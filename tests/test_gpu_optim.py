@@ -1,0 +1,126 @@
+"""GPU parity of the 32-bit AdamW step against the oracle.
+
+Each step is checked on its own: the oracle (float64) starts from the GPU's
+previous float32 state, so the bound covers one step's float32 arithmetic.
+With u the update term lr/(1-β1^t) · m / (sqrt(v)/sqrt(1-β2^t) + eps):
+  |p - p_ref| <= 16·2^-24·|u_ref| + 2·2^-24·(|p_prev| + |p_ref|)
+  |m - m_ref| <= 4·2^-24·(β1·|m_prev| + (1-β1)·|g|)
+  |v - v_ref| <= 6·2^-24·(β2·v_prev + (1-β2)·g²)
+(a few roundings each: the products, the sum, sqrt, the division, and the
+float32 step size, bias correction and clipping coefficient).  The oracle is
+given the hyperparameters as the float32 values the entry point receives
+(0.9 as a float32 is 0.89999998, and 1 - β1 then differs from 0.1 by 4 ulp).
+The bf16 copy must be RNE_bf16 of the float32 result, bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.optim import BETA1, BETA2, EPS, adamw_step, clip_coefficient, global_grad_norm
+
+from support import host, say
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("bit_nf4_quantized_blockwise_amd")
+
+ULP = 2.0 ** -24
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+B1, B2, E = f32(BETA1), f32(BETA2), f32(EPS)
+
+
+def _state(rng, n, step0):
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = (rng.standard_normal(n) * rng.uniform(0.01, 2.0)).astype(np.float32)
+    if step0 == 0:
+        m = np.zeros(n, np.float32)
+        v = np.zeros(n, np.float32)
+    else:  # a state as after some steps
+        m = (rng.standard_normal(n) * 0.05).astype(np.float32)
+        v = (np.abs(rng.standard_normal(n)) * 0.01).astype(np.float32)
+    return p, g, m, v
+
+
+def _np(t):
+    return host(t).numpy()
+
+
+def _run(sizes, steps, lr=2e-4, wd=0.001, max_norm=0.3, seed=0, step0=0):
+    rng = np.random.default_rng(seed)
+    dev = torch.device("cuda:0")
+    st = [_state(rng, n, step0) for n in sizes]
+    P = [torch.from_numpy(s[0].copy()).to(dev) for s in st]
+    M = [torch.from_numpy(s[2].copy()).to(dev) for s in st]
+    V = [torch.from_numpy(s[3].copy()).to(dev) for s in st]
+    PB = [torch.empty(n, dtype=torch.bfloat16, device=dev) if i % 2 == 0 else None
+          for i, n in enumerate(sizes)]
+    norm_t = torch.zeros(4, dtype=torch.float32, device=dev)
+    for k, step in enumerate(steps):
+        grads = [(rng.standard_normal(n) * (0.1 + i)).astype(np.float32)
+                 for i, n in enumerate(sizes)]
+        G = [torch.from_numpy(g).to(dev) for g in grads]
+        p0 = [_np(x).astype(np.float64) for x in P]
+        m0 = [_np(x).astype(np.float64) for x in M]
+        v0 = [_np(x).astype(np.float64) for x in V]
+        say(f"[adamw] sizes={sizes} step={step} max_norm={max_norm}")
+        q.adamw_step(P, G, M, V, step, lr=lr, weight_decay=wd, max_grad_norm=max_norm,
+                     params_bf16=PB, grad_norm=norm_t[:1])
+        torch.cuda.synchronize()
+        norm = global_grad_norm(grads)
+        assert abs(float(_np(norm_t)[0]) - norm) <= 1e-6 * norm + 1e-30
+        coef = clip_coefficient(norm, f32(max_norm))
+        for i in range(len(sizes)):
+            pr, mr, vr = adamw_step(p0[i], grads[i], m0[i], v0[i], step, f32(lr), beta1=B1,
+                                    beta2=B2, eps=E, weight_decay=f32(wd), coef=coef)
+            gp, gm, gv = (_np(x).astype(np.float64) for x in (P[i], M[i], V[i]))
+            g = np.asarray(grads[i], np.float64) * coef
+            u = (f32(lr) / (1 - B1 ** step)) * mr / (np.sqrt(vr / (1 - B2 ** step)) + E)
+            bp = 16 * ULP * np.abs(u) + 2 * ULP * (np.abs(p0[i]) + np.abs(pr)) + 1e-30
+            worst = np.max(np.abs(gp - pr) / bp) if gp.size else 0.0
+            assert worst <= 1.0, (i, worst)
+            assert np.all(np.abs(gm - mr) <= 4 * ULP * (B1 * np.abs(m0[i]) + (1 - B1) * np.abs(g))
+                          + 1e-30), i
+            assert np.all(np.abs(gv - vr) <= 6 * ULP * (B2 * v0[i] + (1 - B2) * g * g) + 1e-38), i
+            if PB[i] is not None:
+                ref = P[i].to(torch.bfloat16)  # RNE of the float32 master
+                assert torch.equal(PB[i].view(torch.int16), ref.view(torch.int16)), i
+
+
+@pytest.mark.parametrize("max_norm", [0.3, 0.0, 1e6])
+def test_multi_tensor_steps(max_norm):
+    _run([1, 3, 4, 5, 257, 4096 * 64 + 3, 0, 11008], [1, 2, 3], max_norm=max_norm)
+
+
+def test_late_step_and_existing_moments():
+    _run([64 * 4096, 11008 * 64], [1000, 1001], step0=1, seed=3)
+
+
+def test_more_tensors_than_one_launch_holds():
+    # 100 tensors: three launches share one global norm
+    _run([17 + (i * 37) % 300 for i in range(100)], [1, 2], seed=5)
+
+
+def test_no_decay_no_clip_repeatable():
+    dev = torch.device("cuda:0")
+    outs = []
+    for _ in range(2):
+        state = _state(np.random.default_rng(9), 100003, 0)
+        p, g, m, v = (torch.from_numpy(x).to(dev) for x in state)
+        q.adamw_step([p], [g], [m], [v], 1, lr=1e-3, weight_decay=0.0, max_grad_norm=0.0)
+        torch.cuda.synchronize()
+        outs.append((_np(p).view(np.uint32), _np(m).view(np.uint32), _np(v).view(np.uint32)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
+def test_empty_list_and_zero_sizes():
+    dev = torch.device("cuda:0")
+    q.adamw_step([], [], [], [], 1)
+    e = torch.empty(0, dtype=torch.float32, device=dev)
+    q.adamw_step([e], [e], [e], [e], 1)
+    torch.cuda.synchronize()
