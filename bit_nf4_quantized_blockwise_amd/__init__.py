@@ -268,6 +268,47 @@ def adamw_workspace_size(count):
     return lib().qlora_adamw_workspace_size(count)
 
 
+class AdamWList:
+    """The descriptor array of one AdamW tensor list (float32 params, grads, ms,
+    vs and optional bf16 copies), checked and built once so that a training
+    loop can step the same tensors without re-marshalling them.  The tensors
+    must stay alive and keep their storage while the list is used."""
+
+    def __init__(self, params, grads, ms, vs, params_bf16=None):
+        n = len(params)
+        if not (len(grads) == len(ms) == len(vs) == n):
+            raise ValueError("params, grads, ms and vs must have the same length")
+        pbs = params_bf16 if params_bf16 is not None else [None] * n
+        if len(pbs) != n:
+            raise ValueError("params_bf16 must have one entry (or None) per param")
+        arr = (AdamWTensor * max(n, 1))()
+        for i in range(n):
+            p = params[i]
+            for t in (grads[i], ms[i], vs[i]):
+                if t.numel() != p.numel():
+                    raise ValueError(f"tensor {i}: sizes differ")
+            if pbs[i] is not None and pbs[i].numel() != p.numel():
+                raise ValueError(f"tensor {i}: bf16 copy size differs")
+            arr[i] = AdamWTensor(p.data_ptr(), grads[i].data_ptr(), ms[i].data_ptr(),
+                                 vs[i].data_ptr(),
+                                 pbs[i].data_ptr() if pbs[i] is not None else None, p.numel())
+        self.arr, self.count = arr, n
+        self.device = params[0].device if n else torch.device("cuda")
+        self._keep = (list(params), list(grads), list(ms), list(vs), list(pbs))
+
+
+def adamw_step_list(lst, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.001,
+                    max_grad_norm=0.3, grad_norm=None, workspace=None):
+    """adamw_step over a prebuilt AdamWList."""
+    if workspace is None:
+        workspace = torch.empty(adamw_workspace_size(lst.count), dtype=torch.uint8,
+                                device=lst.device)
+    _check(lib().qlora_adamw_step(lst.arr, lst.count, lr, beta1, beta2, eps, weight_decay, step,
+                                  max_grad_norm, _ptr(grad_norm), _ptr(workspace),
+                                  workspace.numel(), _stream(lst.device)),
+           "qlora_adamw_step")
+
+
 def adamw_step(params, grads, ms, vs, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8,
                weight_decay=0.001, max_grad_norm=0.3, params_bf16=None, grad_norm=None,
                workspace=None):
@@ -277,24 +318,6 @@ def adamw_step(params, grads, ms, vs, step, lr=2e-4, beta1=0.9, beta2=0.999, eps
     tensor of one element) the global gradient norm before clipping.  The
     defaults are the page's training settings (lr 2e-4, weight decay 0.001,
     max_grad_norm 0.3) and the usual AdamW betas and eps."""
-    n = len(params)
-    if not (len(grads) == len(ms) == len(vs) == n):
-        raise ValueError("params, grads, ms and vs must have the same length")
-    pbs = params_bf16 if params_bf16 is not None else [None] * n
-    arr = (AdamWTensor * max(n, 1))()
-    for i in range(n):
-        p = params[i]
-        for t in (grads[i], ms[i], vs[i]):
-            if t.numel() != p.numel():
-                raise ValueError(f"tensor {i}: sizes differ")
-        if pbs[i] is not None and pbs[i].numel() != p.numel():
-            raise ValueError(f"tensor {i}: bf16 copy size differs")
-        arr[i] = AdamWTensor(p.data_ptr(), grads[i].data_ptr(), ms[i].data_ptr(), vs[i].data_ptr(),
-                             pbs[i].data_ptr() if pbs[i] is not None else None, p.numel())
-    device = params[0].device if n else torch.device("cuda")
-    if workspace is None:
-        workspace = torch.empty(adamw_workspace_size(n), dtype=torch.uint8, device=device)
-    _check(lib().qlora_adamw_step(arr, n, lr, beta1, beta2, eps, weight_decay, step,
-                                  max_grad_norm, _ptr(grad_norm), _ptr(workspace),
-                                  workspace.numel(), _stream(device)),
-           "qlora_adamw_step")
+    adamw_step_list(AdamWList(params, grads, ms, vs, params_bf16), step, lr=lr, beta1=beta1,
+                    beta2=beta2, eps=eps, weight_decay=weight_decay,
+                    max_grad_norm=max_grad_norm, grad_norm=grad_norm, workspace=workspace)

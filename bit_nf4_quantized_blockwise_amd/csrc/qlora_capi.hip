@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "qlora_kernels.h"
+#include "qlora_optim.h"
 
 using namespace qlora;
 
@@ -704,10 +705,14 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const qlora_bf16* X, co
   return QLORA_OK;
 }
 
+// AdamW workspace: the clipping coefficient (float) at byte 0, the norm
+// launches' float64 partial sums from byte kAdamPartialsOffset.
+constexpr size_t kAdamPartialsOffset = 256;
+
 size_t qlora_adamw_workspace_size(int32_t count) {
   if (count < 0) return 0;
   const int64_t groups = std::max<int64_t>(1, ceil_div(count, kAdamMaxTensors));
-  return std::max<size_t>(256, (size_t)groups * kAdamNormWgs * sizeof(double));
+  return kAdamPartialsOffset + (size_t)groups * kAdamNormWgs * sizeof(double);
 }
 
 qlora_status qlora_adamw_step(const qlora_adamw_tensor* t, int32_t count, float lr, float beta1,
@@ -747,37 +752,45 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor* t, int32_t count, float 
   h.decay = (float)(1.0 - (double)lr * (double)weight_decay);
   h.step_size = (float)((double)lr / (1.0 - std::pow((double)beta1, (double)step)));
   h.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow((double)beta2, (double)step)));
-  h.max_norm = max_grad_norm;
-  h.clip = clip ? 1 : 0;
 
+  // Groups of kAdamMaxTensors tensors, each one list per launch.
   const int groups = (int)ceil_div(count, kAdamMaxTensors);
   auto list_of = [&](int gidx) {
     AdamList L{};
     const int first = gidx * kAdamMaxTensors;
     L.count = std::min(kAdamMaxTensors, count - first);
-    int64_t u = 0;
+    int64_t c = 0;
     for (int i = 0; i < L.count; ++i) {
       const qlora_adamw_tensor& x = t[first + i];
-      L.t[i] = AdamTensor{x.param, x.grad, x.m, x.v, x.param_bf16, x.n, u};
-      u += ceil_div(x.n, 4);
+      L.t[i] = AdamTensor{x.param, x.grad, x.m, x.v, x.param_bf16, x.n, c};
+      c += ceil_div(x.n, kAdamChunk);
     }
-    L.units = u;
+    L.chunks = c;
     return L;
   };
-  double* partials = static_cast<double*>(workspace);
+  float* coef = static_cast<float*>(workspace);
   if (need_norm) {
-    for (int gidx = 0; gidx < groups; ++gidx)
-      hipLaunchKernelGGL(adam_sqnorm_kernel, dim3(kAdamNormWgs), dim3(kAdamThreads), 0, st,
-                         list_of(gidx), partials + (size_t)gidx * kAdamNormWgs);
+    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) +
+                                                 kAdamPartialsOffset);
+    int32_t npart = 0;  // partial sums packed back to back, in group order
+    for (int gidx = 0; gidx < groups; ++gidx) {
+      const AdamList L = list_of(gidx);
+      if (L.chunks == 0) continue;
+      const int grid = (int)std::min<int64_t>(L.chunks, kAdamNormWgs);
+      hipLaunchKernelGGL(adam_sqnorm_kernel, dim3(grid), dim3(kAdamThreads), 0, st, L,
+                         partials + npart);
+      npart += grid;
+    }
+    hipLaunchKernelGGL(adam_clip_kernel, dim3(1), dim3(kAdamThreads), 0, st, partials, npart,
+                       max_grad_norm, clip ? 1 : 0, coef, grad_norm);
     if ((s = launched()) != QLORA_OK) return s;
   }
   for (int gidx = 0; gidx < groups; ++gidx) {
     const AdamList L = list_of(gidx);
-    const int grid = (int)std::min<int64_t>(std::max<int64_t>(1, ceil_div(L.units, kAdamThreads)),
-                                            8 * device_cus());
+    if (L.chunks == 0) continue;
+    const int grid = (int)std::min<int64_t>(L.chunks, kAdamMaxGrid);
     hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kAdamThreads), 0, st, L, h,
-                       need_norm ? partials : nullptr, need_norm ? groups * kAdamNormWgs : 0,
-                       gidx == 0 ? grad_norm : nullptr);
+                       clip ? coef : nullptr);
   }
   return launched();
 }

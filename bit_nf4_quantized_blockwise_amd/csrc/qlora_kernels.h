@@ -97,36 +97,6 @@ __global__ void reduce_partials4_kernel(const float* part, int64_t part_stride, 
                                        int64_t cols_pad, int64_t ldp, float scale, ReduceOut o0,
                                        ReduceOut o1);
 __global__ void transpose_pad3_kernel(TransposeJob j0, TransposeJob j1, TransposeJob j2);
-
-// ---- AdamW (32-bit states) over a list of tensors ---------------------------
-constexpr int kAdamThreads = 256;
-constexpr int kAdamMaxTensors = 48;  // tensors per launch (the list travels in the kernel arguments)
-constexpr int kAdamNormWgs = 256;    // workgroups (float64 partial sums) of one norm launch
-struct AdamTensor {
-  float* p;        // fp32 master weights
-  const float* g;  // fp32 gradient
-  float* m;
-  float* v;
-  uint16_t* pb;    // bf16 copy of p after the step, or nullptr
-  int64_t n;
-  int64_t u0;      // first 4-element unit of this tensor within the launch
-};
-struct AdamList {
-  AdamTensor t[kAdamMaxTensors];
-  int32_t count;
-  int64_t units;
-};
-struct AdamHyper {
-  float beta1, beta2, eps;
-  float decay;         // 1 - lr·wd
-  float step_size;     // lr / (1 - beta1^t)
-  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
-  float max_norm;
-  int32_t clip;
-};
-__global__ void adam_sqnorm_kernel(AdamList L, double* partials);
-__global__ void adam_update_kernel(AdamList L, AdamHyper h, const double* partials, int32_t npart,
-                                   float* norm_out);
 __global__ void transpose_pad_kernel(const uint16_t* in, int64_t ldi, int64_t R, int64_t C,
                                      int64_t Rp, int64_t Cp, uint16_t* out, int64_t ldo);
 __global__ void pad_cols_kernel(const uint16_t* in, int64_t ldi, int64_t R, int64_t C, int64_t Cp,

@@ -11,24 +11,31 @@
 //   p <- p − (lr / (1 − β1^t)) · m / (sqrt(v) / sqrt(1 − β2^t) + ε)
 // and the bf16 copy the layer computes with is RNE_bf16(p).
 //
-// Both kernels stream every tensor once with 16-byte accesses (4 elements per
-// lane); the work is split in units of 4 elements, a tensor's last unit
-// possibly short.  The global norm is two fixed-order reductions (per
-// workgroup, then over the workgroups' float64 partial sums, which every
-// workgroup of the update redoes), so the step is bitwise repeatable.
+// The tensors are cut into chunks of kAdamChunk elements (a tensor's last
+// chunk may be short), so a workgroup step never straddles two tensors: the
+// tensor of a chunk is found once per workgroup step, by a binary search over
+// the tensors' first chunks, and every lane keeps kAdamUnroll 16-byte loads of
+// each stream in flight; full chunks stream with nontemporal loads and stores
+// (nothing is re-read).  The global norm is two fixed-order reductions (per
+// workgroup in float64, then one workgroup over those partial sums, which
+// also forms the clipping coefficient), so the step is bitwise repeatable.
 
-#include "qlora_kernels.h"
+#include "qlora_optim.h"
 
 namespace qlora {
 
 namespace {
 
-// Tensor of unit u (units of 4 elements, tensors back to back).
-__device__ inline int tensor_of(const AdamList& L, int64_t u) {
-  int t = 0;
-#pragma unroll 1
-  for (int i = 1; i < L.count; ++i) t = u >= L.t[i].u0 ? i : t;
-  return t;
+// The tensor holding chunk c: the last tensor whose first chunk is <= c (a
+// tensor of no elements shares its first chunk with the next one).
+__device__ inline int chunk_tensor(const AdamList& L, int64_t c) {
+  int lo = 0, hi = L.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (L.t[mid].c0 <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
 __device__ inline double block_sum(double v, double* sh) {
@@ -45,39 +52,79 @@ __device__ inline double block_sum(double v, double* sh) {
   return r;
 }
 
+__device__ inline double sq4(const floatx4& g) {
+  double a = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a += (double)g[e] * (double)g[e];
+  return a;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kAdamThreads) void adam_sqnorm_kernel(AdamList L, double* partials) {
   __shared__ double sh[kAdamThreads];
   double acc = 0.0;
-  const int64_t stride = (int64_t)gridDim.x * kAdamThreads;
-  for (int64_t u = (int64_t)blockIdx.x * kAdamThreads + threadIdx.x; u < L.units; u += stride) {
-    const AdamTensor& T = L.t[tensor_of(L, u)];
-    const int64_t i = (u - T.u0) * 4;
-    if (i + 4 <= T.n) {
-      const floatx4 g = *reinterpret_cast<const floatx4*>(T.g + i);
+  for (int64_t c = blockIdx.x; c < L.chunks; c += gridDim.x) {
+    const AdamTensor& T = L.t[chunk_tensor(L, c)];
+    const int64_t base = (c - T.c0) * kAdamChunk;
+    if (base + kAdamChunk <= T.n) {
+      floatx4 g[kAdamUnroll];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc += (double)g[e] * (double)g[e];
+      for (int k = 0; k < kAdamUnroll; ++k)
+        g[k] = *reinterpret_cast<const floatx4*>(T.g + base + (k * kAdamThreads + threadIdx.x) * 4);
+#pragma unroll
+      for (int k = 0; k < kAdamUnroll; ++k) acc += sq4(g[k]);
     } else {
-      for (int64_t j = i; j < T.n; ++j) acc += (double)T.g[j] * (double)T.g[j];
+#pragma unroll 1
+      for (int k = 0; k < kAdamUnroll; ++k) {
+        const int64_t i = base + (k * kAdamThreads + threadIdx.x) * 4;
+        if (i + 4 <= T.n) {
+          acc += sq4(*reinterpret_cast<const floatx4*>(T.g + i));
+        } else {
+          for (int64_t j = i; j < T.n; ++j) acc += (double)T.g[j] * (double)T.g[j];
+        }
+      }
     }
   }
   const double s = block_sum(acc, sh);
   if (threadIdx.x == 0) partials[blockIdx.x] = s;
 }
 
-__global__ __launch_bounds__(kAdamThreads) void adam_update_kernel(AdamList L, AdamHyper h,
-                                                                   const double* partials,
-                                                                   int32_t npart, float* norm_out) {
+__global__ __launch_bounds__(kAdamThreads) void adam_clip_kernel(const double* partials,
+                                                                 int32_t npart, float max_norm,
+                                                                 int32_t clip, float* coef,
+                                                                 float* norm_out) {
+  // Eight independent accumulators per lane keep eight loads in flight; the
+  // summation order depends on npart only.
+  constexpr int A = 8;
   __shared__ double sh[kAdamThreads];
-  float coef = 1.0f;
-  if (npart > 0) {
-    double acc = 0.0;
-    for (int i = threadIdx.x; i < npart; i += kAdamThreads) acc += partials[i];
-    const double norm = sqrt(block_sum(acc, sh));
-    if (h.clip) coef = (float)fmin(1.0, (double)h.max_norm / (norm + 1e-6));
-    if (norm_out && blockIdx.x == 0 && threadIdx.x == 0) *norm_out = (float)norm;
+  double acc[A];
+#pragma unroll
+  for (int a = 0; a < A; ++a) acc[a] = 0.0;
+  int i = threadIdx.x;
+  for (; i + (A - 1) * kAdamThreads < npart; i += A * kAdamThreads) {
+    double x[A];
+#pragma unroll
+    for (int a = 0; a < A; ++a) x[a] = partials[i + a * kAdamThreads];
+#pragma unroll
+    for (int a = 0; a < A; ++a) acc[a] += x[a];
   }
+#pragma unroll
+  for (int a = 0; a < A - 1; ++a)
+    if (i + a * kAdamThreads < npart) acc[a] += partials[i + a * kAdamThreads];
+  double t = 0.0;
+#pragma unroll
+  for (int a = 0; a < A; ++a) t += acc[a];
+  const double norm = sqrt(block_sum(t, sh));
+  if (threadIdx.x == 0) {
+    *coef = clip ? (float)fmin(1.0, (double)max_norm / (norm + 1e-6)) : 1.0f;
+    if (norm_out) *norm_out = (float)norm;
+  }
+}
+
+__global__ __launch_bounds__(kAdamThreads) void adam_update_kernel(AdamList L, AdamHyper h,
+                                                                   const float* coef_p) {
+  const float coef = coef_p ? *coef_p : 1.0f;
   const float b1 = h.beta1, b2 = h.beta2, c1 = 1.0f - h.beta1, c2 = 1.0f - h.beta2;
   auto one = [&](float& p, float g, float& m, float& v) {
     g *= coef;
@@ -86,35 +133,70 @@ __global__ __launch_bounds__(kAdamThreads) void adam_update_kernel(AdamList L, A
     v = b2 * v + c2 * (g * g);
     p -= h.step_size * (m / (sqrtf(v) * h.inv_sqrt_bc2 + h.eps));
   };
-  const int64_t stride = (int64_t)gridDim.x * kAdamThreads;
-  for (int64_t u = (int64_t)blockIdx.x * kAdamThreads + threadIdx.x; u < L.units; u += stride) {
-    const AdamTensor& T = L.t[tensor_of(L, u)];
-    const int64_t i = (u - T.u0) * 4;
-    if (i + 4 <= T.n) {
-      floatx4 p = *reinterpret_cast<const floatx4*>(T.p + i);
-      const floatx4 g = *reinterpret_cast<const floatx4*>(T.g + i);
-      floatx4 m = *reinterpret_cast<const floatx4*>(T.m + i);
-      floatx4 v = *reinterpret_cast<const floatx4*>(T.v + i);
+  auto four = [&](floatx4& p, const floatx4& g, floatx4& m, floatx4& v) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pe = p[e], me = m[e], ve = v[e];
-        one(pe, g[e], me, ve);
-        p[e] = pe;
-        m[e] = me;
-        v[e] = ve;
+    for (int e = 0; e < 4; ++e) {
+      float pe = p[e], me = m[e], ve = v[e];
+      one(pe, g[e], me, ve);
+      p[e] = pe;
+      m[e] = me;
+      v[e] = ve;
+    }
+  };
+  auto store4 = [&](const AdamTensor& T, int64_t i, const floatx4& p, const floatx4& m,
+                    const floatx4& v) {
+    *reinterpret_cast<floatx4*>(T.p + i) = p;
+    *reinterpret_cast<floatx4*>(T.m + i) = m;
+    *reinterpret_cast<floatx4*>(T.v + i) = v;
+    if (T.pb)
+      *reinterpret_cast<u32x2*>(T.pb + i) = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+  };
+  for (int64_t c = blockIdx.x; c < L.chunks; c += gridDim.x) {
+    const AdamTensor& T = L.t[chunk_tensor(L, c)];
+    const int64_t base = (c - T.c0) * kAdamChunk;
+    if (base + kAdamChunk <= T.n) {
+      floatx4 p[kAdamUnroll], g[kAdamUnroll], m[kAdamUnroll], v[kAdamUnroll];
+#pragma unroll
+      for (int k = 0; k < kAdamUnroll; ++k) {
+        const int64_t i = base + (k * kAdamThreads + threadIdx.x) * 4;
+        g[k] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(T.g + i));
+        m[k] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(T.m + i));
+        v[k] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(T.v + i));
+        p[k] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(T.p + i));
       }
-      *reinterpret_cast<floatx4*>(T.p + i) = p;
-      *reinterpret_cast<floatx4*>(T.m + i) = m;
-      *reinterpret_cast<floatx4*>(T.v + i) = v;
-      if (T.pb) *reinterpret_cast<u32x2*>(T.pb + i) = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+#pragma unroll
+      for (int k = 0; k < kAdamUnroll; ++k) {
+        four(p[k], g[k], m[k], v[k]);
+        const int64_t i = base + (k * kAdamThreads + threadIdx.x) * 4;
+        __builtin_nontemporal_store(p[k], reinterpret_cast<floatx4*>(T.p + i));
+        __builtin_nontemporal_store(m[k], reinterpret_cast<floatx4*>(T.m + i));
+        __builtin_nontemporal_store(v[k], reinterpret_cast<floatx4*>(T.v + i));
+        if (T.pb)
+          __builtin_nontemporal_store(
+              u32x2{pack_bf16x2(p[k][0], p[k][1]), pack_bf16x2(p[k][2], p[k][3])},
+              reinterpret_cast<u32x2*>(T.pb + i));
+      }
     } else {
-      for (int64_t j = i; j < T.n; ++j) {
-        float pe = T.p[j], me = T.m[j], ve = T.v[j];
-        one(pe, T.g[j], me, ve);
-        T.p[j] = pe;
-        T.m[j] = me;
-        T.v[j] = ve;
-        if (T.pb) T.pb[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(pe));
+#pragma unroll 1
+      for (int k = 0; k < kAdamUnroll; ++k) {
+        const int64_t i = base + (k * kAdamThreads + threadIdx.x) * 4;
+        if (i + 4 <= T.n) {
+          floatx4 p = *reinterpret_cast<const floatx4*>(T.p + i);
+          const floatx4 g = *reinterpret_cast<const floatx4*>(T.g + i);
+          floatx4 m = *reinterpret_cast<const floatx4*>(T.m + i);
+          floatx4 v = *reinterpret_cast<const floatx4*>(T.v + i);
+          four(p, g, m, v);
+          store4(T, i, p, m, v);
+        } else {
+          for (int64_t j = i; j < T.n; ++j) {
+            float pe = T.p[j], me = T.m[j], ve = T.v[j];
+            one(pe, T.g[j], me, ve);
+            T.p[j] = pe;
+            T.m[j] = me;
+            T.v[j] = ve;
+            if (T.pb) T.pb[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(pe));
+          }
+        }
       }
     }
   }

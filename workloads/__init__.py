@@ -135,3 +135,9 @@ LLAMA65B_LAYER = [
         ("gate", 8192, 22016), ("up", 8192, 22016), ("down", 22016, 8192),
     ])
 ]
+
+# Workload 6: the AdamW step over LLaMA-7B's LoRA factors on the four attention
+# projections at r = 64: 32 layers x 4 matrices x (A, B) = 256 tensors of
+# 64 x 4096, 67,108,864 parameters in all.
+ADAMW_TENSORS = 32 * 4 * 2
+ADAMW_TENSOR_SIZE = 64 * 4096
