@@ -8,8 +8,10 @@ transposed dequant-GEMM for dX, dA and dB), on resident synthetic inputs.
 other rows of the hot path: the fused NF4 + double-quant quantiser and the
 dequantiser (GB/s over the weight), and the few-token forward at 8192 -> 28672
 (GB/s over the weight it streams, M = 1..8, weight copies rotated past the
-256 MB Infinity Cache), and the 32-bit AdamW step with gradient clipping over
-the 67M LoRA parameters of LLaMA-7B's attention projections (GB/s).
+256 MB Infinity Cache), the 32-bit AdamW step with gradient clipping over
+the 67M LoRA parameters of LLaMA-7B's attention projections (GB/s), and the
+single-quantisation INT4 quantiser, decoder and error pass with the
+NF4-vs-INT4 error on the 11008 x 4096 weight.
 
 Prints ONE JSON line.  --gpus N > 1 is not supported (single-GPU build).
 """
@@ -278,6 +280,7 @@ def main():
         rows["few_token_fwd_8192x28672_r16"] = gemv
         del copies, Ag, Bg
         rows["adamw_step_llama7b_lora_r64"] = adamw_row(dev)
+        rows.update(variant_rows(W))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -346,6 +349,46 @@ def adamw_row(dev):
     nbytes = 34 * nparam
     return dict(tensors=n_t, params=nparam, ms=ms, GBps=nbytes / ms / 1e6,
                 hbm_frac=nbytes / ms / 1e6 / HBM_PEAK_GBS)
+
+
+def variant_rows(W):
+    """Single quantisation with either code on the 11008 x 4096 weight: the
+    INT4 quantiser (4 B read, 0.5 + 4/64 B written per weight), the single
+    decode (0.5 + 4/64 B read, 2 B written), the squared-error pass (4 + 0.5 +
+    4/64 B read), and the NF4-vs-INT4 mean squared error on that weight."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+
+    n = W.numel()
+    nb = (n + 63) // 64
+    qbytes = 4 * n + n // 2 + 4 * nb
+    dbytes = n // 2 + 4 * nb + 2 * n
+    ebytes = 4 * n + n // 2 + 4 * nb
+    rows, mse = {}, {}
+    out = torch.empty(n, dtype=torch.bfloat16, device=W.device)
+    ws = torch.empty(q.quant_error_workspace_size(n), dtype=torch.uint8, device=W.device)
+    sse = torch.empty(1, dtype=torch.float64, device=W.device)
+    for code in ("int4", "nf4"):
+        packed, absmax = q.quantize_4bit(W, code)
+        ms_e = _time_ms(lambda: q.quant_sq_error(W, packed, absmax, code, out=sse, workspace=ws),
+                        10)
+        mse[code] = float(sse.cpu()[0]) / n
+        if code == "int4":
+            ms_q = _time_ms(lambda: q.quantize_4bit(W, code), 10)
+            ms_d = _time_ms(lambda: q.dequantize_4bit(packed, absmax, n, code, out=out), 10)
+            rows["quantize_int4_single"] = dict(shape=list(W.shape), ms=ms_q,
+                                                GBps=qbytes / ms_q / 1e6,
+                                                hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS)
+            rows["dequantize_int4_single"] = dict(shape=list(W.shape), ms=ms_d,
+                                                  GBps=dbytes / ms_d / 1e6,
+                                                  hbm_frac=dbytes / ms_d / 1e6 / HBM_PEAK_GBS)
+            rows["quant_sq_error_int4"] = dict(shape=list(W.shape), ms=ms_e,
+                                               GBps=ebytes / ms_e / 1e6,
+                                               hbm_frac=ebytes / ms_e / 1e6 / HBM_PEAK_GBS)
+    rows["nf4_vs_int4_mse"] = dict(mse_nf4=mse["nf4"], mse_int4=mse["int4"],
+                                   improvement_pct=(1 - mse["nf4"] / mse["int4"]) * 100)
+    return rows
 
 
 def cpu_baseline(inp, wlc):

@@ -73,6 +73,10 @@ _SIGNATURES = {
     "qlora_adamw_step": ([ctypes.POINTER(AdamWTensor), _I32, _F, _F, _F, _F, _F, _I64, _F, _P, _P,
                           _SZ, _P], _I32),
     "qlora_adamw_workspace_size": ([_I32], _SZ),
+    "qlora_quantize_4bit": ([_P, _I64, _I32, _P, _P, _P], _I32),
+    "qlora_dequantize_4bit": ([_P, _P, _I64, _I32, _P, _P], _I32),
+    "qlora_quant_sq_error": ([_P, _I64, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
+    "qlora_quant_error_workspace_size": ([_I64], _SZ),
     "qlora_nf4_codebook": ([_P], None),
     "qlora_status_string": ([_I32], ctypes.c_char_p),
     "qlora_abi_version": ([], _I32),
@@ -200,6 +204,53 @@ def dequantize_nf4(wq, out=None):
     ws = wq.c_struct()
     _check(lib().qlora_dequantize_nf4(ctypes.byref(ws), _ptr(out), _stream(out.device)),
            "qlora_dequantize_nf4")
+    return out
+
+
+CODES = {"nf4": 0, "int4": 1}
+
+
+def _code(code):
+    if code not in CODES:
+        raise ValueError(f"code must be one of {sorted(CODES)}")
+    return CODES[code]
+
+
+def quantize_4bit(w, code="nf4"):
+    """Single quantisation with either code: (packed uint8, absmax float32)."""
+    n = w.numel()
+    nb = _nblocks(n)
+    packed = torch.empty(nb * 32, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(nb, dtype=torch.float32, device=w.device)
+    _check(lib().qlora_quantize_4bit(_ptr(w), n, _code(code), _ptr(packed), _ptr(absmax),
+                                     _stream(w.device)), "qlora_quantize_4bit")
+    return packed, absmax
+
+
+def dequantize_4bit(packed, absmax, n, code="nf4", out=None):
+    """bf16 [n] decoded from single-quantised storage."""
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=packed.device)
+    _check(lib().qlora_dequantize_4bit(_ptr(packed), _ptr(absmax), n, _code(code), _ptr(out),
+                                       _stream(out.device)), "qlora_dequantize_4bit")
+    return out
+
+
+def quant_error_workspace_size(n):
+    return lib().qlora_quant_error_workspace_size(n)
+
+
+def quant_sq_error(w, packed, absmax, code="nf4", out=None, workspace=None):
+    """float64 device tensor [1]: Σ (w − RN32(level·absmax))² over w."""
+    n = w.numel()
+    dev = w.device
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(quant_error_workspace_size(n), dtype=torch.uint8, device=dev)
+    _check(lib().qlora_quant_sq_error(_ptr(w), n, _code(code), _ptr(packed), _ptr(absmax),
+                                      _ptr(out), _ptr(workspace), workspace.numel(),
+                                      _stream(dev)), "qlora_quant_sq_error")
     return out
 
 

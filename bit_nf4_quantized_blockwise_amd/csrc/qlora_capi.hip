@@ -11,6 +11,7 @@
 
 #include "qlora_kernels.h"
 #include "qlora_optim.h"
+#include "qlora_quant_variants.h"
 
 using namespace qlora;
 
@@ -427,6 +428,95 @@ qlora_status qlora_quantize_nf4(const float* w, int64_t n, int32_t blocksize, ui
   QCHECK(ceil_div(threads, 256) <= 0x7fffffff, QLORA_ERR_SHAPE);
   hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0,
                      as_stream(stream), w, n, nb, packed, absmax);
+  return launched();
+}
+
+qlora_status qlora_quantize_4bit(const float* w, int64_t n, int32_t code, uint8_t* packed,
+                                 float* absmax, void* stream) {
+  QCHECK(n >= 0, QLORA_ERR_SHAPE);
+  QCHECK(code == QLORA_CODE_NF4 || code == QLORA_CODE_INT4, QLORA_ERR_UNSUPPORTED);
+  if (n == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(w);
+  ALIGNED_OR_NULL(packed);
+  ALIGNED_OR_NULL(absmax);
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  const int64_t nb = ceil_div(n, 64);
+  const int64_t grid = ceil_div(nb * 4, 256);
+  QCHECK(grid <= 0x7fffffff, QLORA_ERR_SHAPE);
+  if (code == QLORA_CODE_NF4)
+    hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
+                       w, n, nb, packed, absmax);
+  else
+    hipLaunchKernelGGL(quantize_int4_kernel, dim3((unsigned)grid), dim3(256), 0,
+                       as_stream(stream), w, n, nb, packed, absmax);
+  return launched();
+}
+
+qlora_status qlora_dequantize_4bit(const uint8_t* packed, const float* absmax, int64_t n,
+                                   int32_t code, qlora_bf16* out, void* stream) {
+  QCHECK(n >= 0, QLORA_ERR_SHAPE);
+  QCHECK(code == QLORA_CODE_NF4 || code == QLORA_CODE_INT4, QLORA_ERR_UNSUPPORTED);
+  if (n == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(packed);
+  ALIGNED_OR_NULL(absmax);
+  ALIGNED_OR_NULL(out);
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  const int64_t ndw = ceil_div(n, 8);
+  const dim3 grid(grid_for(ndw, 1024, 1 << 20));
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
+  if (code == QLORA_CODE_NF4)
+    hipLaunchKernelGGL(dequantize_4bit_kernel<kCodeNF4>, grid, dim3(256), 0, as_stream(stream), p,
+                       absmax, n, out);
+  else
+    hipLaunchKernelGGL(dequantize_4bit_kernel<kCodeINT4>, grid, dim3(256), 0, as_stream(stream),
+                       p, absmax, n, out);
+  return launched();
+}
+
+namespace {
+int64_t quant_error_wgs(int64_t n) {
+  return std::max<int64_t>(1, std::min<int64_t>(ceil_div(ceil_div(n, 8), 1024), kErrMaxWgs));
+}
+}  // namespace
+
+size_t qlora_quant_error_workspace_size(int64_t n) {
+  if (n < 0) return 0;
+  return std::max<size_t>(256, (size_t)quant_error_wgs(n) * sizeof(double));
+}
+
+qlora_status qlora_quant_sq_error(const float* w, int64_t n, int32_t code, const uint8_t* packed,
+                                  const float* absmax, double* sse, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  QCHECK(n >= 0, QLORA_ERR_SHAPE);
+  QCHECK(code == QLORA_CODE_NF4 || code == QLORA_CODE_INT4, QLORA_ERR_UNSUPPORTED);
+  QCHECK(sse != nullptr, QLORA_ERR_NULL);
+  QCHECK((reinterpret_cast<uintptr_t>(sse) & 7) == 0, QLORA_ERR_ALIGN);
+  if (n > 0) {
+    ALIGNED_OR_NULL(w);
+    ALIGNED_OR_NULL(packed);
+    ALIGNED_OR_NULL(absmax);
+  }
+  QCHECK(workspace != nullptr && aligned16(workspace) &&
+             ws_bytes >= qlora_quant_error_workspace_size(n),
+         QLORA_ERR_WORKSPACE);
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = as_stream(stream);
+  double* partials = static_cast<double*>(workspace);
+  int32_t npart = 0;
+  if (n > 0) {
+    npart = (int32_t)quant_error_wgs(n);
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
+    if (code == QLORA_CODE_NF4)
+      hipLaunchKernelGGL(quant_sq_error_kernel<kCodeNF4>, dim3(npart), dim3(256), 0, st, w, n, p,
+                         absmax, partials);
+    else
+      hipLaunchKernelGGL(quant_sq_error_kernel<kCodeINT4>, dim3(npart), dim3(256), 0, st, w, n, p,
+                         absmax, partials);
+  }
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(256), 0, st, partials, npart, sse);
   return launched();
 }
 

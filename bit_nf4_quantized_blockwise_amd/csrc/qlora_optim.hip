@@ -21,6 +21,7 @@
 // also forms the clipping coefficient), so the step is bitwise repeatable.
 
 #include "qlora_optim.h"
+#include "qlora_reduce.h"
 
 namespace qlora {
 
@@ -36,20 +37,6 @@ __device__ inline int chunk_tensor(const AdamList& L, int64_t c) {
     else hi = mid - 1;
   }
   return lo;
-}
-
-__device__ inline double block_sum(double v, double* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-#pragma unroll
-  for (int s = kAdamThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) sh[tid] += sh[tid + s];
-    __syncthreads();
-  }
-  const double r = sh[0];
-  __syncthreads();
-  return r;
 }
 
 __device__ inline double sq4(const floatx4& g) {
@@ -86,7 +73,7 @@ __global__ __launch_bounds__(kAdamThreads) void adam_sqnorm_kernel(AdamList L, d
       }
     }
   }
-  const double s = block_sum(acc, sh);
+  const double s = block_sum_f64<kAdamThreads>(acc, sh);
   if (threadIdx.x == 0) partials[blockIdx.x] = s;
 }
 
@@ -94,28 +81,8 @@ __global__ __launch_bounds__(kAdamThreads) void adam_clip_kernel(const double* p
                                                                  int32_t npart, float max_norm,
                                                                  int32_t clip, float* coef,
                                                                  float* norm_out) {
-  // Eight independent accumulators per lane keep eight loads in flight; the
-  // summation order depends on npart only.
-  constexpr int A = 8;
   __shared__ double sh[kAdamThreads];
-  double acc[A];
-#pragma unroll
-  for (int a = 0; a < A; ++a) acc[a] = 0.0;
-  int i = threadIdx.x;
-  for (; i + (A - 1) * kAdamThreads < npart; i += A * kAdamThreads) {
-    double x[A];
-#pragma unroll
-    for (int a = 0; a < A; ++a) x[a] = partials[i + a * kAdamThreads];
-#pragma unroll
-    for (int a = 0; a < A; ++a) acc[a] += x[a];
-  }
-#pragma unroll
-  for (int a = 0; a < A - 1; ++a)
-    if (i + a * kAdamThreads < npart) acc[a] += partials[i + a * kAdamThreads];
-  double t = 0.0;
-#pragma unroll
-  for (int a = 0; a < A; ++a) t += acc[a];
-  const double norm = sqrt(block_sum(t, sh));
+  const double norm = sqrt(workgroup_sum_f64<kAdamThreads>(partials, npart, sh));
   if (threadIdx.x == 0) {
     *coef = clip ? (float)fmin(1.0, (double)max_norm / (norm + 1e-6)) : 1.0f;
     if (norm_out) *norm_out = (float)norm;

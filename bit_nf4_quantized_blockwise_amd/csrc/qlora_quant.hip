@@ -14,28 +14,59 @@
 // w exceeds the real product exactly when it exceeds the largest float32 not
 // above it.  idx = #{i : w > T_i}, ties at a midpoint go to the lower index.
 //
+// The same exact-threshold quantiser serves the uniform INT4 comparison code
+// of the same page ("NF4による量子化と量子化誤差の比較": 16 evenly spaced
+// levels on [-1, 1], here each rounded once to float32), stored like NF4 with
+// a float32 absmax per block (single quantisation, 4 + 32/64 = 4.5 bits per
+// weight, §5-2 "メモリ削減の計算").  INT4 has no zero level: a zero weight
+// ties between ±1/15 and takes the lower index, 7, which is also the index of
+// an all-zero block.
+//
 // These kernels are HBM-bound: 4 B read + 0.5 B written per weight for the
 // quantiser, 0.52 B read + 2 B written per weight for the dequantiser.
 
 #include "qlora_kernels.h"
+#include "qlora_quant_variants.h"
+#include "qlora_reduce.h"
 
 namespace qlora {
 
 namespace {
 
+// RN32((2k − 15)/15), k = 0..15: the uniform INT4 levels, ascending.
+constexpr uint32_t kINT4Bits[16] = {
+    0xbf800000u, 0xbf5ddddeu, 0xbf3bbbbcu, 0xbf19999au, 0xbeeeeeefu, 0xbeaaaaabu,
+    0xbe4ccccdu, 0xbd888889u, 0x3d888889u, 0x3e4ccccdu, 0x3eaaaaabu, 0x3eeeeeefu,
+    0x3f19999au, 0x3f3bbbbcu, 0x3f5ddddeu, 0x3f800000u,
+};
+
+template <int CODE>
+struct Code;
+template <>
+struct Code<kCodeNF4> {
+  static constexpr const uint32_t* bits = kNF4Bits;
+  static constexpr uint32_t zero_word = 0x88888888u;  // eight codes of the zero level
+};
+template <>
+struct Code<kCodeINT4> {
+  static constexpr const uint32_t* bits = kINT4Bits;
+  static constexpr uint32_t zero_word = 0x77777777u;  // eight codes 7 (a zero weight's code)
+};
+
 struct Midpoints {
   double m[15];
 };
 
-constexpr Midpoints make_midpoints() {
+constexpr Midpoints make_midpoints(const uint32_t* bits) {
   Midpoints r{};
   for (int i = 0; i < 15; ++i)
-    r.m[i] = ((double)__builtin_bit_cast(float, kNF4Bits[i]) +
-              (double)__builtin_bit_cast(float, kNF4Bits[i + 1])) * 0.5;
+    r.m[i] = ((double)__builtin_bit_cast(float, bits[i]) +
+              (double)__builtin_bit_cast(float, bits[i + 1])) * 0.5;
   return r;
 }
 
-constexpr Midpoints kMid = make_midpoints();
+template <int CODE>
+constexpr Midpoints kMid = make_midpoints(Code<CODE>::bits);
 
 // RD32(m * a): the largest float32 not above the exact product.
 __device__ inline float rd32_mul(double m, float a) {
@@ -74,7 +105,8 @@ __device__ inline float dq_step(float gmax) {
 // j = floor((x + 1) · 32) spans [j/32 − 1, (j+1)/32 − 1); j = 64 is x = 1 (the
 // estimate never leaves [0, 64], so no clamp is needed).
 // kBucketMargin exceeds the error of the float32 quotient w · RN(1/a) by orders
-// of magnitude and, because consecutive midpoints are more than 0.088 apart,
+// of magnitude and, because consecutive midpoints are more than 0.088 apart
+// (NF4; 2/15 for INT4),
 // a bucket widened by the margin on both sides still holds at most one
 // midpoint.  first[j] = #{i : m_i < j/32 − 1 − margin}: the exact index is
 // first[j] or first[j] + 1, decided by one exact compare w > T_first[j].
@@ -86,24 +118,26 @@ struct BucketTable {
   uint8_t first[kNBuckets];
 };
 
-constexpr BucketTable make_buckets() {
+constexpr BucketTable make_buckets(const Midpoints& mid) {
   BucketTable t{};
   for (int j = 0; j < kNBuckets; ++j) {
     const double lo = j / 32.0 - 1.0 - kBucketMargin;
     int c = 0;
-    for (int i = 0; i < 15; ++i) c += (kMid.m[i] < lo) ? 1 : 0;
+    for (int i = 0; i < 15; ++i) c += (mid.m[i] < lo) ? 1 : 0;
     t.first[j] = (uint8_t)c;
   }
   return t;
 }
 
-constexpr BucketTable kBuckets = make_buckets();
+template <int CODE>
+constexpr BucketTable kBuckets = make_buckets(kMid<CODE>);
 
 constexpr int kTStride = 17;  // floats per block in the LDS threshold table (bank spread)
 
 // One lane handles 16 consecutive elements; 4 lanes form one 64-block.
 // T: this block's 16-entry threshold row in LDS (T[15] = +inf); bk: bucket table.
-// Block absmax (over the block's 4 lanes) and NF4 indices of 16 loaded values.
+// Block absmax (over the block's 4 lanes) and the codes of 16 loaded values.
+template <int CODE>
 __device__ inline float quantize_16v(const float (&v)[16], int sub, float* __restrict__ T,
                                      const uint8_t* __restrict__ bk, u32x2& out_bytes) {
   float m = 0.0f;
@@ -114,12 +148,12 @@ __device__ inline float quantize_16v(const float (&v)[16], int sub, float* __res
 
   // the 4 lanes of the block write its 15 thresholds (+ the +inf sentinel)
 #pragma unroll
-  for (int i = sub; i < 16; i += 4) T[i] = (i < 15) ? rd32_mul(kMid.m[i], m) : __builtin_inff();
+  for (int i = sub; i < 16; i += 4) T[i] = (i < 15) ? rd32_mul(kMid<CODE>.m[i], m) : __builtin_inff();
   // the block's 4 lanes share one wave, whose LDS accesses complete in order;
   // the barrier only keeps the compiler from moving the reads above the writes
   __builtin_amdgcn_wave_barrier();
 
-  uint32_t lo = 0x88888888u, hi = 0x88888888u;  // all-zero block: every index 8
+  uint32_t lo = Code<CODE>::zero_word, hi = Code<CODE>::zero_word;  // all-zero block
   if (m > 0.0f) {
     // the estimate only picks a bucket; a power-of-two rescale keeps 1/m finite
     // for subnormal block maxima without changing any ratio
@@ -167,34 +201,41 @@ __device__ inline void load_16(const float* __restrict__ w, int64_t n, int64_t b
   }
 }
 
-__device__ inline float quantize_16(const float* __restrict__ w, int64_t n, int64_t blk, int sub,
-                                    float* __restrict__ T, const uint8_t* __restrict__ bk,
-                                    u32x2& out_bytes) {
-  float v[16];
-  load_16(w, n, blk, sub, v);
-  return quantize_16v(v, sub, T, bk, out_bytes);
-}
-
-}  // namespace
-
 // packed[nblocks*32], absmax[nblocks]; 64 blocks per 256-thread workgroup.
-__global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ w, int64_t n,
-                                                           int64_t nblocks,
-                                                           uint8_t* __restrict__ packed,
-                                                           float* __restrict__ absmax) {
+template <int CODE>
+__device__ inline void quantize_blocks(const float* __restrict__ w, int64_t n, int64_t nblocks,
+                                       uint8_t* __restrict__ packed, float* __restrict__ absmax) {
   __shared__ float thr[64 * kTStride];
   __shared__ uint8_t bk[kNBuckets];
   const int t = threadIdx.x;
-  if (t < kNBuckets) bk[t] = kBuckets.first[t];
+  if (t < kNBuckets) bk[t] = kBuckets<CODE>.first[t];
   __syncthreads();
   const int64_t gt = (int64_t)blockIdx.x * 256 + t;
   const int64_t blk = gt >> 2;
   const int sub = (int)(gt & 3);
   if (blk >= nblocks) return;  // the 4 lanes of a block leave together
+  float v[16];
+  load_16(w, n, blk, sub, v);
   u32x2 bytes;
-  const float m = quantize_16(w, n, blk, sub, thr + (t >> 2) * kTStride, bk, bytes);
+  const float m = quantize_16v<CODE>(v, sub, thr + (t >> 2) * kTStride, bk, bytes);
   *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
   if (sub == 0) absmax[blk] = m;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ w, int64_t n,
+                                                           int64_t nblocks,
+                                                           uint8_t* __restrict__ packed,
+                                                           float* __restrict__ absmax) {
+  quantize_blocks<kCodeNF4>(w, n, nblocks, packed, absmax);
+}
+
+__global__ __launch_bounds__(256) void quantize_int4_kernel(const float* __restrict__ w, int64_t n,
+                                                            int64_t nblocks,
+                                                            uint8_t* __restrict__ packed,
+                                                            float* __restrict__ absmax) {
+  quantize_blocks<kCodeINT4>(w, n, nblocks, packed, absmax);
 }
 
 // One workgroup per group of 256 blocks.
@@ -230,7 +271,7 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
   __shared__ float thr[64 * kTStride];
   __shared__ uint8_t bk[kNBuckets];
   const int t = threadIdx.x;
-  if (t < kNBuckets) bk[t] = kBuckets.first[t];
+  if (t < kNBuckets) bk[t] = kBuckets<kCodeNF4>.first[t];
   __syncthreads();
   const int sub = t & 3;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
@@ -254,7 +295,7 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
       float m = 0.0f;
       if (blk < nblocks) {
         u32x2 bytes;
-        m = quantize_16v(cur, sub, thr + (t >> 2) * kTStride, bk, bytes);
+        m = quantize_16v<kCodeNF4>(cur, sub, thr + (t >> 2) * kTStride, bk, bytes);
         *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
       }
       if (sub == 0) amax[lb] = m;
@@ -310,5 +351,108 @@ __global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __r
     }
   }
 }
+
+// Single-quantisation decode of n weights (any n): ŵ = RNE_bf16(RN32(level · a)).
+// Lane layout as in dequantize_nf4_kernel; the last dword may be partial.
+template <int CODE>
+__global__ __launch_bounds__(256) void dequantize_4bit_kernel(const uint32_t* __restrict__ packed,
+                                                              const float* __restrict__ absmax,
+                                                              int64_t n,
+                                                              uint16_t* __restrict__ out) {
+  __shared__ float cb[16];
+  if (threadIdx.x < 16) cb[threadIdx.x] = bits_to_float(Code<CODE>::bits[threadIdx.x]);
+  __syncthreads();
+  const int64_t ndw = (n + 7) >> 3;
+  const int64_t stride = (int64_t)gridDim.x * 1024;
+  for (int64_t base = (int64_t)blockIdx.x * 1024; base < ndw; base += stride) {
+    uint32_t p[4];
+    float a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x + 256 * u;
+      p[u] = (i < ndw) ? packed[i] : 0u;
+      a[u] = (i < ndw) ? absmax[i >> 3] : 0.0f;  // 8 dwords per 64-block
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x + 256 * u;
+      if (i >= ndw) continue;
+      const u32x4 o = decode8(p[u], a[u], cb);
+      if (8 * i + 8 <= n) {
+        *reinterpret_cast<u32x4*>(out + 8 * i) = o;
+      } else {
+        for (int e = 0; 8 * i + e < n; ++e) out[8 * i + e] = (uint16_t)(o[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
+// Partial sums of (w − RN32(level_idx · a))², float64, one per workgroup.
+// Lane t takes dwords (8 weights) base + t + 256u, u = 0..3, like the decoder.
+template <int CODE>
+__global__ __launch_bounds__(256) void quant_sq_error_kernel(const float* __restrict__ w, int64_t n,
+                                                             const uint32_t* __restrict__ packed,
+                                                             const float* __restrict__ absmax,
+                                                             double* __restrict__ partials) {
+  __shared__ float cb[16];
+  __shared__ double sh[256];
+  if (threadIdx.x < 16) cb[threadIdx.x] = bits_to_float(Code<CODE>::bits[threadIdx.x]);
+  __syncthreads();
+  const int64_t ndw = (n + 7) >> 3;
+  const int64_t stride = (int64_t)gridDim.x * 1024;
+  double acc = 0.0;
+  for (int64_t base = (int64_t)blockIdx.x * 1024; base < ndw; base += stride) {
+    uint32_t p[4];
+    float a[4];
+    floatx4 x[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x + 256 * u;
+      const bool full = 8 * i + 8 <= n;
+      p[u] = (i < ndw) ? packed[i] : 0u;
+      a[u] = (i < ndw) ? absmax[i >> 3] : 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (full) {
+          x[u][h] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(w + 8 * i + 4 * h));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t j = 8 * i + 4 * h + e;
+            x[u][h][e] = (i < ndw && j < n) ? w[j] : 0.0f;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x + 256 * u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float r = cb[(p[u] >> (4 * e)) & 15u] * a[u];
+        const double d = (double)x[u][e >> 2][e & 3] - (double)r;
+        if (i < ndw && 8 * i + e < n) acc += d * d;
+      }
+    }
+  }
+  const double s = block_sum_f64<256>(acc, sh);
+  if (threadIdx.x == 0) partials[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void sum_partials_kernel(const double* __restrict__ partials,
+                                                           int32_t npart, double* __restrict__ out) {
+  __shared__ double sh[256];
+  const double s = workgroup_sum_f64<256>(partials, npart, sh);
+  if (threadIdx.x == 0) *out = s;
+}
+
+template __global__ void dequantize_4bit_kernel<kCodeNF4>(const uint32_t*, const float*, int64_t,
+                                                          uint16_t*);
+template __global__ void dequantize_4bit_kernel<kCodeINT4>(const uint32_t*, const float*, int64_t,
+                                                           uint16_t*);
+template __global__ void quant_sq_error_kernel<kCodeNF4>(const float*, int64_t, const uint32_t*,
+                                                         const float*, double*);
+template __global__ void quant_sq_error_kernel<kCodeINT4>(const float*, int64_t, const uint32_t*,
+                                                          const float*, double*);
 
 }  // namespace qlora

@@ -19,7 +19,7 @@
  *
  * Conventions (every entry point):
  *   * Pointers are DEVICE pointers unless marked (host).  Every device pointer
- *     must be 16-byte aligned.  The caller owns every buffer; the library never
+ *     must be 16-byte aligned (unless its entry point states otherwise).  The caller owns every buffer; the library never
  *     allocates, frees or keeps a pointer past the call.
  *   * `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously on it; no call synchronises.
@@ -108,6 +108,42 @@ qlora_status qlora_quantize_nf4_dq(const float *w, int64_t n, uint8_t *packed, i
  * out[n_out*k_in] bf16, row-major.  Any n_out, k_in >= 0 with n_out*k_in % 64 == 0. */
 qlora_status qlora_dequantize_nf4(const qlora_nf4_weight *w /* host struct */, qlora_bf16 *out,
                                   void *stream);
+
+/* ---- quantiser variants -------------------------------------------------- */
+
+#define QLORA_CODE_NF4 0   /* the 16 NormalFloat levels */
+#define QLORA_CODE_INT4 1  /* 16 uniform levels (2k − 15)/15, k = 0..15, each RN32 */
+
+/* First level with either code, one float32 absmax per block kept as is:
+ * single quantisation, 4 + 32/64 = 4.5 bits per weight ("QLoRAの理論と実装",
+ * §5-2 "メモリ削減の計算"; the uniform INT4 code is the page's comparison
+ * quantiser, "NF4による量子化と量子化誤差の比較", levels linspace(−1, 1, 16)).
+ * Blocks, absmax, exact nearest-level decision and packing as for
+ * qlora_quantize_nf4 (QLORA_CODE_NF4 gives the same bytes).  INT4 has no zero
+ * level: a zero weight ties between ∓1/15 and takes the lower index, 7, which
+ * is also the index of an all-zero block and of padded slots.
+ * Outputs packed[ceil(n/64)*32], absmax[ceil(n/64)].  n >= 0. */
+qlora_status qlora_quantize_4bit(const float *w, int64_t n, int32_t code, uint8_t *packed,
+                                 float *absmax, void *stream);
+
+/* Single-quantisation decode: out[i] = RNE_bf16(RN32(level[idx_i] · absmax[i/64]))
+ * for i < n (any n >= 0), levels of `code`.  packed and absmax as written by
+ * qlora_quantize_4bit for the same n. */
+qlora_status qlora_dequantize_4bit(const uint8_t *packed, const float *absmax, int64_t n,
+                                   int32_t code, qlora_bf16 *out, void *stream);
+
+/* Quantisation error of a single-quantised weight (the page's NF4-vs-INT4
+ * comparison measures its mean, "NF4による量子化と量子化誤差の比較"):
+ *   *sse = Σ_{i<n} (w[i] − RN32(level[idx_i] · absmax[i/64]))²
+ * each term formed in float64, summed in float64 in a fixed order (repeated
+ * calls give the same bits).  sse is one device double (8-byte aligned); n = 0
+ * writes 0.  workspace: at least qlora_quant_error_workspace_size(n) bytes. */
+qlora_status qlora_quant_sq_error(const float *w, int64_t n, int32_t code, const uint8_t *packed,
+                                  const float *absmax, double *sse, void *workspace,
+                                  size_t ws_bytes, void *stream);
+
+/* Bytes of workspace qlora_quant_sq_error needs for n weights (0 if n < 0). */
+size_t qlora_quant_error_workspace_size(int64_t n);
 
 /* ---- QLoRA linear ------------------------------------------------------- */
 

@@ -142,3 +142,28 @@ def test_adamw_argument_errors(L):
     assert L.qlora_adamw_workspace_size(-1) == 0
     assert L.qlora_adamw_workspace_size(0) >= 256
     assert L.qlora_adamw_workspace_size(200) >= 5 * 256 * 8
+
+
+def test_quantizer_variant_argument_errors(L):
+    f = L.qlora_quantize_4bit
+    assert f(FAKE, 100, 2, FAKE, FAKE, None) == UNSUP
+    assert f(FAKE, -1, 1, FAKE, FAKE, None) == SHAPE
+    assert f(None, 100, 1, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 100, 1, FAKE, MIS, None) == ALIGN
+    assert f(None, 0, 1, None, None, None) == OK
+    d = L.qlora_dequantize_4bit
+    assert d(FAKE, FAKE, 100, -1, FAKE, None) == UNSUP
+    assert d(FAKE, FAKE, -3, 0, FAKE, None) == SHAPE
+    assert d(FAKE, None, 100, 0, FAKE, None) == NULL
+    assert d(FAKE, FAKE, 100, 1, MIS, None) == ALIGN
+    assert d(None, None, 0, 1, None, None) == OK
+    e = L.qlora_quant_sq_error
+    ws = L.qlora_quant_error_workspace_size
+    assert ws(-1) == 0 and ws(0) >= 256 and ws(10 ** 9) >= 2048 * 8
+    assert e(FAKE, 100, 3, FAKE, FAKE, FAKE, FAKE, 4096, None) == UNSUP
+    assert e(FAKE, 100, 0, FAKE, FAKE, None, FAKE, 4096, None) == NULL
+    assert e(FAKE, 100, 0, FAKE, FAKE, FAKE + 4, FAKE, 4096, None) == ALIGN
+    assert e(FAKE, 100, 0, FAKE, FAKE, FAKE + 8, FAKE, 4096, None) != ALIGN  # 8 bytes suffice
+    assert e(FAKE, 100, 0, FAKE, FAKE, FAKE, None, 4096, None) == WS
+    assert e(FAKE, 100, 0, FAKE, FAKE, FAKE, FAKE, 8, None) == WS
+    assert e(MIS, 100, 0, FAKE, FAKE, FAKE, FAKE, 4096, None) == ALIGN
