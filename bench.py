@@ -11,7 +11,8 @@ dequantiser (GB/s over the weight), and the few-token forward at 8192 -> 28672
 256 MB Infinity Cache), the 32-bit AdamW step with gradient clipping over
 the 67M LoRA parameters of LLaMA-7B's attention projections (GB/s), and the
 single-quantisation INT4 quantiser, decoder and error pass with the
-NF4-vs-INT4 error on the 11008 x 4096 weight.
+NF4-vs-INT4 error on the 11008 x 4096 weight, and the training step with LoRA
+dropout (p = 0.05) on the adapter input.
 
 Prints ONE JSON line.  --gpus N > 1 is not supported (single-GPU build).
 """
@@ -112,6 +113,37 @@ def summarize_pmc(fetch_csv, write_csv, out_path):
     print(open(out_path).read())
 
 
+def summarize_stats(stats_csv, bench_log, out_path):
+    """Short text summary of a rocprofv3 --kernel-trace --stats run of this
+    script: per-kernel calls and durations, with the bench line it printed."""
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    line = [ln for ln in open(bench_log) if ln.startswith('{"metric"')][-1]
+    d = json.loads(line)
+    with open(out_path, "w") as fh:
+        fh.write("# rocprofv3 kernel statistics of bench.py (LLaMA-7B MLP QLoRA linear: 4096 "
+                 "tokens,\n# 4096 -> 11008, r = 64, alpha = 16, and the other rows of the "
+                 "bench line), one MI355X.\n")
+        fh.write("# commands (from /tmp, TMPDIR=/tmp):\n")
+        fh.write("#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
+                 "python3 <repo>/bench.py --no-cpu-baseline --steps 10 --warmup 2 > <log>\n")
+        fh.write("#   python3 <repo>/bench.py --summarize-stats <dir>/bench_kernel_stats.csv "
+                 "<log> <this file>\n")
+        fh.write(f"# bench line under the profiler: value = {d['value']:.1f} TFLOP/s, "
+                 f"ms_per_step = {d['ms_per_step']:.3f},\n")
+        fh.write(f"#   forward dequant-GEMM (events) = {d['roofline']['ms'] * 1e3:.1f} us\n\n")
+        fh.write(f"{'kernel':<80} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} "
+                 f"{'total_ms':>10}\n")
+        for r in rows:
+            fh.write(f"{r['Name'][:80]:<80} {int(r['Calls']):>6} "
+                     f"{float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:>10.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:>10.3f}\n")
+    print(open(out_path).read())
+
+
 def pmc_pass():
     """Short run for counter collection: the forward dequant-GEMM a few times
     and a device copy of CALIB_BYTES (the byte counters' calibration)."""
@@ -162,16 +194,21 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="time only the training step")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only run the forward dequant-GEMM and a calibration copy (counters)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "BENCH_LOG", "OUT_TXT"),
+                    help="write the kernel statistics summary of a rocprofv3 --stats run")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the build has no multi-GPU path "
@@ -227,7 +264,7 @@ def main():
     # dominant kernel: the forward dequant-GEMM (one launch: Y = X·Ŵᵀ + s·U·Bᵀ)
     gemm_flops = 2 * M * K * N + 2 * M * r * N
     ms_gemm = _time_ms(lambda: q.nf4_matmul_fwd(wq, X, U, B, alpha, workspace=ws_f, Y=Y),
-                       args.steps)
+                       args.steps, warmup=args.warmup)
     gemm_tflops = gemm_flops / (ms_gemm * 1e-3) / 1e12
     # the input-gradient GEMM, timed through the backward (reported for context)
     ms_bwd = _time_ms(lambda: q.linear_bwd(wq, X, dY, A, B, U, alpha, workspace=ws_b, dX=dX,
@@ -279,6 +316,21 @@ def main():
                                 hbm_frac=gbytes / ms / 1e6 / HBM_PEAK_GBS)
         rows["few_token_fwd_8192x28672_r16"] = gemv
         del copies, Ag, Bg
+        # the same training step with LoRA dropout p = 0.05 on the adapter input
+        Xdr = torch.empty_like(X)
+        ws_d = torch.empty(q.workspace_size(2, M, N, K, r), dtype=torch.uint8, device=dev)
+        it = [0]
+
+        def step_dropout():
+            it[0] += 1
+            q.linear_fwd_dropout(wq, X, A, B, alpha, 0.05, 1234, it[0], workspace=ws_f, Y=Y, U=U,
+                                 Xd=Xdr)
+            q.linear_bwd_dropout(wq, Xdr, dY, A, B, U, alpha, 0.05, 1234, it[0], workspace=ws_d,
+                                 dX=dX, dA=dA, dB=dB)
+        ms_dr = _time_ms(step_dropout, args.steps)
+        rows["train_step_lora_dropout_0.05"] = dict(ms=ms_dr, TFLOPs=flops / (ms_dr * 1e-3) / 1e12,
+                                                    overhead_vs_plain=ms_dr / ms_step - 1.0)
+        del Xdr, ws_d
         rows["adamw_step_llama7b_lora_r64"] = adamw_row(dev)
         rows.update(variant_rows(W))
 

@@ -58,6 +58,7 @@ _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
+_U64 = ctypes.c_uint64
 _W = ctypes.POINTER(NF4Weight)
 
 _SIGNATURES = {
@@ -73,6 +74,11 @@ _SIGNATURES = {
     "qlora_adamw_step": ([ctypes.POINTER(AdamWTensor), _I32, _F, _F, _F, _F, _F, _I64, _F, _P, _P,
                           _SZ, _P], _I32),
     "qlora_adamw_workspace_size": ([_I32], _SZ),
+    "qlora_lora_dropout": ([_P, _I64, _I64, _F, _U64, _U64, _P, _P], _I32),
+    "qlora_linear_fwd_dropout": ([_W, _P, _I64, _P, _P, _I32, _F, _F, _U64, _U64, _P, _P, _P, _P,
+                                  _SZ, _P], _I32),
+    "qlora_linear_bwd_dropout": ([_W, _P, _P, _I64, _P, _P, _I32, _F, _F, _U64, _U64, _P, _P, _P,
+                                  _P, _P, _SZ, _P], _I32),
     "qlora_quantize_4bit": ([_P, _I64, _I32, _P, _P, _P], _I32),
     "qlora_dequantize_4bit": ([_P, _P, _I64, _I32, _P, _P], _I32),
     "qlora_quant_sq_error": ([_P, _I64, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
@@ -310,6 +316,51 @@ def linear_bwd(wq, X, dY, A, B, U, alpha, workspace=None, dX=None, dA=None, dB=N
     _check(lib().qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r,
                                   alpha, _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
                                   ws.numel(), _stream(dev)), "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+# ---- LoRA dropout ---------------------------------------------------------------
+
+def lora_dropout(X, p, seed, offset, Xd=None):
+    """Xd = mask ⊙ X (bf16) for the dropout rate p and the (seed, offset) mask."""
+    M, K = X.shape
+    Xd = torch.empty_like(X) if Xd is None else Xd
+    _check(lib().qlora_lora_dropout(_ptr(X), M, K, p, seed, offset, _ptr(Xd), _stream(X.device)),
+           "qlora_lora_dropout")
+    return Xd
+
+
+def linear_fwd_dropout(wq, X, A, B, alpha, p, seed, offset, workspace=None, Y=None, U=None,
+                       Xd=None):
+    """(Y, U, Xd) with dropout on the adapter input: Xd = mask ⊙ X,
+    U = Xd·Aᵀ, Y = X·Ŵᵀ + (alpha/r)/(1 − p)·U·Bᵀ."""
+    M, r = X.shape[0], A.shape[0]
+    dev = X.device
+    Y = torch.empty(M, wq.n_out, dtype=torch.bfloat16, device=dev) if Y is None else Y
+    U = torch.empty(M, r, dtype=torch.bfloat16, device=dev) if U is None else U
+    Xd = torch.empty_like(X) if Xd is None else Xd
+    ws = _workspace(0, M, wq, r, dev) if workspace is None else workspace
+    st = wq.c_struct()
+    _check(lib().qlora_linear_fwd_dropout(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, alpha,
+                                          p, seed, offset, _ptr(Y), _ptr(U), _ptr(Xd), _ptr(ws),
+                                          ws.numel(), _stream(dev)), "qlora_linear_fwd_dropout")
+    return Y, U, Xd
+
+
+def linear_bwd_dropout(wq, Xd, dY, A, B, U, alpha, p, seed, offset, workspace=None, dX=None,
+                       dA=None, dB=None):
+    """(dX bf16, dA fp32, dB fp32) of the dropout forward (same p, seed, offset)."""
+    M, r = dY.shape[0], A.shape[0]
+    dev = dY.device
+    dX = torch.empty(M, wq.k_in, dtype=torch.bfloat16, device=dev) if dX is None else dX
+    dA = torch.empty(r, wq.k_in, dtype=torch.float32, device=dev) if dA is None else dA
+    dB = torch.empty(wq.n_out, r, dtype=torch.float32, device=dev) if dB is None else dB
+    ws = _workspace(2, M, wq, r, dev) if workspace is None else workspace
+    st = wq.c_struct()
+    _check(lib().qlora_linear_bwd_dropout(ctypes.byref(st), _ptr(Xd), _ptr(dY), M, _ptr(A), _ptr(B),
+                                          r, alpha, p, seed, offset, _ptr(U), _ptr(dX), _ptr(dA),
+                                          _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)),
+           "qlora_linear_bwd_dropout")
     return dX, dA, dB
 
 

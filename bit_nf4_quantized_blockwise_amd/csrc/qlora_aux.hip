@@ -136,4 +136,24 @@ __global__ __launch_bounds__(256) void pad_cols_kernel(const uint16_t* __restric
   }
 }
 
+// LoRA dropout of the adapter input: each lane takes blocks of 8 consecutive
+// elements (one generator block, one 16-byte load and store); a dropped
+// element becomes +0, a kept one is copied bit for bit.
+__global__ __launch_bounds__(256) void lora_dropout_kernel(const uint16_t* __restrict__ x,
+                                                           int64_t nblk, DropoutKey d,
+                                                           uint16_t* __restrict__ xd) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += stride) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + b);
+    const uint32_t keep = keep_bits8(d, (uint64_t)b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = ((keep >> (2 * e)) & 1u) ? 0x0000ffffu : 0u;
+      const uint32_t hi = ((keep >> (2 * e + 1)) & 1u) ? 0xffff0000u : 0u;
+      v[e] &= lo | hi;
+    }
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(xd) + b);
+  }
+}
+
 }  // namespace qlora

@@ -381,6 +381,206 @@ qlora_status matmul_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64
 
 float scale_of(float alpha, int32_t r) { return alpha / (float)r; }
 
+// Forward with the main product on X and the adapter on Xl (X itself, or its
+// dropout): U = Xl·Aᵀ, Y = X·Ŵᵀ + s·U·Bᵀ.
+qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* Xl,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float s,
+                             uint16_t* Y, uint16_t* U, char* ws, const FwdWs& L, hipStream_t st) {
+  // the few-token kernel can form U itself, from the same tokens it multiplies
+  if (X == Xl && gemv_forms_u(M, w->n_out, w->k_in, r))
+    return gemv_impl(w, X, M, U, B, r, s, Y, ws, st, A);
+  const bool pad = r % 8 != 0 && !use_gemv(M);
+  uint16_t* Up = pad ? reinterpret_cast<uint16_t*>(ws + L.pad_u) : nullptr;
+  qlora_status e = lora_down_impl(Xl, M, w->k_in, A, r, U, Up, L.rp, ws, L, st);
+  if (e != QLORA_OK) return e;
+  const uint16_t* bp = B;
+  if (pad) {
+    uint16_t* Bp = reinterpret_cast<uint16_t*>(ws + L.pad_b);
+    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(w->n_out * L.rp)), dim3(256), 0, st, B,
+                       (int64_t)r, w->n_out, (int64_t)r, L.rp, Bp, L.rp);
+    if ((e = launched()) != QLORA_OK) return e;
+    bp = Bp;
+  }
+  return matmul_fwd_impl(w, X, M, pad ? Up : U, pad ? L.rp : r, bp, pad ? L.rp : r, r, s, Y, ws,
+                         L, st);
+}
+
+// LoRA dropout key of rate p (false for p outside [0, 1)).
+bool dropout_key(float p, uint64_t seed, uint64_t offset, DropoutKey* k) {
+  if (!(p >= 0.0f && p < 1.0f)) return false;
+  k->seed = seed;
+  k->offset = offset;
+  k->thr = (uint32_t)std::floor((double)p * 4294967296.0);
+  return true;
+}
+
+// s' = s / (1 − p): the inverted-dropout factor folded into the adapter scale.
+float scale_with_dropout(float s, float p) { return (float)((double)s / (1.0 - (double)p)); }
+
+qlora_status run_dropout(const uint16_t* X, int64_t n, const DropoutKey& key, uint16_t* Xd,
+                         hipStream_t st) {
+  const int64_t nblk = n / 8;
+  hipLaunchKernelGGL(lora_dropout_kernel, dim3(grid_for(nblk, 256, 1 << 16)), dim3(256), 0, st,
+                     X, nblk, key, Xd);
+  return launched();
+}
+
+// Arguments of both backward entry points (X: the tokens dA multiplies).
+qlora_status validate_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY,
+                          int64_t M, const uint16_t* A, const uint16_t* B, int32_t r,
+                          const uint16_t* U, const uint16_t* dX, const float* dA, const float* dB) {
+  qlora_status s = validate_linear(w, M, r);
+  if (s != QLORA_OK) return s;
+  ALIGNED_OR_NULL(A);
+  ALIGNED_OR_NULL(B);
+  ALIGNED_OR_NULL(dA);
+  ALIGNED_OR_NULL(dB);
+  if (M > 0) {
+    ALIGNED_OR_NULL(X);
+    ALIGNED_OR_NULL(dY);
+    ALIGNED_OR_NULL(U);
+    ALIGNED_OR_NULL(dX);
+  }
+  return QLORA_OK;
+}
+
+// Workspace of the dropout backward: the plain backward's, then the masked
+// adapter term T [M][K] fp32.
+size_t bwd_dropout_ws(const BwdWs& L, int64_t M, int64_t K) {
+  return align256(L.total) + align256((size_t)M * K * 4);
+}
+
+// Backward; X is the input dA multiplies (the tokens, or their dropout).  With
+// drop, dX = dY·Ŵ + T where T = s·mask ⊙ (V·A) is formed first (fp32, in the
+// workspace after the plain backward's layout) and the dX GEMM starts its
+// accumulators from it.
+qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float sc,
+                             const DropoutKey* drop, const uint16_t* U, uint16_t* dX, float* dA,
+                             float* dB, char* ws, const BwdWs& L, hipStream_t st) {
+  const int64_t N = w->n_out, K = w->k_in;
+  qlora_status s = QLORA_OK;
+
+  if (M == 0) {  // no tokens: the adapter gradients are zero
+    s = run_reduce(nullptr, 0, 0, 0, 0, (int64_t)r, K, 0, 0.0f, ReduceOut{nullptr, dA, K, 0},
+                   kNoOut, st);
+    if (s != QLORA_OK) return s;
+    return run_reduce(nullptr, 0, 0, 0, 0, N, (int64_t)r, 0, 0.0f,
+                      ReduceOut{nullptr, dB, (int64_t)r, 0}, kNoOut, st);
+  }
+
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + L.bt);  // [r][N]
+  uint16_t* V = reinterpret_cast<uint16_t*>(ws + L.v);    // [M][rp]
+  uint16_t* Vt = reinterpret_cast<uint16_t*>(ws + L.vt);  // [r][Mp]
+  uint16_t* Ut = reinterpret_cast<uint16_t*>(ws + L.ut);  // [r][Mp]
+  uint16_t* At = reinterpret_cast<uint16_t*>(ws + L.at);  // [K][rp]
+  float* part = reinterpret_cast<float*>(ws + L.part);
+
+  // adapter factors in the layouts the GEMMs read
+  {
+    const TransposeJob jb{B, (int64_t)r, N, (int64_t)r, N, (int64_t)r, Bt, N};
+    const TransposeJob ju{U, (int64_t)r, M, (int64_t)r, L.Mp, (int64_t)r, Ut, L.Mp};
+    const TransposeJob ja{A, K, (int64_t)r, K, L.rp, K, At, L.rp};
+    const int64_t tiles = std::max({ceil_div(N, 64) * ceil_div(r, 64), ceil_div(L.Mp, 64) * ceil_div(r, 64),
+                                    ceil_div(L.rp, 64) * ceil_div(K, 64)});
+    hipLaunchKernelGGL(transpose_pad3_kernel, dim3((unsigned)std::min<int64_t>(tiles, 1024), 3),
+                       dim3(256), 0, st, jb, ju, ja);
+  }
+  if ((s = launched()) != QLORA_OK) return s;
+
+  // V = dY·B  -> V [M][rp] (zero-padded) and Vᵀ [r][Mp] (zero-padded), bf16
+  {
+    GemmArgs g{};
+    g.a = dY; g.lda = N; g.rows = M; g.cols = r; g.red = N;
+    g.b = Bt; g.ldb = N;
+    g.out_f32 = part;
+    g.ldo = (int64_t)L.pv.tiles_n * SK_NT;
+    g.part_stride = M * g.ldo;
+    if ((s = run_gemm<SK_MT, SK_NT, 4, 1, B_BF16_CR, false, O_F32>(g, L.pv, st)) != QLORA_OK)
+      return s;
+    if (L.rp == r && L.Mp == M) {  // no padding: V and Vᵀ from one pass over the partials
+      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, r, g.ldo, 1.0f,
+                          ReduceOut{V, nullptr, L.rp, 0}, ReduceOut{Vt, nullptr, L.Mp, 1}, st)) !=
+          QLORA_OK)
+        return s;
+    } else {
+      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, L.rp, g.ldo, 1.0f,
+                          ReduceOut{V, nullptr, L.rp, 0}, kNoOut, st)) != QLORA_OK)
+        return s;
+      // Vᵀ from the same partials: rows_pad = Mp pads the token axis with zeros
+      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, L.Mp, r, g.ldo, 1.0f,
+                          ReduceOut{Vt, nullptr, L.Mp, 1}, kNoOut, st)) != QLORA_OK)
+        return s;
+    }
+  }
+
+  // with dropout: T = s·mask ⊙ (V·A), [M][K] fp32 (mask and scale in the epilogue)
+  float* T = drop ? reinterpret_cast<float*>(ws + align256(L.total)) : nullptr;
+  if (drop) {
+    GemmArgs g{};
+    g.a = V; g.lda = L.rp; g.rows = M; g.cols = K; g.red = r;
+    g.b = A; g.ldb = K;
+    g.out_f32 = T; g.ldo = K; g.part_stride = M * K;
+    g.s = sc; g.drop = *drop;
+    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(
+             g, plan(M, K, r, TR_MT, TR_NT, false), st)) != QLORA_OK)
+      return s;
+  }
+
+  // dX = dY·Ŵ + s·V·A  (with dropout: dY·Ŵ + T)
+  {
+    GemmArgs g{};
+    g.a = dY; g.lda = N; g.rows = M; g.cols = K; g.red = N;
+    g.packed = w->packed; g.qabsmax = w->qabsmax; g.c2 = w->c2; g.w_kin = K;
+    g.pl = V; g.ldpl = L.rp; g.pr = At; g.ldpr = L.rp; g.rl = r; g.s = sc;
+    g.s_split = needs_split(sc);
+    if (drop) {
+      g.c_init = T; g.ldc = K; g.rl = 0;
+    }
+    if (use_big(M)) {
+      g.out_bf16 = dX; g.ldo = K;
+      s = run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_RED, true, O_BF16, A_DMA>(
+          g, plan(M, K, N, BIG_MT, BIG_NT, false), st);
+      if (s != QLORA_OK) return s;
+    } else {
+      g.out_f32 = part; g.ldo = K; g.part_stride = M * K;
+      if ((s = run_gemm<SM_MT, SM_NT, 1, 4, B_NF4_RED, true, O_F32>(g, L.pdx, st)) != QLORA_OK)
+        return s;
+      if ((s = run_reduce(part, g.part_stride, L.pdx.nsplit, M, K, M, K, K, 1.0f,
+                          ReduceOut{dX, nullptr, K, 0}, kNoOut, st)) != QLORA_OK)
+        return s;
+    }
+  }
+
+  // dA = s·Vᵀ·X   [r][K]
+  {
+    GemmArgs g{};
+    g.a = Vt; g.lda = L.Mp; g.rows = r; g.cols = K; g.red = M;
+    g.b = X; g.ldb = K;
+    g.out_f32 = part; g.ldo = K; g.part_stride = (int64_t)r * K;
+    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pda, st)) != QLORA_OK)
+      return s;
+    if ((s = run_reduce(part, g.part_stride, L.pda.nsplit, r, K, r, K, K, sc,
+                        ReduceOut{nullptr, dA, K, 0}, kNoOut, st)) != QLORA_OK)
+      return s;
+  }
+
+  // dB = s·dYᵀ·U  computed as (s·Uᵀ·dY)ᵀ: rows j, cols n, written transposed into [N][r]
+  {
+    GemmArgs g{};
+    g.a = Ut; g.lda = L.Mp; g.rows = r; g.cols = N; g.red = M;
+    g.b = dY; g.ldb = N;
+    g.out_f32 = part; g.ldo = N; g.part_stride = (int64_t)r * N;
+    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pdb, st)) != QLORA_OK)
+      return s;
+    if ((s = run_reduce(part, g.part_stride, L.pdb.nsplit, r, N, r, N, N, sc,
+                        ReduceOut{nullptr, dB, (int64_t)r, 1}, kNoOut, st)) != QLORA_OK)
+      return s;
+  }
+  return QLORA_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -410,6 +610,7 @@ size_t qlora_workspace_size(int32_t op, int64_t M, int64_t n_out, int64_t k_in, 
   if (M < 0 || n_out <= 0 || k_in <= 0 || r < 1 || r > QLORA_MAX_RANK) return 0;
   if (op == 0) return fwd_ws(M, n_out, k_in, r).total;
   if (op == 1) return bwd_ws(M, n_out, k_in, r).total;
+  if (op == 2) return bwd_dropout_ws(bwd_ws(M, n_out, k_in, r), M, k_in);
   return 0;
 }
 
@@ -647,152 +848,82 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const qlora_bf16* X, in
   QCHECK(workspace != nullptr && aligned16(workspace) && ws_bytes >= L.total, QLORA_ERR_WORKSPACE);
   s = check_device();
   if (s != QLORA_OK) return s;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t st = as_stream(stream);
-  if (gemv_forms_u(M, w->n_out, w->k_in, r))  // U formed and stored by the few-token kernel
-    return gemv_impl(w, X, M, U, B, r, scale_of(alpha, r), Y, ws, st, A);
-  const bool pad = r % 8 != 0 && !use_gemv(M);
-  uint16_t* Up = pad ? reinterpret_cast<uint16_t*>(ws + L.pad_u) : nullptr;
-  s = lora_down_impl(X, M, w->k_in, A, r, U, Up, L.rp, ws, L, st);
+  return linear_fwd_impl(w, X, X, M, A, B, r, scale_of(alpha, r), Y, U,
+                         static_cast<char*>(workspace), L, as_stream(stream));
+}
+
+qlora_status qlora_lora_dropout(const qlora_bf16* X, int64_t M, int64_t k_in, float p,
+                                uint64_t seed, uint64_t offset, qlora_bf16* Xd, void* stream) {
+  QCHECK(M >= 0 && k_in >= 0 && k_in % 8 == 0, QLORA_ERR_SHAPE);
+  DropoutKey key;
+  QCHECK(dropout_key(p, seed, offset, &key), QLORA_ERR_UNSUPPORTED);
+  if (M == 0 || k_in == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(X);
+  ALIGNED_OR_NULL(Xd);
+  qlora_status s = check_device();
   if (s != QLORA_OK) return s;
-  const uint16_t* bp = B;
-  if (pad) {
-    uint16_t* Bp = reinterpret_cast<uint16_t*>(ws + L.pad_b);
-    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(w->n_out * L.rp)), dim3(256), 0, st, B,
-                       (int64_t)r, w->n_out, (int64_t)r, L.rp, Bp, L.rp);
-    if ((s = launched()) != QLORA_OK) return s;
-    bp = Bp;
-  }
-  return matmul_fwd_impl(w, X, M, pad ? Up : U, pad ? L.rp : r, bp, pad ? L.rp : r, r,
-                         scale_of(alpha, r), Y, ws, L, st);
+  return run_dropout(X, M * k_in, key, Xd, as_stream(stream));
+}
+
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const qlora_bf16* X, int64_t M,
+                                      const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                      float alpha, float p, uint64_t seed, uint64_t offset,
+                                      qlora_bf16* Y, qlora_bf16* U, qlora_bf16* Xd,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+  qlora_status s = validate_linear(w, M, r);
+  if (s != QLORA_OK) return s;
+  DropoutKey key;
+  QCHECK(dropout_key(p, seed, offset, &key), QLORA_ERR_UNSUPPORTED);
+  if (M == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(X);
+  ALIGNED_OR_NULL(A);
+  ALIGNED_OR_NULL(B);
+  ALIGNED_OR_NULL(Y);
+  ALIGNED_OR_NULL(U);
+  ALIGNED_OR_NULL(Xd);
+  const FwdWs L = fwd_ws(M, w->n_out, w->k_in, r);
+  QCHECK(workspace != nullptr && aligned16(workspace) && ws_bytes >= L.total, QLORA_ERR_WORKSPACE);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = as_stream(stream);
+  if ((s = run_dropout(X, M * w->k_in, key, Xd, st)) != QLORA_OK) return s;
+  return linear_fwd_impl(w, X, Xd, M, A, B, r, scale_with_dropout(scale_of(alpha, r), p), Y, U,
+                         static_cast<char*>(workspace), L, st);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const qlora_bf16* X, const qlora_bf16* dY,
                               int64_t M, const qlora_bf16* A, const qlora_bf16* B, int32_t r,
                               float alpha, const qlora_bf16* U, qlora_bf16* dX, float* dA,
                               float* dB, void* workspace, size_t ws_bytes, void* stream) {
-  qlora_status s = validate_linear(w, M, r);
+  qlora_status s = validate_bwd(w, X, dY, M, A, B, r, U, dX, dA, dB);
   if (s != QLORA_OK) return s;
-  ALIGNED_OR_NULL(A);
-  ALIGNED_OR_NULL(B);
-  ALIGNED_OR_NULL(dA);
-  ALIGNED_OR_NULL(dB);
-  if (M > 0) {
-    ALIGNED_OR_NULL(X);
-    ALIGNED_OR_NULL(dY);
-    ALIGNED_OR_NULL(U);
-    ALIGNED_OR_NULL(dX);
-  }
-  const int64_t N = w->n_out, K = w->k_in;
-  const BwdWs L = bwd_ws(M, N, K, r);
+  const BwdWs L = bwd_ws(M, w->n_out, w->k_in, r);
   QCHECK(workspace != nullptr && aligned16(workspace) && ws_bytes >= L.total, QLORA_ERR_WORKSPACE);
   s = check_device();
   if (s != QLORA_OK) return s;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t st = as_stream(stream);
-  const float sc = scale_of(alpha, r);
+  return linear_bwd_impl(w, X, dY, M, A, B, r, scale_of(alpha, r), nullptr, U, dX, dA, dB,
+                         static_cast<char*>(workspace), L, as_stream(stream));
+}
 
-  if (M == 0) {  // no tokens: the adapter gradients are zero
-    s = run_reduce(nullptr, 0, 0, 0, 0, (int64_t)r, K, 0, 0.0f, ReduceOut{nullptr, dA, K, 0},
-                   kNoOut, st);
-    if (s != QLORA_OK) return s;
-    return run_reduce(nullptr, 0, 0, 0, 0, N, (int64_t)r, 0, 0.0f,
-                      ReduceOut{nullptr, dB, (int64_t)r, 0}, kNoOut, st);
-  }
-
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + L.bt);  // [r][N]
-  uint16_t* V = reinterpret_cast<uint16_t*>(ws + L.v);    // [M][rp]
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(ws + L.vt);  // [r][Mp]
-  uint16_t* Ut = reinterpret_cast<uint16_t*>(ws + L.ut);  // [r][Mp]
-  uint16_t* At = reinterpret_cast<uint16_t*>(ws + L.at);  // [K][rp]
-  float* part = reinterpret_cast<float*>(ws + L.part);
-
-  // adapter factors in the layouts the GEMMs read
-  {
-    const TransposeJob jb{B, (int64_t)r, N, (int64_t)r, N, (int64_t)r, Bt, N};
-    const TransposeJob ju{U, (int64_t)r, M, (int64_t)r, L.Mp, (int64_t)r, Ut, L.Mp};
-    const TransposeJob ja{A, K, (int64_t)r, K, L.rp, K, At, L.rp};
-    const int64_t tiles = std::max({ceil_div(N, 64) * ceil_div(r, 64), ceil_div(L.Mp, 64) * ceil_div(r, 64),
-                                    ceil_div(L.rp, 64) * ceil_div(K, 64)});
-    hipLaunchKernelGGL(transpose_pad3_kernel, dim3((unsigned)std::min<int64_t>(tiles, 1024), 3),
-                       dim3(256), 0, st, jb, ju, ja);
-  }
-  if ((s = launched()) != QLORA_OK) return s;
-
-  // V = dY·B  -> V [M][rp] (zero-padded) and Vᵀ [r][Mp] (zero-padded), bf16
-  {
-    GemmArgs g{};
-    g.a = dY; g.lda = N; g.rows = M; g.cols = r; g.red = N;
-    g.b = Bt; g.ldb = N;
-    g.out_f32 = part;
-    g.ldo = (int64_t)L.pv.tiles_n * SK_NT;
-    g.part_stride = M * g.ldo;
-    if ((s = run_gemm<SK_MT, SK_NT, 4, 1, B_BF16_CR, false, O_F32>(g, L.pv, st)) != QLORA_OK)
-      return s;
-    if (L.rp == r && L.Mp == M) {  // no padding: V and Vᵀ from one pass over the partials
-      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, r, g.ldo, 1.0f,
-                          ReduceOut{V, nullptr, L.rp, 0}, ReduceOut{Vt, nullptr, L.Mp, 1}, st)) !=
-          QLORA_OK)
-        return s;
-    } else {
-      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, L.rp, g.ldo, 1.0f,
-                          ReduceOut{V, nullptr, L.rp, 0}, kNoOut, st)) != QLORA_OK)
-        return s;
-      // Vᵀ from the same partials: rows_pad = Mp pads the token axis with zeros
-      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, L.Mp, r, g.ldo, 1.0f,
-                          ReduceOut{Vt, nullptr, L.Mp, 1}, kNoOut, st)) != QLORA_OK)
-        return s;
-    }
-  }
-
-  // dX = dY·Ŵ + s·V·A
-  {
-    GemmArgs g{};
-    g.a = dY; g.lda = N; g.rows = M; g.cols = K; g.red = N;
-    g.packed = w->packed; g.qabsmax = w->qabsmax; g.c2 = w->c2; g.w_kin = K;
-    g.pl = V; g.ldpl = L.rp; g.pr = At; g.ldpr = L.rp; g.rl = r; g.s = sc;
-    g.s_split = needs_split(sc);
-    if (use_big(M)) {
-      g.out_bf16 = dX; g.ldo = K;
-      s = run_gemm<BIG_MT, BIG_NT, 2, 2, B_NF4_RED, true, O_BF16, A_DMA>(
-          g, plan(M, K, N, BIG_MT, BIG_NT, false), st);
-      if (s != QLORA_OK) return s;
-    } else {
-      g.out_f32 = part; g.ldo = K; g.part_stride = M * K;
-      if ((s = run_gemm<SM_MT, SM_NT, 1, 4, B_NF4_RED, true, O_F32>(g, L.pdx, st)) != QLORA_OK)
-        return s;
-      if ((s = run_reduce(part, g.part_stride, L.pdx.nsplit, M, K, M, K, K, 1.0f,
-                          ReduceOut{dX, nullptr, K, 0}, kNoOut, st)) != QLORA_OK)
-        return s;
-    }
-  }
-
-  // dA = s·Vᵀ·X   [r][K]
-  {
-    GemmArgs g{};
-    g.a = Vt; g.lda = L.Mp; g.rows = r; g.cols = K; g.red = M;
-    g.b = X; g.ldb = K;
-    g.out_f32 = part; g.ldo = K; g.part_stride = (int64_t)r * K;
-    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pda, st)) != QLORA_OK)
-      return s;
-    if ((s = run_reduce(part, g.part_stride, L.pda.nsplit, r, K, r, K, K, sc,
-                        ReduceOut{nullptr, dA, K, 0}, kNoOut, st)) != QLORA_OK)
-      return s;
-  }
-
-  // dB = s·dYᵀ·U  computed as (s·Uᵀ·dY)ᵀ: rows j, cols n, written transposed into [N][r]
-  {
-    GemmArgs g{};
-    g.a = Ut; g.lda = L.Mp; g.rows = r; g.cols = N; g.red = M;
-    g.b = dY; g.ldb = N;
-    g.out_f32 = part; g.ldo = N; g.part_stride = (int64_t)r * N;
-    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pdb, st)) != QLORA_OK)
-      return s;
-    if ((s = run_reduce(part, g.part_stride, L.pdb.nsplit, r, N, r, N, N, sc,
-                        ReduceOut{nullptr, dB, (int64_t)r, 1}, kNoOut, st)) != QLORA_OK)
-      return s;
-  }
-  return QLORA_OK;
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const qlora_bf16* Xd,
+                                      const qlora_bf16* dY, int64_t M, const qlora_bf16* A,
+                                      const qlora_bf16* B, int32_t r, float alpha, float p,
+                                      uint64_t seed, uint64_t offset, const qlora_bf16* U,
+                                      qlora_bf16* dX, float* dA, float* dB, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  qlora_status s = validate_bwd(w, Xd, dY, M, A, B, r, U, dX, dA, dB);
+  if (s != QLORA_OK) return s;
+  DropoutKey key;
+  QCHECK(dropout_key(p, seed, offset, &key), QLORA_ERR_UNSUPPORTED);
+  const BwdWs L = bwd_ws(M, w->n_out, w->k_in, r);
+  QCHECK(workspace != nullptr && aligned16(workspace) &&
+             ws_bytes >= bwd_dropout_ws(L, M, w->k_in),
+         QLORA_ERR_WORKSPACE);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  return linear_bwd_impl(w, Xd, dY, M, A, B, r, scale_with_dropout(scale_of(alpha, r), p),
+                         key.thr > 0 ? &key : nullptr, U, dX, dA, dB,
+                         static_cast<char*>(workspace), L, as_stream(stream));
 }
 
 // AdamW workspace: the clipping coefficient (float) at byte 0, the norm

@@ -582,6 +582,40 @@ struct Mma {
 
 }  // namespace
 
+namespace {
+
+// Accumulators from a float32 tile (accumulator layout: see mfma_t); rows
+// past the end start at zero.
+template <int FM, int FN>
+__device__ inline void load_acc(floatx16 (&acc)[FM][FN], const GemmArgs& g, int64_t wrow0,
+                                int64_t wcol0, int lane) {
+  const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t row = wrow0 + i * 32 + lr;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = wcol0 + j * 32 + 8 * q + 4 * lh;
+        floatx4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (row < g.rows && col < g.cols)
+          v = *reinterpret_cast<const floatx4*>(g.c_init + row * g.ldc + col);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[i][j][4 * q + c] = v[c];
+      }
+  }
+}
+
+// Keep bits of the run of four columns col..col+3 of a row (col % 4 == 0, so
+// the run lies inside one 8-element generator block).
+__device__ inline uint32_t keep_bits4(const GemmArgs& g, int64_t row, int64_t col) {
+  const int64_t f = row * g.cols + col;
+  return keep_bits8(g.drop, (uint64_t)f >> 3) >> (f & 7);
+}
+
+}  // namespace
+
 template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE, int AMODE>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   static_assert(WM * WN == 4, "4 waves");
@@ -636,7 +670,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   if constexpr (PROLOGUE) {
     // acc = s · L·Rᵀ over the rank dimension, L through registers (scaled by s
     // there: two bf16 parts when s·L is not exact in one), R through LDS.
-    if (blockIdx.y == 0 && g.rl > 0) {
+    if (blockIdx.y == 0 && g.c_init != nullptr) {
+      load_acc<FM, FN>(mma.acc, g, wrow0, col0 + wn * WTN, lane);
+    } else if (blockIdx.y == 0 && g.rl > 0) {
       ARegs<FM> la;
       RowTile<NT> rt;
       la.init(g.pl, g.ldpl, g.rows, wrow0, lane);
@@ -883,8 +919,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const floatx16& c = mma.acc[i][j];
-            *reinterpret_cast<floatx4*>(o + 32 * j + 8 * q) =
-                floatx4{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+            floatx4 v{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+            if (g.drop.thr > 0) {
+              const uint32_t keep = keep_bits4(g, row, wcol0 + 32 * j + 8 * q + 4 * lh);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = ((keep >> e) & 1u) ? g.s * v[e] : 0.0f;
+            }
+            *reinterpret_cast<floatx4*>(o + 32 * j + 8 * q) = v;
           }
       }
     }
@@ -900,10 +941,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       for (int e = 0; e < 16; ++e) {
         const int64_t col = wcol0 + j * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
         if (col >= g.cols) continue;
-        const float v = mma.acc[i][j][e];
+        float v = mma.acc[i][j][e];
         if constexpr (OMODE == O_BF16) {
           g.out_bf16[row * g.ldo + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
         } else {
+          if (g.drop.thr > 0)
+            v = ((keep_bits4(g, row, col & ~(int64_t)3) >> (col & 3)) & 1u) ? g.s * v : 0.0f;
           g.out_f32[(int64_t)blockIdx.y * g.part_stride + row * g.ldo + col] = v;
         }
       }

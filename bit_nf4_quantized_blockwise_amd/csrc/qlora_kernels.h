@@ -3,6 +3,7 @@
 #pragma once
 
 #include "qlora_common.h"
+#include "qlora_philox.h"
 
 namespace qlora {
 
@@ -28,6 +29,10 @@ struct GemmArgs {
   int32_t rl;
   float s;
   int32_t s_split;     // 1: stage s·L as two bf16 parts (s·L not exact in bf16)
+  DropoutKey drop;     // O_F32 with drop.thr > 0: the epilogue writes s·acc where the
+                       // LoRA-dropout mask at index row·cols + col keeps, 0 where it drops
+  const float* c_init;  // prologue modes: acc starts from c_init[rows][ldc] (split 0)
+  int64_t ldc;          // instead of s·L·Rᵀ (fp32, ldc % 4 == 0, cols % 4 == 0)
   uint16_t* out_bf16;  // O_BF16: [rows][ldo]
   float* out_f32;      // O_F32: [split][rows][ldo] partial sums
   int64_t ldo;
@@ -77,6 +82,8 @@ constexpr int kGemvWaves = 8;   // waves per few-token GEMV workgroup (they spli
 template <int CPW, int MG, int G, bool QV>
 __global__ void nf4_gemv_kernel(GemvArgs g);
 
+// xd = mask ⊙ x over n / 8 blocks of 8 bf16 (LoRA dropout, see qlora_philox.h).
+__global__ void lora_dropout_kernel(const uint16_t* x, int64_t nblk, DropoutKey d, uint16_t* xd);
 __global__ void lora_down_small_kernel(const uint16_t* x, int M, int64_t K, const uint16_t* a,
                                        int r, uint16_t* u);
 

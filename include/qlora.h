@@ -109,6 +109,42 @@ qlora_status qlora_quantize_nf4_dq(const float *w, int64_t n, uint8_t *packed, i
 qlora_status qlora_dequantize_nf4(const qlora_nf4_weight *w /* host struct */, qlora_bf16 *out,
                                   void *stream);
 
+/* ---- LoRA dropout -------------------------------------------------------- */
+
+/* The training example's lora_dropout ("QLoRAの理論と実装", LoraConfig: 0.05)
+ * as inverted dropout on the adapter's input: the adapter sees
+ * X̃ = mask ⊙ X / (1 − p), the frozen path sees X.  The mask is a pure
+ * function of (seed, offset, element): element f = token·k_in + k draws the
+ * 32-bit value f & 7 of Philox4x64-10 block f >> 3 (key (seed, 0), counter
+ * (f >> 3, offset, 0, 0); word (f & 7) >> 1, low half for even f) and is
+ * dropped when that value is below floor(p · 2^32).  p must lie in [0, 1)
+ * (else QLORA_ERR_UNSUPPORTED).  With s' = RN32(α/r) / (1 − p):
+ *
+ * qlora_lora_dropout:        Xd = mask ⊙ X (bf16, bit copies and +0), X and Xd
+ *                            [M][k_in], k_in % 8 == 0.
+ * qlora_linear_fwd_dropout:  Xd as above, U = Xd·Aᵀ (saved), Y = RNE_bf16(X·Ŵᵀ +
+ *                            s'·U·Bᵀ).  Workspace: qlora_workspace_size(0, ...).
+ * qlora_linear_bwd_dropout:  V = dY·B;  dX = RNE_bf16(dY·Ŵ + s'·mask ⊙ (V·A));
+ *                            dA = s'·Vᵀ·Xd;  dB = s'·dYᵀ·U, with the same
+ *                            (p, seed, offset) as the forward (the mask is
+ *                            regenerated, not stored).  Workspace:
+ *                            qlora_workspace_size(2, ...).
+ * Shapes, dtypes and layouts otherwise as qlora_linear_fwd / qlora_linear_bwd. */
+qlora_status qlora_lora_dropout(const qlora_bf16 *X, int64_t M, int64_t k_in, float p,
+                                uint64_t seed, uint64_t offset, qlora_bf16 *Xd, void *stream);
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight *w /* host struct */,
+                                      const qlora_bf16 *X, int64_t M, const qlora_bf16 *A,
+                                      const qlora_bf16 *B, int32_t r, float alpha, float p,
+                                      uint64_t seed, uint64_t offset, qlora_bf16 *Y,
+                                      qlora_bf16 *U, qlora_bf16 *Xd, void *workspace,
+                                      size_t ws_bytes, void *stream);
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight *w /* host struct */,
+                                      const qlora_bf16 *Xd, const qlora_bf16 *dY, int64_t M,
+                                      const qlora_bf16 *A, const qlora_bf16 *B, int32_t r,
+                                      float alpha, float p, uint64_t seed, uint64_t offset,
+                                      const qlora_bf16 *U, qlora_bf16 *dX, float *dA, float *dB,
+                                      void *workspace, size_t ws_bytes, void *stream);
+
 /* ---- quantiser variants -------------------------------------------------- */
 
 #define QLORA_CODE_NF4 0   /* the 16 NormalFloat levels */
@@ -222,8 +258,9 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor *tensors /* host array */
 /* Bytes of workspace qlora_adamw_step needs for `count` tensors (0 if count < 0). */
 size_t qlora_adamw_workspace_size(int32_t count);
 
-/* Bytes of device workspace needed by op 0 (forward, also qlora_lora_down and
- * qlora_nf4_matmul_fwd) or op 1 (backward).  Returns 0 for an invalid op. */
+/* Bytes of device workspace needed by op 0 (forward, also qlora_lora_down,
+ * qlora_nf4_matmul_fwd and qlora_linear_fwd_dropout), op 1 (backward) or op 2
+ * (qlora_linear_bwd_dropout).  Returns 0 for an invalid op. */
 size_t qlora_workspace_size(int32_t op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);
 
 /* (host) The 16 float32 NF4 levels the kernels use, ascending. */

@@ -48,7 +48,9 @@ def test_codebook_matches_oracle_bitwise(L):
 def test_workspace_size(L):
     assert q.workspace_size(0, 4096, 11008, 4096, 64) > 0
     assert q.workspace_size(1, 4096, 11008, 4096, 64) > 0
-    assert q.workspace_size(2, 16, 64, 64, 8) == 0
+    assert q.workspace_size(3, 16, 64, 64, 8) == 0
+    assert q.workspace_size(2, 4096, 11008, 4096, 64) >= \
+        q.workspace_size(1, 4096, 11008, 4096, 64) + 4096 * 4096 * 4
     assert q.workspace_size(0, 16, 64, 64, 0) == 0
     assert q.workspace_size(0, 16, 64, 64, 257) == 0
     assert q.workspace_size(0, 0, 64, 64, 8) >= 256
@@ -167,3 +169,28 @@ def test_quantizer_variant_argument_errors(L):
     assert e(FAKE, 100, 0, FAKE, FAKE, FAKE, None, 4096, None) == WS
     assert e(FAKE, 100, 0, FAKE, FAKE, FAKE, FAKE, 8, None) == WS
     assert e(MIS, 100, 0, FAKE, FAKE, FAKE, FAKE, 4096, None) == ALIGN
+
+
+def test_dropout_argument_errors(L):
+    d = L.qlora_lora_dropout
+    assert d(FAKE, 16, 64, 1.0, 1, 2, FAKE, None) == UNSUP
+    assert d(FAKE, 16, 64, -0.1, 1, 2, FAKE, None) == UNSUP
+    assert d(FAKE, 16, 64, float("nan"), 1, 2, FAKE, None) == UNSUP
+    assert d(FAKE, 16, 60, 0.05, 1, 2, FAKE, None) == SHAPE
+    assert d(FAKE, 16, 64, 0.05, 1, 2, MIS, None) == ALIGN
+    assert d(None, 0, 64, 0.05, 1, 2, None, None) == OK
+    f = L.qlora_linear_fwd_dropout
+    assert f(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, 1.5, 1, 2, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+             None) == UNSUP
+    assert f(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, 0.05, 1, 2, FAKE, FAKE, None, FAKE, 1 << 30,
+             None) == NULL
+    assert f(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, 0.05, 1, 2, FAKE, FAKE, FAKE, FAKE, 8,
+             None) == WS
+    b = L.qlora_linear_bwd_dropout
+    ws1 = q.workspace_size(1, 16, 64, 128, 8)
+    assert b(_weight(), FAKE, FAKE, 16, FAKE, FAKE, 8, 16.0, 0.05, 1, 2, FAKE, FAKE, FAKE, FAKE,
+             FAKE, ws1, None) == WS  # needs the op-2 size
+    assert b(_weight(), FAKE, FAKE, 16, FAKE, FAKE, 8, 16.0, 1.0, 1, 2, FAKE, FAKE, FAKE, FAKE,
+             FAKE, 1 << 30, None) == UNSUP
+    assert b(_weight(), None, FAKE, 16, FAKE, FAKE, 8, 16.0, 0.05, 1, 2, FAKE, FAKE, FAKE, FAKE,
+             FAKE, 1 << 30, None) == NULL
