@@ -1,0 +1,133 @@
+"""Pins of the oracle's adapter merge and re-quantisation."""
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from oracle.merge import merge_16bit, merge_4bit, merge_bf16, rank_r_sum, requantize
+from oracle.quant import bf16_round, bf16_to_f64, dequantize_nf4, double_quant, quantize_nf4, \
+    unpack_nibbles
+
+
+def _bf16_vals(x):
+    """float32 array of the bf16 values nearest to x."""
+    return bf16_to_f64(bf16_round(np.asarray(x, np.float32).ravel())).astype(np.float32).reshape(
+        np.shape(x))
+
+
+def test_rank_r_sum_exact_on_dyadic_inputs():
+    """Small dyadic factors: every partial sum is exact, so the float32 sum
+    equals the exact rational product."""
+    rng = np.random.default_rng(31)
+    r, N, K = 8, 5, 7
+    A = (rng.integers(-16, 17, (r, K)) / 8.0).astype(np.float32)
+    B = (rng.integers(-16, 17, (N, r)) / 16.0).astype(np.float32)
+    got = rank_r_sum(A, B)
+    for n in range(N):
+        for k in range(K):
+            exact = sum(Fraction(float(B[n, j])) * Fraction(float(A[j, k])) for j in range(r))
+            assert Fraction(float(got[n, k])) == exact
+
+
+def test_rank_r_sum_error_bound_random():
+    rng = np.random.default_rng(32)
+    r, N, K = 64, 16, 32
+    A = _bf16_vals(rng.standard_normal((r, K)) * 0.01)
+    B = _bf16_vals(rng.standard_normal((N, r)) * 0.01)
+    got = rank_r_sum(A, B).astype(np.float64)
+    exact = B.astype(np.float64) @ A.astype(np.float64)  # products and sums exact enough in f64
+    bound = r * 2.0 ** -24 * (np.abs(B.astype(np.float64)) @ np.abs(A.astype(np.float64)))
+    assert np.all(np.abs(got - exact) <= bound)
+    # the order is fixed: j ascending (a reversed order rounds differently somewhere)
+    rev = np.zeros_like(got, dtype=np.float32)
+    for j in reversed(range(r)):
+        rev = rev + B[:, j:j + 1] * A[j:j + 1, :]
+    assert not np.array_equal(rev, rank_r_sum(A, B))
+
+
+def test_zero_adapter_leaves_the_base():
+    rng = np.random.default_rng(33)
+    N, K, r = 8, 128, 4
+    base = _bf16_vals(rng.standard_normal((N, K)) * 0.02)
+    A = _bf16_vals(rng.standard_normal((r, K)) * 0.01)
+    Z = np.zeros((N, r), np.float32)
+    m = merge_bf16(base, A, Z, 0.25)
+    assert np.array_equal(m, bf16_round(base.ravel()).reshape(N, K))
+    m2 = merge_bf16(base, np.zeros_like(A), _bf16_vals(rng.standard_normal((N, r))), 4.0)
+    assert np.array_equal(m2, m)
+
+
+def test_merge_formula_on_one_element():
+    """x = RN32(w + RN32(s·acc)), then RNE to bf16."""
+    A = np.array([[0.5], [0.25]], np.float32).T.reshape(2, 1)   # [r=2][K=1]
+    B = np.array([[0.75, -1.5]], np.float32)                     # [N=1][r=2]
+    base = np.array([[1.0]], np.float32)
+    s = np.float32(1 / 3)
+    acc = np.float32(0.75 * 0.5) + np.float32(-1.5 * 0.25)       # 0.375 - 0.375 = 0
+    assert acc == 0.0
+    assert merge_bf16(base, A, B, s)[0, 0] == bf16_round(np.array([1.0], np.float32))[0]
+    B2 = np.array([[0.75, 1.5]], np.float32)
+    x = np.float32(1.0) + np.float32(s * np.float32(0.75))
+    assert merge_bf16(base, A, B2, s)[0, 0] == bf16_round(np.array([x], np.float32))[0]
+
+
+def test_requantized_decode_is_stable_and_tiny_adapters_vanish_in_4bit():
+    """The page's warning: merging into the 4-bit base re-rounds onto the
+    4-bit grid.  Re-quantising a decoded NF4 weight returns its own codes, so
+    an adapter far below the level spacing is lost entirely."""
+    rng = np.random.default_rng(34)
+    N, K, r = 64, 512, 8
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    packed, absmax = quantize_nf4(W.ravel())
+    q, c2 = double_quant(absmax)
+    # without an adapter the re-quantised decode returns the original codes
+    z = np.zeros((N, r), np.float32)
+    _, (p0, _, _, _) = merge_4bit(packed, q, c2, (N, K), np.zeros((r, K), np.float32), z, 0.25)
+    assert np.array_equal(unpack_nibbles(p0), unpack_nibbles(packed))
+    # an adapter of ~6e-4 per weight: above the bf16 step of these weights,
+    # well below the NF4 level gaps (~5e-3)
+    A = _bf16_vals(rng.standard_normal((r, K)) * 3e-2)
+    B = _bf16_vals(rng.standard_normal((N, r)) * 3e-2)
+    m, (p4, q4, c24, d4) = merge_4bit(packed, q, c2, (N, K), A, B, 0.25)
+    base = dequantize_nf4(packed, q, c2, N * K).reshape(N, K)
+    # the delta is real in 16 bits (most merged bf16 values moved) ...
+    assert np.mean(m != base) > 0.5
+    # ... and gone after re-quantisation: nearly every code is the original one,
+    # and the decoded change keeps under 15 % of the delta (its projection on
+    # the delta; the rest is scale noise from the re-quantised absmax)
+    assert np.mean(unpack_nibbles(p4) != unpack_nibbles(packed)) < 0.01
+    D = 0.25 * (B.astype(np.float64) @ A.astype(np.float64))
+    d = bf16_to_f64(d4) - bf16_to_f64(base)
+    assert np.sum(d * D) / np.sum(D * D) < 0.15
+
+
+def test_16bit_path_is_closer_to_the_merged_weight():
+    rng = np.random.default_rng(35)
+    N, K, r = 64, 1024, 16
+    W16 = _bf16_vals(rng.standard_normal((N, K)) * 0.02)
+    A = _bf16_vals(rng.standard_normal((r, K)) * 0.05)
+    B = _bf16_vals(rng.standard_normal((N, r)) * 0.05)
+    s = 0.25
+    target = W16.astype(np.float64) + s * (B.astype(np.float64) @ A.astype(np.float64))
+    m16, (_, _, _, d16) = merge_16bit(bf16_round(W16.ravel()).reshape(N, K), A, B, s)
+    packed, absmax = quantize_nf4(W16.ravel())
+    q, c2 = double_quant(absmax)
+    m4, (_, _, _, d4) = merge_4bit(packed, q, c2, (N, K), A, B, s)
+    e16 = np.linalg.norm(bf16_to_f64(d16) - target)
+    e4 = np.linalg.norm(bf16_to_f64(d4) - target)
+    assert e4 > 1.2 * e16, (e4, e16)
+    # the merged 16-bit weight itself is within bf16 rounding of the target
+    assert np.all(np.abs(bf16_to_f64(m16) - target) <= 2.0 ** -8 * np.abs(target) + 1e-12)
+
+
+def test_requantize_goes_through_the_quantiser():
+    rng = np.random.default_rng(36)
+    m = bf16_round((rng.standard_normal(64 * 300) * 0.03).astype(np.float32)).reshape(75, 256)
+    packed, q, c2, dec = requantize(m)
+    p2, a2 = quantize_nf4(bf16_to_f64(m).astype(np.float32).ravel())
+    q2, c22 = double_quant(a2)
+    assert np.array_equal(packed, p2) and np.array_equal(q, q2) and np.array_equal(c2, c22)
+    assert dec.shape == (75, 256)
+    t = torch.from_numpy(bf16_to_f64(dec))
+    assert torch.all(torch.isfinite(t))
