@@ -11,8 +11,9 @@ dequantiser (GB/s over the weight), and the few-token forward at 8192 -> 28672
 256 MB Infinity Cache), the 32-bit AdamW step with gradient clipping over
 the 67M LoRA parameters of LLaMA-7B's attention projections (GB/s), and the
 single-quantisation INT4 quantiser, decoder and error pass with the
-NF4-vs-INT4 error on the 11008 x 4096 weight, and the training step with LoRA
-dropout (p = 0.05) on the adapter input.
+NF4-vs-INT4 error on the 11008 x 4096 weight, the training step with LoRA
+dropout (p = 0.05) on the adapter input, and the adapter merge with
+re-quantisation at that shape.
 
 Prints ONE JSON line.  --gpus N > 1 is not supported (single-GPU build).
 """
@@ -29,7 +30,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-GEMM_SOURCES = ["qlora_gemm.hip", "qlora_common.h", "qlora_kernels.h"]
+# float32 fma on the vector ALU without packed-float32 instructions (the
+# library is built without them): 256 CUs x 64 lanes x 2 flop x 2.4 GHz
+FP32_FMA_PEAK_TFLOPS = 78.6
+GEMM_SOURCES = ["qlora_gemm.hip", "qlora_common.h", "qlora_kernels.h", "qlora_philox.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_gemm_fwd_llama7b_mlp.txt")
 CALIB_BYTES = 512 << 20  # plain device copy used to scale the byte counters
 
@@ -333,6 +337,7 @@ def main():
         del Xdr, ws_d
         rows["adamw_step_llama7b_lora_r64"] = adamw_row(dev)
         rows.update(variant_rows(W))
+        rows["merge_adapter_11008x4096_r64"] = merge_row(W, B, A, alpha)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -441,6 +446,39 @@ def variant_rows(W):
     rows["nf4_vs_int4_mse"] = dict(mse_nf4=mse["nf4"], mse_int4=mse["int4"],
                                    improvement_pct=(1 - mse["nf4"] / mse["int4"]) * 100)
     return rows
+
+
+def merge_row(W, B, A, alpha):
+    """Adapter merge at the 11008 x 4096 shape, r = 64: the merge kernel alone
+    (2·n·r flop of float32 fma on the vector ALU, fixed order), the merge with
+    re-quantisation, both bases, and how much of the adapter's delta survives
+    re-quantisation on each path (its projection on the delta)."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+
+    N, K = W.shape
+    r = A.shape[0]
+    s = alpha / r
+    W16 = W.to(torch.bfloat16)
+    wq = q.quantize_weight(W)
+    merged = torch.empty(N, K, dtype=torch.bfloat16, device=W.device)
+    ms_m = _time_ms(lambda: q.merge_adapter(W16, A, B, alpha, requantize=False, merged=merged), 10)
+    ms_mq = _time_ms(lambda: q.merge_adapter(W16, A, B, alpha, merged=merged), 10)
+    ms_m4 = _time_ms(lambda: q.merge_adapter(wq, A, B, alpha, merged=merged), 10)
+    flops = 2.0 * N * K * r
+    D = s * (B.float() @ A.float())
+    base4 = q.dequantize_nf4(wq).float()
+    out = {}
+    for name, base in (("16bit", W16), ("4bit", wq)):
+        _, rq = q.merge_adapter(base, A, B, alpha)
+        d = q.dequantize_nf4(rq).float()
+        ref = base4 if name == "4bit" else W16.float()
+        out["delta_kept_" + name] = float(((d - ref) * D).sum() / (D * D).sum())
+        out["rel_err_" + name] = float((d - (W16.float() + D)).norm() / (W16.float() + D).norm())
+    return dict(r=r, ms_merge=ms_m, TFLOPs_merge=flops / (ms_m * 1e-3) / 1e12,
+                alu_frac=flops / (ms_m * 1e-3) / 1e12 / FP32_FMA_PEAK_TFLOPS,
+                ms_merge_requant_16bit=ms_mq, ms_merge_requant_4bit=ms_m4, **out)
 
 
 def cpu_baseline(inp, wlc):

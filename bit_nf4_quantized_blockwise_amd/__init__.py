@@ -79,6 +79,7 @@ _SIGNATURES = {
                                   _SZ, _P], _I32),
     "qlora_linear_bwd_dropout": ([_W, _P, _P, _I64, _P, _P, _I32, _F, _F, _U64, _U64, _P, _P, _P,
                                   _P, _P, _SZ, _P], _I32),
+    "qlora_merge_adapter": ([_P, _W, _I64, _I64, _P, _P, _I32, _F, _P, _P, _P, _P, _P], _I32),
     "qlora_quantize_4bit": ([_P, _I64, _I32, _P, _P, _P], _I32),
     "qlora_dequantize_4bit": ([_P, _P, _I64, _I32, _P, _P], _I32),
     "qlora_quant_sq_error": ([_P, _I64, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
@@ -317,6 +318,34 @@ def linear_bwd(wq, X, dY, A, B, U, alpha, workspace=None, dX=None, dA=None, dB=N
                                   alpha, _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
                                   ws.numel(), _stream(dev)), "qlora_linear_bwd")
     return dX, dA, dB
+
+
+# ---- adapter merge ----------------------------------------------------------------
+
+def merge_adapter(base, A, B, alpha, requantize=True, merged=None):
+    """(merged bf16 [n_out][k_in], NF4Tensor of it or None).  base: a bf16
+    tensor [n_out][k_in] (the 16-bit base) or an NF4Tensor (the 4-bit base)."""
+    r = A.shape[0]
+    if isinstance(base, NF4Tensor):
+        n_out, k_in, dev = base.n_out, base.k_in, base.packed.device
+        w16, st = None, base.c_struct()
+        w4 = ctypes.byref(st)
+    else:
+        (n_out, k_in), dev = base.shape, base.device
+        w16, w4 = base, None
+    merged = torch.empty(n_out, k_in, dtype=torch.bfloat16, device=dev) if merged is None else merged
+    out = None
+    packed = qa = c2 = None
+    if requantize:
+        n = n_out * k_in
+        packed = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        qa = torch.empty(n // 64, dtype=torch.int8, device=dev)
+        c2 = torch.empty((n // 64 + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=dev)
+        out = NF4Tensor(packed, qa, c2, n_out, k_in)
+    _check(lib().qlora_merge_adapter(_ptr(w16), w4, n_out, k_in, _ptr(A), _ptr(B), r, alpha,
+                                     _ptr(merged), _ptr(packed), _ptr(qa), _ptr(c2),
+                                     _stream(dev)), "qlora_merge_adapter")
+    return merged, out
 
 
 # ---- LoRA dropout ---------------------------------------------------------------

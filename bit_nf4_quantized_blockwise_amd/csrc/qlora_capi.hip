@@ -11,6 +11,7 @@
 
 #include "qlora_kernels.h"
 #include "qlora_optim.h"
+#include "qlora_merge.h"
 #include "qlora_quant_variants.h"
 
 using namespace qlora;
@@ -718,6 +719,56 @@ qlora_status qlora_quant_sq_error(const float* w, int64_t n, int32_t code, const
                          absmax, partials);
   }
   hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(256), 0, st, partials, npart, sse);
+  return launched();
+}
+
+qlora_status qlora_merge_adapter(const qlora_bf16* w16, const qlora_nf4_weight* w4, int64_t n_out,
+                                 int64_t k_in, const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                 float alpha, qlora_bf16* merged, uint8_t* packed, int8_t* qabsmax,
+                                 float* c2, void* stream) {
+  QCHECK(w16 != nullptr || w4 != nullptr, QLORA_ERR_NULL);
+  QCHECK(w16 == nullptr || w4 == nullptr, QLORA_ERR_UNSUPPORTED);
+  QCHECK(n_out >= 0 && k_in >= 0 && k_in % 64 == 0, QLORA_ERR_SHAPE);
+  QCHECK(ceil_div(n_out, kMergeRows) <= 65535, QLORA_ERR_SHAPE);
+  QCHECK(r >= 1 && r <= QLORA_MAX_RANK, QLORA_ERR_UNSUPPORTED);
+  if (w4) {
+    qlora_status v = validate_weight(w4);
+    if (v != QLORA_OK) return v;
+    QCHECK(w4->n_out == n_out && w4->k_in == k_in, QLORA_ERR_SHAPE);
+  }
+  if (n_out == 0 || k_in == 0) return QLORA_OK;
+  if (w16) {
+    ALIGNED_OR_NULL(w16);
+  }
+  ALIGNED_OR_NULL(A);
+  ALIGNED_OR_NULL(B);
+  ALIGNED_OR_NULL(merged);
+  if (packed) {
+    ALIGNED_OR_NULL(packed);
+    ALIGNED_OR_NULL(qabsmax);
+    ALIGNED_OR_NULL(c2);
+  }
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = as_stream(stream);
+  MergeArgs g{};
+  g.w16 = w16;
+  if (w4) {
+    g.packed = w4->packed;
+    g.qabsmax = w4->qabsmax;
+    g.c2 = w4->c2;
+  }
+  g.a = A; g.b = B; g.n_out = n_out; g.k_in = k_in; g.r = r; g.s = scale_of(alpha, r);
+  g.merged = merged;
+  hipLaunchKernelGGL(merge_adapter_kernel,
+                     dim3((unsigned)ceil_div(k_in, kMergeCols), (unsigned)ceil_div(n_out, kMergeRows)),
+                     dim3(256), 0, st, g);
+  if ((s = launched()) != QLORA_OK || !packed) return s;
+  const int64_t n = n_out * k_in, nb = n / 64, ng = ceil_div(nb, 256);
+  QCHECK(ng <= 0x7fffffff, QLORA_ERR_SHAPE);
+  const int64_t grid = std::min<int64_t>(ng, 4 * (int64_t)device_cus());
+  hipLaunchKernelGGL(quantize_nf4_dq_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, st, merged, n,
+                     nb, packed, qabsmax, c2);
   return launched();
 }
 

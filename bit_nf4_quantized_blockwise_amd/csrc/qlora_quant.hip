@@ -26,6 +26,7 @@
 // quantiser, 0.52 B read + 2 B written per weight for the dequantiser.
 
 #include "qlora_kernels.h"
+#include "qlora_merge.h"
 #include "qlora_quant_variants.h"
 #include "qlora_reduce.h"
 
@@ -201,6 +202,27 @@ __device__ inline void load_16(const float* __restrict__ w, int64_t n, int64_t b
   }
 }
 
+// The 16 values of lane `sub` of block blk from a bf16 input (exact in float32).
+__device__ inline void load_16(const uint16_t* __restrict__ w, int64_t n, int64_t blk, int sub,
+                               float (&v)[16]) {
+  const int64_t base = blk * kBlock + (int64_t)sub * 16;
+  if (base + 16 <= n) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(w + base);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u32x4 x = p[j];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v[8 * j + 2 * d] = bits_to_float(x[d] << 16);
+        v[8 * j + 2 * d + 1] = bits_to_float(x[d] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = (base + j < n) ? bits_to_float((uint32_t)w[base + j] << 16) : 0.0f;
+  }
+}
+
 // packed[nblocks*32], absmax[nblocks]; 64 blocks per 256-thread workgroup.
 template <int CODE>
 __device__ inline void quantize_blocks(const float* __restrict__ w, int64_t n, int64_t nblocks,
@@ -260,12 +282,13 @@ __global__ __launch_bounds__(256) void double_quant_kernel(const float* __restri
 
 // Fused: one workgroup per DQ group (256 blocks = 16384 elements), four passes
 // of 64 blocks, then the second level from the absmax values kept in LDS.
-__global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __restrict__ w, int64_t n,
-                                                              int64_t nblocks,
-                                                              uint8_t* __restrict__ packed,
-                                                              int8_t* __restrict__ qabsmax,
-                                                              float* __restrict__ c2,
-                                                              float* __restrict__ absmax_out) {
+namespace {
+
+template <typename In>
+__device__ inline void quantize_dq_groups(const In* __restrict__ w, int64_t n, int64_t nblocks,
+                                          uint8_t* __restrict__ packed,
+                                          int8_t* __restrict__ qabsmax, float* __restrict__ c2,
+                                          float* __restrict__ absmax_out) {
   __shared__ float amax[kGroup];
   __shared__ float red[4];
   __shared__ float thr[64 * kTStride];
@@ -317,6 +340,26 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
     }
     __syncthreads();  // amax and red are rewritten by the next group
   }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __restrict__ w, int64_t n,
+                                                              int64_t nblocks,
+                                                              uint8_t* __restrict__ packed,
+                                                              int8_t* __restrict__ qabsmax,
+                                                              float* __restrict__ c2,
+                                                              float* __restrict__ absmax_out) {
+  quantize_dq_groups(w, n, nblocks, packed, qabsmax, c2, absmax_out);
+}
+
+// The same from a bf16 weight (the merged 16-bit weight of an adapter merge).
+__global__ __launch_bounds__(256) void quantize_nf4_dq_bf16_kernel(const uint16_t* __restrict__ w,
+                                                                   int64_t n, int64_t nblocks,
+                                                                   uint8_t* __restrict__ packed,
+                                                                   int8_t* __restrict__ qabsmax,
+                                                                   float* __restrict__ c2) {
+  quantize_dq_groups(w, n, nblocks, packed, qabsmax, c2, static_cast<float*>(nullptr));
 }
 
 // Standalone dequantisation to bf16.  A workgroup decodes 1024 consecutive

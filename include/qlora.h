@@ -145,6 +145,29 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight *w /* host struct *
                                       const qlora_bf16 *U, qlora_bf16 *dX, float *dA, float *dB,
                                       void *workspace, size_t ws_bytes, void *stream);
 
+/* ---- adapter merge ------------------------------------------------------- */
+
+/* Merge a trained adapter into the base weight and (optionally) re-quantise
+ * it ("QLoRAとは？4bit量子化＋LoRAの仕組み・VRAM目安・実装手順と採用判断を解説",
+ * issoh.co.jp, section on merging and distributing the adapter: merge into the
+ * 16-bit base, keep the merged 16-bit model, quantise it again for 4-bit
+ * inference; merging into the 4-bit base re-rounds the sum onto the 4-bit
+ * grid).  Exactly one base: w16 (bf16 [n_out][k_in], the recommended path) or
+ * w4 (the NF4 + DQ weight, decoded as qlora_dequantize_nf4 does; the path the
+ * page warns about).  With s = RN32(alpha / r), for every element:
+ *   acc = Σ_j B[n][j]·A[j][k]   float32, j = 0, 1, …, r − 1 in order
+ *   merged[n][k] = RNE_bf16(RN32(base + RN32(s·acc)))
+ * A [r][k_in], B [n_out][r] bf16; merged bf16 [n_out][k_in] (required).  When
+ * packed is not NULL, merged is then quantised exactly as
+ * qlora_quantize_nf4_dq would quantise its float32 values: packed
+ * [n_out*k_in/2], qabsmax [n_out*k_in/64], c2 [ceil(n_out*k_in/16384)].
+ * k_in % 64 == 0, ceil(n_out/16) <= 65535, 1 <= r <= 256.  Both bases NULL:
+ * QLORA_ERR_NULL; both given: QLORA_ERR_UNSUPPORTED. */
+qlora_status qlora_merge_adapter(const qlora_bf16 *w16, const qlora_nf4_weight *w4 /* host struct */,
+                                 int64_t n_out, int64_t k_in, const qlora_bf16 *A,
+                                 const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *merged,
+                                 uint8_t *packed, int8_t *qabsmax, float *c2, void *stream);
+
 /* ---- quantiser variants -------------------------------------------------- */
 
 #define QLORA_CODE_NF4 0   /* the 16 NormalFloat levels */

@@ -194,3 +194,18 @@ def test_dropout_argument_errors(L):
              FAKE, 1 << 30, None) == UNSUP
     assert b(_weight(), None, FAKE, 16, FAKE, FAKE, 8, 16.0, 0.05, 1, 2, FAKE, FAKE, FAKE, FAKE,
              FAKE, 1 << 30, None) == NULL
+
+
+def test_merge_argument_errors(L):
+    m = L.qlora_merge_adapter
+    w4 = _weight(64, 128)
+    assert m(None, None, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, None, None, None, None) == NULL
+    assert m(FAKE, w4, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, None, None, None, None) == UNSUP
+    assert m(FAKE, None, 64, 100, FAKE, FAKE, 8, 16.0, FAKE, None, None, None, None) == SHAPE
+    assert m(FAKE, None, 64, 128, FAKE, FAKE, 0, 16.0, FAKE, None, None, None, None) == UNSUP
+    assert m(FAKE, None, 64, 128, FAKE, FAKE, 257, 16.0, FAKE, None, None, None, None) == UNSUP
+    assert m(None, _weight(32, 128), 64, 128, FAKE, FAKE, 8, 16.0, FAKE, None, None, None,
+             None) == SHAPE
+    assert m(FAKE, None, 64, 128, FAKE, FAKE, 8, 16.0, None, None, None, None, None) == NULL
+    assert m(FAKE, None, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, FAKE, MIS, FAKE, None) == ALIGN
+    assert m(FAKE, None, 0, 128, FAKE, FAKE, 8, 16.0, None, None, None, None, None) == OK
