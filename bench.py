@@ -148,6 +148,44 @@ def summarize_stats(stats_csv, bench_log, out_path):
     print(open(out_path).read())
 
 
+def summarize_counters(out_path, *csvs):
+    """Per-dispatch averages of the SQ counters of the forward dequant-GEMM from
+    rocprofv3 --pmc runs of --pmc-pass, with the ratios read off them."""
+    import csv
+
+    vals = {}
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            if "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0>" not in r["Kernel_Name"]:
+                continue
+            d = vals.setdefault(r["Counter_Name"], {})
+            key = (path, r["Dispatch_Id"])  # a counter may appear in several runs
+            d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+    avg = {k: sum(v.values()) / len(v) for k, v in vals.items()}
+    with open(out_path, "w") as fh:
+        fh.write("# SQ counters of the forward dequant-GEMM (LLaMA-7B MLP: 4096 tokens, 4096 -> "
+                 "11008, r = 64),\n# per dispatch, averaged over the dispatches of --pmc-pass.  "
+                 "Commands (from /tmp, TMPDIR=/tmp),\n# one rocprofv3 run per counter set:\n")
+        fh.write("#   rocprofv3 --pmc <set> --output-format csv -d <dir_i> -o c -- python3 "
+                 "<repo>/bench.py --pmc-pass\n")
+        fh.write("#   python3 <repo>/bench.py --summarize-counters <this file> "
+                 "<dir_1>/c_counter_collection.csv ...\n")
+        fh.write(f"kernel_source_sha256_16 = {gemm_source_hash()}\n")
+        for k in sorted(avg):
+            fh.write(f"{k} = {avg[k]:.6g}\n")
+        if "SQ_INSTS_MFMA" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            fh.write(f"# matrix-pipe cycles per MFMA = "
+                     f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / avg['SQ_INSTS_MFMA']:.2f}\n")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            fh.write(f"# share of matrix-pipe busy cycles with VALU work beside it = "
+                     f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}\n")
+        if "SQ_WAIT_INST_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+            fh.write(f"# wave cycles waiting on a dependency (s_waitcnt) = "
+                     f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.3f}, on LDS = "
+                     f"{avg.get('SQ_WAIT_INST_LDS', 0.0) / avg['SQ_WAVE_CYCLES']:.3f}\n")
+    print(open(out_path).read())
+
+
 def pmc_pass():
     """Short run for counter collection: the forward dequant-GEMM a few times
     and a device copy of CALIB_BYTES (the byte counters' calibration)."""
@@ -207,12 +245,17 @@ def main():
                     help="write the HBM traffic summary from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "BENCH_LOG", "OUT_TXT"),
                     help="write the kernel statistics summary of a rocprofv3 --stats run")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PATH",
+                    help="OUT_TXT then the counter CSVs of rocprofv3 --pmc runs of --pmc-pass")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the build has no multi-GPU path "
