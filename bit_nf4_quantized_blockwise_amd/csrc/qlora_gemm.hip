@@ -486,15 +486,18 @@ __device__ inline u32x4 scale_part(const u32x4& v, float s, int part) {
 // up to two LDS reads, one VMEM instruction and four VALU instructions, with
 // the LDS writes spread in.  One wave per SIMD issues in order, so VALU work
 // placed between MFMAs runs while the matrix core is busy instead of after it.
-template <int NMFMA>
+// DSR LDS reads and VALU instructions per MFMA: measured best at 2 and 4 for
+// the forward tile and at 3 and 3 for the input-gradient tile (whose decode
+// finishes each quarter in place); more VALU per MFMA delays the next MFMA.
+template <int NMFMA, int DSR = 2, int VALU = 4>
 __device__ inline void interleave() {
 #pragma unroll
   for (int i = 0; i < NMFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);     // DS write
   }
 }
 
@@ -784,6 +787,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     // loads issued with them are a whole tile old by then).
     ADma<MT> adma;
     adma.init(g.a, g.lda, g.rows, row0, wave, lane);
+    constexpr int kDsr = BMODE == B_NF4_RED ? 3 : 2, kValu = BMODE == B_NF4_RED ? 3 : 4;
     bf16x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
     float lk0[16], lk1[16];
     // Codebook reads a quarter ahead where registers allow (column tiles: one
@@ -830,12 +834,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         lookup(D, ks + 1, ln);
         mma.mfma(ac, bc);
         finish(D, ks, lc, cur ^ 1);
-        interleave<FM * FN>();
+        interleave<FM * FN, kDsr, kValu>();
         __builtin_amdgcn_sched_barrier(0);
       }
       mfma_half(fa1, fb1, 0);
       finish(D, 3, lk1, cur ^ 1);
-      interleave<FM * FN / 2>();
+      interleave<FM * FN / 2, kDsr, kValu>();
       __builtin_amdgcn_sched_barrier(0);
       wait_vmem_all();
       __syncthreads();
@@ -845,7 +849,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       adma.issue(As(cur), (int64_t)(kt + 2) * KT, kend);
       load_b(D, kt + 3);
       mfma_half(fa1, fb1, 1);
-      interleave<FM * FN / 2>();
+      interleave<FM * FN / 2, kDsr, kValu>();
       __builtin_amdgcn_sched_barrier(0);
     };
     if (kt_begin < kt_end) {
