@@ -19,6 +19,7 @@ Prints ONE JSON line.  --gpus N > 1 is not supported (single-GPU build).
 """
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -218,6 +219,19 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+def _c_call(fn, *args):
+    """A library entry point with its arguments marshalled once, so a timing
+    loop spends ~µs per call on the host and the GPU queue stays ahead of it."""
+    import bit_nf4_quantized_blockwise_amd as q
+    name = fn.__name__
+
+    def call():
+        s = fn(*args)
+        if s != 0:
+            raise q.QloraError(s, name)
+    return call
+
+
 def _time_ms(fn, iters, warmup=2):
     import torch
     for _ in range(warmup):
@@ -324,11 +338,17 @@ def main():
         n = K * N
         # quantiser (fused NF4 + DQ): reads 4 B, writes 0.5 + 1/64 + 4/16384 B per weight
         qbytes = n * 4 + n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4
-        ms_q = _time_ms(lambda: q.quantize_nf4_dq(W), 10)
+        L = q.lib()
+        st = q._stream(dev)
+        pk_, qa_, c2_, am_ = q.quantize_nf4_dq(W, want_absmax=True)
+        ms_q = _time_ms(_c_call(L.qlora_quantize_nf4_dq, q._ptr(W), n, q._ptr(pk_), q._ptr(qa_),
+                                q._ptr(c2_), q._ptr(am_), st), 20, warmup=5)
         # dequantiser: reads the NF4 storage, writes bf16
         dbytes = n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4 + 2 * n
         wd = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
-        ms_d = _time_ms(lambda: q.dequantize_nf4(wq, out=wd), 10)
+        wst = wq.c_struct()
+        ms_d = _time_ms(_c_call(L.qlora_dequantize_nf4, ctypes.byref(wst), q._ptr(wd), st), 20,
+                        warmup=5)
         rows["quantize_nf4_dq"] = dict(shape=[N, K], ms=ms_q, GBps=qbytes / ms_q / 1e6,
                                        hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS)
         rows["dequantize_nf4"] = dict(shape=[N, K], ms=ms_d, GBps=dbytes / ms_d / 1e6,
@@ -466,17 +486,25 @@ def variant_rows(W):
     dbytes = n // 2 + 4 * nb + 2 * n
     ebytes = 4 * n + n // 2 + 4 * nb
     rows, mse = {}, {}
+    L = q.lib()
+    st = q._stream(W.device)
     out = torch.empty(n, dtype=torch.bfloat16, device=W.device)
     ws = torch.empty(q.quant_error_workspace_size(n), dtype=torch.uint8, device=W.device)
     sse = torch.empty(1, dtype=torch.float64, device=W.device)
     for code in ("int4", "nf4"):
         packed, absmax = q.quantize_4bit(W, code)
-        ms_e = _time_ms(lambda: q.quant_sq_error(W, packed, absmax, code, out=sse, workspace=ws),
-                        10)
+        cd = q.CODES[code]
+        ms_e = _time_ms(_c_call(L.qlora_quant_sq_error, q._ptr(W), n, cd, q._ptr(packed),
+                                q._ptr(absmax), q._ptr(sse), q._ptr(ws), ws.numel(), st), 20,
+                        warmup=5)
         mse[code] = float(sse.cpu()[0]) / n
         if code == "int4":
-            ms_q = _time_ms(lambda: q.quantize_4bit(W, code), 10)
-            ms_d = _time_ms(lambda: q.dequantize_4bit(packed, absmax, n, code, out=out), 10)
+            p2 = torch.empty_like(packed)
+            a2 = torch.empty_like(absmax)
+            ms_q = _time_ms(_c_call(L.qlora_quantize_4bit, q._ptr(W), n, cd, q._ptr(p2), q._ptr(a2),
+                                    st), 20, warmup=5)
+            ms_d = _time_ms(_c_call(L.qlora_dequantize_4bit, q._ptr(packed), q._ptr(absmax), n, cd,
+                                    q._ptr(out), st), 20, warmup=5)
             rows["quantize_int4_single"] = dict(shape=list(W.shape), ms=ms_q,
                                                 GBps=qbytes / ms_q / 1e6,
                                                 hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS)

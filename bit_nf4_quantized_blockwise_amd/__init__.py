@@ -183,15 +183,16 @@ def double_quant(absmax):
     return q, c2
 
 
-def quantize_nf4_dq(w, want_absmax=False):
-    """Both levels in one pass: (packed, qabsmax, c2[, absmax])."""
+def quantize_nf4_dq(w, want_absmax=False, one_pass=False):
+    """Both levels: (packed, qabsmax, c2[, absmax]).  The first-level scales
+    are always given a buffer (the faster two-launch route) unless one_pass."""
     n = w.numel()
     nb = _nblocks(n)
     dev = w.device
     packed = torch.empty(nb * 32, dtype=torch.uint8, device=dev)
     q = torch.empty(nb, dtype=torch.int8, device=dev)
     c2 = torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=dev)
-    absmax = torch.empty(nb, dtype=torch.float32, device=dev) if want_absmax else None
+    absmax = None if one_pass else torch.empty(nb, dtype=torch.float32, device=dev)
     _check(lib().qlora_quantize_nf4_dq(_ptr(w), n, _ptr(packed), _ptr(q), _ptr(c2),
                                        _ptr(absmax), _stream(dev)), "qlora_quantize_nf4_dq")
     return (packed, q, c2, absmax) if want_absmax else (packed, q, c2)

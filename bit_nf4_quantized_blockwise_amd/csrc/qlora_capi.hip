@@ -802,12 +802,25 @@ qlora_status qlora_quantize_nf4_dq(const float* w, int64_t n, uint8_t* packed, i
   if (s != QLORA_OK) return s;
   const int64_t nb = ceil_div(n, 64);
   const int64_t ng = ceil_div(nb, 256);
-  QCHECK(ng <= 0x7fffffff, QLORA_ERR_SHAPE);
-  // four workgroups per CU stride over the groups (enough bytes in flight,
-  // and every workgroup overlaps its loads with its own arithmetic)
+  QCHECK(ng <= 0x7fffffff && ceil_div(nb * 4, 256) <= 0x7fffffff, QLORA_ERR_SHAPE);
+  hipStream_t st = as_stream(stream);
+  if (absmax) {
+    // With somewhere to put the first-level scales: the first level over
+    // 64-block workgroups (many small workgroups keep far more loads in
+    // flight than one workgroup per 256-block group can), then the second
+    // level from the scales — measured faster than the one-pass kernel
+    // despite writing and re-reading 4 bytes per 64 weights.
+    hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)ceil_div(nb * 4, 256)), dim3(256), 0, st,
+                       w, n, nb, packed, absmax);
+    hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ng), dim3(256), 0, st,
+                       (const float*)absmax, nb, qabsmax, c2);
+    return launched();
+  }
+  // one pass: four workgroups per CU stride over the groups (enough bytes in
+  // flight, and every workgroup overlaps its loads with its own arithmetic)
   const int64_t grid = std::min<int64_t>(ng, 4 * (int64_t)device_cus());
-  hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
-                     w, n, nb, packed, qabsmax, c2, absmax);
+  hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)grid), dim3(256), 0, st, w, n, nb,
+                     packed, qabsmax, c2, absmax);
   return launched();
 }
 

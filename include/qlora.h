@@ -97,9 +97,10 @@ qlora_status qlora_quantize_nf4(const float *w, int64_t n, int32_t blocksize, ui
 qlora_status qlora_double_quant(const float *absmax, int64_t nblocks, int32_t group,
                                 int8_t *qabsmax, float *c2, void *stream);
 
-/* Both levels in one pass over w.  Produces exactly the bytes that
- * qlora_quantize_nf4 followed by qlora_double_quant produce.  absmax may be
- * NULL (not written). */
+/* Both levels.  Produces exactly the bytes that qlora_quantize_nf4 followed by
+ * qlora_double_quant produce.  absmax (float32 [ceil(n/64)], optional)
+ * receives the first-level scales; given it, the two levels run as those two
+ * launches (the faster route), without it as one pass over w. */
 qlora_status qlora_quantize_nf4_dq(const float *w, int64_t n, uint8_t *packed, int8_t *qabsmax,
                                    float *c2, float *absmax, void *stream);
 

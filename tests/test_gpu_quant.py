@@ -17,15 +17,18 @@ q = pytest.importorskip("bit_nf4_quantized_blockwise_amd")
 
 
 def _gpu_all(flat):
-    """Both GPU routes: separate calls and the fused one (must agree bytewise)."""
+    """Every GPU route: separate calls, the combined entry point with the scales
+    kept (two launches) and without them (one pass) — all must agree bytewise."""
     w = to_dev(flat)
     packed, absmax = q.quantize_nf4(w)
     qa, c2 = q.double_quant(absmax)
     fp, fq, fc2, fabs = q.quantize_nf4_dq(w, want_absmax=True)
+    op, oq, oc2 = q.quantize_nf4_dq(w, one_pass=True)
     torch.cuda.synchronize()
-    assert np.array_equal(u8(packed), u8(fp))
-    assert np.array_equal(u8(qa), u8(fq))
-    assert np.array_equal(f32_bits(c2), f32_bits(fc2))
+    for p_, q_, c_ in ((fp, fq, fc2), (op, oq, oc2)):
+        assert np.array_equal(u8(packed), u8(p_))
+        assert np.array_equal(u8(qa), u8(q_))
+        assert np.array_equal(f32_bits(c2), f32_bits(c_))
     assert np.array_equal(f32_bits(absmax), f32_bits(fabs))
     return packed, absmax, qa, c2
 
