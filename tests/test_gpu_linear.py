@@ -77,6 +77,9 @@ def _run_case(M, K, N, r, alpha, seed, bwd=True):
     (12, 4096, 40, 16, 32.0),     # few tokens in two groups of 8, U formed in the kernel
     (6, 4096, 40, 32, 16.0),      # few tokens, rank too large to form U in the kernel
     (2, 1088, 48, 8, 16.0),       # few tokens, byte-wise scale codes, k split in two
+    (256, 512, 264, 256, 16.0),   # largest rank, many-token path
+    (40, 256, 96, 256, 64.0),     # largest rank, split-K path
+    (3, 512, 64, 256, 16.0),      # largest rank, few-token path
 ])
 def test_small_shapes(M, K, N, r, alpha):
     _run_case(M, K, N, r, alpha, seed=M + K + N + r)

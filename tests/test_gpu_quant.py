@@ -170,3 +170,35 @@ def test_llama7b_last_layer_sampled_groups():
             assert np.array_equal(qq[e0 // 64:e0 // 64 + o["q"].size], o["q"])
             assert np.array_equal(cc[o["g0"]:o["g1"]], o["c2"].view(np.uint32))
             assert np.array_equal(ww[int(r0):int(r0) + 8], o["w_hat"])
+
+
+def test_weight_beyond_two_to_the_31_elements():
+    """524,290 x 4096 float32 (2^31 + 8192 weights, 8.6 GB): 64-bit indexing in
+    the quantisers and the dequantiser.  Whole DQ groups (independent of the
+    rest) at the 2^31 boundary and at the end are checked against the oracle;
+    both quantiser routes must give the same bytes everywhere."""
+    n_out, k_in = (1 << 31) // 4096 + 2, 4096
+    n = n_out * k_in
+    say(f"[quant] {n_out} x {k_in} = {n} weights")
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    W = torch.randn(n_out, k_in, generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    W.view(-1)[n - 64:] = 0.0                      # an all-zero last block
+    packed, qa, c2, absmax = q.quantize_nf4_dq(W, want_absmax=True)
+    p1, q1, c21 = q.quantize_nf4_dq(W, one_pass=True)
+    assert torch.equal(packed, p1) and torch.equal(qa, q1) and torch.equal(c2.view(torch.int32),
+                                                                         c21.view(torch.int32))
+    del p1, q1, c21
+    out = q.dequantize_nf4(q.NF4Tensor(packed, qa, c2, n_out, k_in))
+    G = 64 * 256
+    ngroups = n // G
+    for g in (0, (1 << 31) // G - 1, (1 << 31) // G, ngroups - 1):
+        s0, s1 = g * G, (g + 1) * G
+        flat = host(W.view(-1)[s0:s1]).numpy()
+        op, oa = quantize_nf4(flat)
+        oq, oc2 = double_quant(oa)
+        assert np.array_equal(u8(packed[s0 // 2:s1 // 2]), op), g
+        assert np.array_equal(u8(qa[s0 // 64:s1 // 64]).view(np.int8), oq), g
+        assert f32_bits(c2[g:g + 1])[0] == oc2.view(np.uint32)[0], g
+        assert np.array_equal(f32_bits(absmax[s0 // 64:s1 // 64]), oa.view(np.uint32)), g
+        ref = dequantize_nf4(op, oq, oc2, G)
+        assert np.array_equal(bf16_bits(out.view(-1)[s0:s1]), ref), g
