@@ -459,16 +459,22 @@ def adamw_row(dev):
     lst = q.AdamWList(list(P), list(G), list(Mo), list(V), list(PB))
     ws = torch.empty(q.adamw_workspace_size(n_t), dtype=torch.uint8, device=dev)
     norm = torch.empty(1, dtype=torch.float32, device=dev)
+    plan = q.AdamWPlan(list(P), list(G), list(Mo), list(V), list(PB))
     it = [1]
 
-    def step():
+    def step_plan():  # the prepared list: one launch per pass
+        q.adamw_step_plan(plan, it[0], grad_norm=norm)
+        it[0] += 1
+
+    def step_list():  # descriptors in the kernel arguments, 48 tensors per launch
         q.adamw_step_list(lst, it[0], grad_norm=norm, workspace=ws)
         it[0] += 1
-    ms = _time_ms(step, 20, warmup=3)
+    ms = _time_ms(step_plan, 20, warmup=5)
+    ms_list = _time_ms(step_list, 20, warmup=5)
     nparam = n_t * size
     nbytes = 34 * nparam
     return dict(tensors=n_t, params=nparam, ms=ms, GBps=nbytes / ms / 1e6,
-                hbm_frac=nbytes / ms / 1e6 / HBM_PEAK_GBS)
+                hbm_frac=nbytes / ms / 1e6 / HBM_PEAK_GBS, ms_unprepared_list=ms_list)
 
 
 def variant_rows(W):

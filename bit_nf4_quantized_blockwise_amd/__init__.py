@@ -53,6 +53,10 @@ class AdamWTensor(ctypes.Structure):
     ]
 
 
+class AdamWPlanC(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int32), ("chunks", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -74,6 +78,12 @@ _SIGNATURES = {
     "qlora_adamw_step": ([ctypes.POINTER(AdamWTensor), _I32, _F, _F, _F, _F, _F, _I64, _F, _P, _P,
                           _SZ, _P], _I32),
     "qlora_adamw_workspace_size": ([_I32], _SZ),
+    "qlora_adamw_plan_size": ([ctypes.POINTER(AdamWTensor), _I32], _SZ),
+    "qlora_adamw_plan_init": ([ctypes.POINTER(AdamWTensor), _I32, _P, _SZ,
+                               ctypes.POINTER(AdamWPlanC), _P], _I32),
+    "qlora_adamw_plan_workspace_size": ([ctypes.POINTER(AdamWPlanC)], _SZ),
+    "qlora_adamw_step_plan": ([ctypes.POINTER(AdamWPlanC), _F, _F, _F, _F, _F, _I64, _F, _P, _P,
+                               _SZ, _P], _I32),
     "qlora_lora_dropout": ([_P, _I64, _I64, _F, _U64, _U64, _P, _P], _I32),
     "qlora_linear_fwd_dropout": ([_W, _P, _I64, _P, _P, _I32, _F, _F, _U64, _U64, _P, _P, _P, _P,
                                   _SZ, _P], _I32),
@@ -439,6 +449,35 @@ def adamw_step_list(lst, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight
                                   max_grad_norm, _ptr(grad_norm), _ptr(workspace),
                                   workspace.numel(), _stream(lst.device)),
            "qlora_adamw_step")
+
+
+class AdamWPlan:
+    """An AdamW tensor list prepared once in device memory (one launch per pass
+    for any number of tensors).  Keeps the tensors and its device buffer."""
+
+    def __init__(self, params, grads, ms, vs, params_bf16=None):
+        lst = AdamWList(params, grads, ms, vs, params_bf16)
+        n = lst.count
+        nbytes = lib().qlora_adamw_plan_size(lst.arr, n)
+        if nbytes == 0:
+            raise ValueError("invalid tensor list")
+        self.device = lst.device
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.c = AdamWPlanC()
+        _check(lib().qlora_adamw_plan_init(lst.arr, n, _ptr(self.buf), nbytes, ctypes.byref(self.c),
+                                           _stream(self.device)), "qlora_adamw_plan_init")
+        self._list = lst  # keeps the tensors alive
+        self.workspace = torch.empty(lib().qlora_adamw_plan_workspace_size(ctypes.byref(self.c)),
+                                     dtype=torch.uint8, device=self.device)
+
+
+def adamw_step_plan(plan, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.001,
+                    max_grad_norm=0.3, grad_norm=None):
+    """adamw_step over an AdamWPlan."""
+    _check(lib().qlora_adamw_step_plan(ctypes.byref(plan.c), lr, beta1, beta2, eps, weight_decay,
+                                       step, max_grad_norm, _ptr(grad_norm), _ptr(plan.workspace),
+                                       plan.workspace.numel(), _stream(plan.device)),
+           "qlora_adamw_step_plan")
 
 
 def adamw_step(params, grads, ms, vs, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8,

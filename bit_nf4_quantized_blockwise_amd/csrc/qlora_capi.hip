@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "qlora_kernels.h"
 #include "qlora_optim.h"
@@ -582,6 +583,56 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
 }
 
 
+// AdamW arguments shared by both step entry points.
+qlora_status validate_adamw_tensors(const qlora_adamw_tensor* t, int32_t count) {
+  QCHECK(count >= 0, QLORA_ERR_SHAPE);
+  QCHECK(count == 0 || t != nullptr, QLORA_ERR_NULL);
+  for (int32_t i = 0; i < count; ++i) {
+    QCHECK(t[i].n >= 0, QLORA_ERR_SHAPE);
+    if (t[i].n == 0) continue;
+    QCHECK(t[i].param && t[i].grad && t[i].m && t[i].v, QLORA_ERR_NULL);
+    QCHECK(aligned16(t[i].param) && aligned16(t[i].grad) && aligned16(t[i].m) && aligned16(t[i].v),
+           QLORA_ERR_ALIGN);
+    QCHECK(t[i].param_bf16 == nullptr || aligned16(t[i].param_bf16), QLORA_ERR_ALIGN);
+  }
+  return QLORA_OK;
+}
+
+qlora_status validate_adamw_hyper(float lr, float beta1, float beta2, float eps,
+                                  float weight_decay, int64_t step, float max_grad_norm,
+                                  const float* grad_norm) {
+  QCHECK(step >= 1, QLORA_ERR_SHAPE);
+  QCHECK(std::isfinite(lr) && lr >= 0.0f && std::isfinite(weight_decay) && weight_decay >= 0.0f,
+         QLORA_ERR_UNSUPPORTED);
+  QCHECK(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f, QLORA_ERR_UNSUPPORTED);
+  QCHECK(std::isfinite(eps) && eps > 0.0f && std::isfinite(max_grad_norm), QLORA_ERR_UNSUPPORTED);
+  QCHECK(grad_norm == nullptr || aligned16(grad_norm), QLORA_ERR_ALIGN);
+  return QLORA_OK;
+}
+
+// Step size and bias corrections in float64 on the host, rounded once.
+AdamHyper adamw_hyper(float lr, float beta1, float beta2, float eps, float weight_decay,
+                      int64_t step) {
+  AdamHyper h{};
+  h.beta1 = beta1;
+  h.beta2 = beta2;
+  h.eps = eps;
+  h.decay = (float)(1.0 - (double)lr * (double)weight_decay);
+  h.step_size = (float)((double)lr / (1.0 - std::pow((double)beta1, (double)step)));
+  h.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow((double)beta2, (double)step)));
+  return h;
+}
+
+// Prepared list layout: the descriptors, then (from a 256-byte boundary) the
+// chunk map.
+size_t plan_tmap_offset(int32_t count) { return align256((size_t)count * sizeof(AdamTensor)); }
+
+int64_t plan_chunks(const qlora_adamw_tensor* t, int32_t count) {
+  int64_t c = 0;
+  for (int32_t i = 0; i < count; ++i) c += ceil_div(t[i].n, kAdamChunk);
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1004,39 +1055,22 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor* t, int32_t count, float 
                               float beta2, float eps, float weight_decay, int64_t step,
                               float max_grad_norm, float* grad_norm, void* workspace,
                               size_t ws_bytes, void* stream) {
-  QCHECK(count >= 0 && step >= 1, QLORA_ERR_SHAPE);
-  QCHECK(count == 0 || t != nullptr, QLORA_ERR_NULL);
-  QCHECK(std::isfinite(lr) && lr >= 0.0f && std::isfinite(weight_decay) && weight_decay >= 0.0f,
-         QLORA_ERR_UNSUPPORTED);
-  QCHECK(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f, QLORA_ERR_UNSUPPORTED);
-  QCHECK(std::isfinite(eps) && eps > 0.0f && std::isfinite(max_grad_norm), QLORA_ERR_UNSUPPORTED);
-  for (int32_t i = 0; i < count; ++i) {
-    QCHECK(t[i].n >= 0, QLORA_ERR_SHAPE);
-    if (t[i].n == 0) continue;
-    QCHECK(t[i].param && t[i].grad && t[i].m && t[i].v, QLORA_ERR_NULL);
-    QCHECK(aligned16(t[i].param) && aligned16(t[i].grad) && aligned16(t[i].m) && aligned16(t[i].v),
-           QLORA_ERR_ALIGN);
-    QCHECK(t[i].param_bf16 == nullptr || aligned16(t[i].param_bf16), QLORA_ERR_ALIGN);
-  }
-  QCHECK(grad_norm == nullptr || aligned16(grad_norm), QLORA_ERR_ALIGN);
+  qlora_status s = validate_adamw_tensors(t, count);
+  if (s != QLORA_OK) return s;
+  if ((s = validate_adamw_hyper(lr, beta1, beta2, eps, weight_decay, step, max_grad_norm,
+                                grad_norm)) != QLORA_OK)
+    return s;
   const bool clip = max_grad_norm > 0.0f;
   const bool need_norm = clip || grad_norm != nullptr;
   if (need_norm)
     QCHECK(workspace != nullptr && aligned16(workspace) &&
                ws_bytes >= qlora_adamw_workspace_size(count),
            QLORA_ERR_WORKSPACE);
-  qlora_status s = check_device();
+  s = check_device();
   if (s != QLORA_OK) return s;
   if (count == 0) return QLORA_OK;
   hipStream_t st = as_stream(stream);
-
-  AdamHyper h{};
-  h.beta1 = beta1;
-  h.beta2 = beta2;
-  h.eps = eps;
-  h.decay = (float)(1.0 - (double)lr * (double)weight_decay);
-  h.step_size = (float)((double)lr / (1.0 - std::pow((double)beta1, (double)step)));
-  h.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow((double)beta2, (double)step)));
+  const AdamHyper h = adamw_hyper(lr, beta1, beta2, eps, weight_decay, step);
 
   // Groups of kAdamMaxTensors tensors, each one list per launch.
   const int groups = (int)ceil_div(count, kAdamMaxTensors);
@@ -1077,6 +1111,102 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor* t, int32_t count, float 
     hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kAdamThreads), 0, st, L, h,
                        clip ? coef : nullptr);
   }
+  return launched();
+}
+
+size_t qlora_adamw_plan_size(const qlora_adamw_tensor* tensors, int32_t count) {
+  if (count < 0 || (count > 0 && tensors == nullptr)) return 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (tensors[i].n < 0) return 0;
+  return std::max<size_t>(256, plan_tmap_offset(count) +
+                                   align256((size_t)plan_chunks(tensors, count) * 4));
+}
+
+qlora_status qlora_adamw_plan_init(const qlora_adamw_tensor* tensors, int32_t count, void* device,
+                                   size_t bytes, qlora_adamw_plan* plan, void* stream) {
+  qlora_status s = validate_adamw_tensors(tensors, count);
+  if (s != QLORA_OK) return s;
+  QCHECK(plan != nullptr, QLORA_ERR_NULL);
+  QCHECK(device != nullptr && aligned16(device) && bytes >= qlora_adamw_plan_size(tensors, count),
+         QLORA_ERR_WORKSPACE);
+  const int64_t chunks = plan_chunks(tensors, count);
+  QCHECK(chunks <= 0x7fffffff, QLORA_ERR_SHAPE);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  const size_t toff = plan_tmap_offset(count);
+  std::vector<char> host(toff + (size_t)chunks * 4, 0);
+  AdamTensor* d = reinterpret_cast<AdamTensor*>(host.data());
+  int32_t* tmap = reinterpret_cast<int32_t*>(host.data() + toff);
+  int64_t c = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_adamw_tensor& x = tensors[i];
+    d[i] = AdamTensor{x.param, x.grad, x.m, x.v, x.param_bf16, x.n, c};
+    const int64_t ci = ceil_div(x.n, kAdamChunk);
+    for (int64_t k = 0; k < ci; ++k) tmap[c + k] = i;
+    c += ci;
+  }
+  hipStream_t st = as_stream(stream);
+  if (!host.empty()) {
+    if (hipMemcpyAsync(device, host.data(), host.size(), hipMemcpyHostToDevice, st) != hipSuccess)
+      return QLORA_ERR_LAUNCH;
+    // the host copy lives only for this call
+    if (hipStreamSynchronize(st) != hipSuccess) return QLORA_ERR_LAUNCH;
+  }
+  plan->device = device;
+  plan->count = count;
+  plan->chunks = chunks;
+  return QLORA_OK;
+}
+
+size_t qlora_adamw_plan_workspace_size(const qlora_adamw_plan* plan) {
+  if (plan == nullptr || plan->chunks < 0) return 0;
+  return kAdamPartialsOffset +
+         (size_t)std::max<int64_t>(1, std::min<int64_t>(plan->chunks, kAdamPlanNormWgs)) *
+             sizeof(double);
+}
+
+qlora_status qlora_adamw_step_plan(const qlora_adamw_plan* plan, float lr, float beta1,
+                                   float beta2, float eps, float weight_decay, int64_t step,
+                                   float max_grad_norm, float* grad_norm, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  QCHECK(plan != nullptr, QLORA_ERR_NULL);
+  QCHECK(plan->count >= 0 && plan->chunks >= 0, QLORA_ERR_SHAPE);
+  QCHECK(plan->chunks == 0 || plan->device != nullptr, QLORA_ERR_NULL);
+  qlora_status s = validate_adamw_hyper(lr, beta1, beta2, eps, weight_decay, step, max_grad_norm,
+                                        grad_norm);
+  if (s != QLORA_OK) return s;
+  const bool clip = max_grad_norm > 0.0f;
+  const bool need_norm = clip || grad_norm != nullptr;
+  if (need_norm)
+    QCHECK(workspace != nullptr && aligned16(workspace) &&
+               ws_bytes >= qlora_adamw_plan_workspace_size(plan),
+           QLORA_ERR_WORKSPACE);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = as_stream(stream);
+  const AdamHyper h = adamw_hyper(lr, beta1, beta2, eps, weight_decay, step);
+  AdamPlanDev P{};
+  P.t = static_cast<const AdamTensor*>(plan->device);
+  P.tmap = reinterpret_cast<const int32_t*>(static_cast<const char*>(plan->device) +
+                                            plan_tmap_offset(plan->count));
+  P.chunks = plan->chunks;
+  float* coef = static_cast<float*>(workspace);
+  if (need_norm) {
+    double* partials =
+        reinterpret_cast<double*>(static_cast<char*>(workspace) + kAdamPartialsOffset);
+    int32_t npart = 0;
+    if (P.chunks > 0) {
+      npart = (int32_t)std::min<int64_t>(P.chunks, kAdamPlanNormWgs);
+      hipLaunchKernelGGL(adam_sqnorm_plan_kernel, dim3(npart), dim3(kAdamThreads), 0, st, P,
+                         partials);
+    }
+    hipLaunchKernelGGL(adam_clip_kernel, dim3(1), dim3(kAdamThreads), 0, st, partials, npart,
+                       max_grad_norm, clip ? 1 : 0, coef, grad_norm);
+    if ((s = launched()) != QLORA_OK) return s;
+  }
+  if (P.chunks == 0) return QLORA_OK;
+  hipLaunchKernelGGL(adam_update_plan_kernel, dim3((unsigned)std::min<int64_t>(P.chunks, kAdamMaxGrid)),
+                     dim3(kAdamThreads), 0, st, P, h, clip ? coef : nullptr);
   return launched();
 }
 

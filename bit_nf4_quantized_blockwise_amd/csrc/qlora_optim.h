@@ -33,6 +33,15 @@ struct AdamHyper {
   float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
 };
 
+// A prepared list in device memory: the descriptors (c0 as above, over all
+// tensors) and the tensor index of every chunk.
+constexpr int kAdamPlanNormWgs = 8192;  // most workgroups of the norm launch over a prepared list
+struct AdamPlanDev {
+  const AdamTensor* t;
+  const int32_t* tmap;
+  int64_t chunks;
+};
+
 // partials[blockIdx.x] = Σ g² over the chunks this workgroup visits (float64)
 __global__ void adam_sqnorm_kernel(AdamList L, double* partials);
 // One workgroup: norm = sqrt(Σ partials) in a fixed order; *coef = min(1, max_norm/(norm+1e-6))
@@ -41,5 +50,8 @@ __global__ void adam_clip_kernel(const double* partials, int32_t npart, float ma
                                  int32_t clip, float* coef, float* norm_out);
 // The step; coef == nullptr means no clipping.
 __global__ void adam_update_kernel(AdamList L, AdamHyper h, const float* coef);
+// The same two passes over a prepared list.
+__global__ void adam_sqnorm_plan_kernel(AdamPlanDev P, double* partials);
+__global__ void adam_update_plan_kernel(AdamPlanDev P, AdamHyper h, const float* coef);
 
 }  // namespace qlora

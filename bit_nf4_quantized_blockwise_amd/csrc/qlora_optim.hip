@@ -39,6 +39,20 @@ __device__ inline int chunk_tensor(const AdamList& L, int64_t c) {
   return lo;
 }
 
+// Where a launch finds its tensors: the list in the kernel arguments (tensor of
+// a chunk by binary search), or a prepared list in device memory (tensor of a
+// chunk from the chunk map: one scalar load).
+struct ArgSrc {
+  const AdamList& L;
+  __device__ inline int64_t chunks() const { return L.chunks; }
+  __device__ inline const AdamTensor& tensor(int64_t c) const { return L.t[chunk_tensor(L, c)]; }
+};
+struct PlanSrc {
+  const AdamPlanDev& P;
+  __device__ inline int64_t chunks() const { return P.chunks; }
+  __device__ inline const AdamTensor& tensor(int64_t c) const { return P.t[P.tmap[c]]; }
+};
+
 __device__ inline double sq4(const floatx4& g) {
   double a = 0.0;
 #pragma unroll
@@ -48,11 +62,12 @@ __device__ inline double sq4(const floatx4& g) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kAdamThreads) void adam_sqnorm_kernel(AdamList L, double* partials) {
+template <class Src>
+__device__ inline void sqnorm_body(const Src& S, double* partials) {
   __shared__ double sh[kAdamThreads];
   double acc = 0.0;
-  for (int64_t c = blockIdx.x; c < L.chunks; c += gridDim.x) {
-    const AdamTensor& T = L.t[chunk_tensor(L, c)];
+  for (int64_t c = blockIdx.x; c < S.chunks(); c += gridDim.x) {
+    const AdamTensor& T = S.tensor(c);
     const int64_t base = (c - T.c0) * kAdamChunk;
     if (base + kAdamChunk <= T.n) {
       floatx4 g[kAdamUnroll];
@@ -77,6 +92,15 @@ __global__ __launch_bounds__(kAdamThreads) void adam_sqnorm_kernel(AdamList L, d
   if (threadIdx.x == 0) partials[blockIdx.x] = s;
 }
 
+__global__ __launch_bounds__(kAdamThreads) void adam_sqnorm_kernel(AdamList L, double* partials) {
+  sqnorm_body(ArgSrc{L}, partials);
+}
+
+__global__ __launch_bounds__(kAdamThreads) void adam_sqnorm_plan_kernel(AdamPlanDev P,
+                                                                        double* partials) {
+  sqnorm_body(PlanSrc{P}, partials);
+}
+
 __global__ __launch_bounds__(kAdamThreads) void adam_clip_kernel(const double* partials,
                                                                  int32_t npart, float max_norm,
                                                                  int32_t clip, float* coef,
@@ -89,8 +113,8 @@ __global__ __launch_bounds__(kAdamThreads) void adam_clip_kernel(const double* p
   }
 }
 
-__global__ __launch_bounds__(kAdamThreads) void adam_update_kernel(AdamList L, AdamHyper h,
-                                                                   const float* coef_p) {
+template <class Src>
+__device__ inline void update_body(const Src& S, const AdamHyper& h, const float* coef_p) {
   const float coef = coef_p ? *coef_p : 1.0f;
   const float b1 = h.beta1, b2 = h.beta2, c1 = 1.0f - h.beta1, c2 = 1.0f - h.beta2;
   auto one = [&](float& p, float g, float& m, float& v) {
@@ -118,8 +142,8 @@ __global__ __launch_bounds__(kAdamThreads) void adam_update_kernel(AdamList L, A
     if (T.pb)
       *reinterpret_cast<u32x2*>(T.pb + i) = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
   };
-  for (int64_t c = blockIdx.x; c < L.chunks; c += gridDim.x) {
-    const AdamTensor& T = L.t[chunk_tensor(L, c)];
+  for (int64_t c = blockIdx.x; c < S.chunks(); c += gridDim.x) {
+    const AdamTensor& T = S.tensor(c);
     const int64_t base = (c - T.c0) * kAdamChunk;
     if (base + kAdamChunk <= T.n) {
       floatx4 p[kAdamUnroll], g[kAdamUnroll], m[kAdamUnroll], v[kAdamUnroll];
@@ -167,6 +191,16 @@ __global__ __launch_bounds__(kAdamThreads) void adam_update_kernel(AdamList L, A
       }
     }
   }
+}
+
+__global__ __launch_bounds__(kAdamThreads) void adam_update_kernel(AdamList L, AdamHyper h,
+                                                                   const float* coef_p) {
+  update_body(ArgSrc{L}, h, coef_p);
+}
+
+__global__ __launch_bounds__(kAdamThreads) void adam_update_plan_kernel(AdamPlanDev P, AdamHyper h,
+                                                                        const float* coef_p) {
+  update_body(PlanSrc{P}, h, coef_p);
 }
 
 }  // namespace qlora

@@ -282,6 +282,41 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor *tensors /* host array */
 /* Bytes of workspace qlora_adamw_step needs for `count` tensors (0 if count < 0). */
 size_t qlora_adamw_workspace_size(int32_t count);
 
+/* A prepared tensor list for a training loop that steps the same tensors
+ * every iteration: the descriptors and a chunk -> tensor map copied once into
+ * a caller-owned device buffer, so that a step is one norm pass, one clip and
+ * one update launch over all tensors whatever their number (qlora_adamw_step
+ * takes 48 tensors per launch), with nothing marshalled per tensor. */
+typedef struct {
+  void *device;   /* the prepared list (caller-owned device memory) */
+  int32_t count;  /* tensors */
+  int64_t chunks; /* 2048-element chunks over all tensors */
+} qlora_adamw_plan;
+
+/* Device bytes of the prepared list of these tensors (0 if invalid). */
+size_t qlora_adamw_plan_size(const qlora_adamw_tensor *tensors /* host array */, int32_t count);
+
+/* Validates the tensors as qlora_adamw_step does and writes the prepared list
+ * into `device` (at least qlora_adamw_plan_size bytes, else
+ * QLORA_ERR_WORKSPACE); fills *plan (host).  Copies from host memory and
+ * synchronises `stream` before returning: call it once, outside graph
+ * capture.  The tensors' memory must stay where it is while the plan is used. */
+qlora_status qlora_adamw_plan_init(const qlora_adamw_tensor *tensors /* host array */,
+                                   int32_t count, void *device, size_t bytes,
+                                   qlora_adamw_plan *plan /* host out */, void *stream);
+
+/* Bytes of workspace qlora_adamw_step_plan needs (0 if plan is NULL). */
+size_t qlora_adamw_plan_workspace_size(const qlora_adamw_plan *plan /* host */);
+
+/* One AdamW step over a prepared list: the same arithmetic, arguments and
+ * errors as qlora_adamw_step (the norm's float64 partial sums are grouped
+ * differently, so the last bits of the norm and of a clipped step may differ
+ * from it; each path repeats its own bits exactly). */
+qlora_status qlora_adamw_step_plan(const qlora_adamw_plan *plan /* host */, float lr, float beta1,
+                                   float beta2, float eps, float weight_decay, int64_t step,
+                                   float max_grad_norm, float *grad_norm, void *workspace,
+                                   size_t ws_bytes, void *stream);
+
 /* Bytes of device workspace needed by op 0 (forward, also qlora_lora_down,
  * qlora_nf4_matmul_fwd and qlora_linear_fwd_dropout), op 1 (backward) or op 2
  * (qlora_linear_bwd_dropout).  Returns 0 for an invalid op. */

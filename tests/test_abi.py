@@ -209,3 +209,31 @@ def test_merge_argument_errors(L):
     assert m(FAKE, None, 64, 128, FAKE, FAKE, 8, 16.0, None, None, None, None, None) == NULL
     assert m(FAKE, None, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, FAKE, MIS, FAKE, None) == ALIGN
     assert m(FAKE, None, 0, 128, FAKE, FAKE, 8, 16.0, None, None, None, None, None) == OK
+
+
+def test_adamw_plan_argument_errors(L):
+    T = q.AdamWTensor
+    good = T(FAKE, FAKE, FAKE, FAKE, None, 5000)
+    arr = (T * 2)(good, good)
+    assert L.qlora_adamw_plan_size(arr, 2) >= 2 * 56 + 4 * 2 * 3
+    assert L.qlora_adamw_plan_size(arr, -1) == 0
+    bad = (T * 1)(T(FAKE, FAKE, FAKE, FAKE, None, -3))
+    assert L.qlora_adamw_plan_size(bad, 1) == 0
+    plan = q.AdamWPlanC()
+    init = L.qlora_adamw_plan_init
+    assert init(arr, 2, FAKE, 8, ctypes.byref(plan), None) == WS
+    assert init(arr, 2, None, 1 << 20, ctypes.byref(plan), None) == WS
+    assert init(arr, 2, FAKE, 1 << 20, None, None) == NULL
+    mis = (T * 1)(T(MIS, FAKE, FAKE, FAKE, None, 8))
+    assert init(mis, 1, FAKE, 1 << 20, ctypes.byref(plan), None) == ALIGN
+    step = L.qlora_adamw_step_plan
+    p = q.AdamWPlanC(FAKE, 2, 5)
+    assert L.qlora_adamw_plan_workspace_size(ctypes.byref(p)) >= 256 + 8 * 5
+    assert step(None, 2e-4, 0.9, 0.999, 1e-8, 0.0, 1, 0.3, None, FAKE, 1 << 20, None) == NULL
+    assert step(ctypes.byref(p), 2e-4, 0.9, 0.999, 1e-8, 0.0, 0, 0.3, None, FAKE, 1 << 20,
+                None) == SHAPE
+    assert step(ctypes.byref(p), 2e-4, 1.0, 0.999, 1e-8, 0.0, 1, 0.3, None, FAKE, 1 << 20,
+                None) == UNSUP
+    assert step(ctypes.byref(p), 2e-4, 0.9, 0.999, 1e-8, 0.0, 1, 0.3, None, FAKE, 8, None) == WS
+    assert step(ctypes.byref(q.AdamWPlanC(None, 2, 5)), 2e-4, 0.9, 0.999, 1e-8, 0.0, 1, 0.0,
+                None, None, 0, None) == NULL

@@ -2,8 +2,11 @@
 
 Each step is checked on its own: the oracle (float64) starts from the GPU's
 previous float32 state, so the bound covers one step's float32 arithmetic.
-With u the update term lr/(1-β1^t) · m / (sqrt(v)/sqrt(1-β2^t) + eps):
-  |p - p_ref| <= 16·2^-24·|u_ref| + 2·2^-24·(|p_prev| + |p_ref|)
+With D = sqrt(v_ref)/sqrt(1-β2^t) + eps and
+|u| = lr/(1-β1^t) · (β1·|m_prev| + (1-β1)·|g|) / D the update term taken at
+the magnitudes of the two terms that make up m (the new m can nearly cancel,
+so its float32 rounding error is relative to those magnitudes, not to m):
+  |p - p_ref| <= 16·2^-24·|u| + 2·2^-24·(|p_prev| + |p_ref|)
   |m - m_ref| <= 4·2^-24·(β1·|m_prev| + (1-β1)·|g|)
   |v - v_ref| <= 6·2^-24·(β2·v_prev + (1-β2)·g²)
 (a few roundings each: the products, the sum, sqrt, the division, and the
@@ -50,26 +53,33 @@ def _np(t):
     return host(t).numpy()
 
 
-def _run(sizes, steps, lr=2e-4, wd=0.001, max_norm=0.3, seed=0, step0=0):
+def _run(sizes, steps, lr=2e-4, wd=0.001, max_norm=0.3, seed=0, step0=0, plan=False):
     rng = np.random.default_rng(seed)
     dev = torch.device("cuda:0")
     st = [_state(rng, n, step0) for n in sizes]
     P = [torch.from_numpy(s[0].copy()).to(dev) for s in st]
     M = [torch.from_numpy(s[2].copy()).to(dev) for s in st]
     V = [torch.from_numpy(s[3].copy()).to(dev) for s in st]
+    G = [torch.empty(n, dtype=torch.float32, device=dev) for n in sizes]
     PB = [torch.empty(n, dtype=torch.bfloat16, device=dev) if i % 2 == 0 else None
           for i, n in enumerate(sizes)]
     norm_t = torch.zeros(4, dtype=torch.float32, device=dev)
+    pl = q.AdamWPlan(P, G, M, V, PB) if plan else None
     for k, step in enumerate(steps):
         grads = [(rng.standard_normal(n) * (0.1 + i)).astype(np.float32)
                  for i, n in enumerate(sizes)]
-        G = [torch.from_numpy(g).to(dev) for g in grads]
+        for t, g in zip(G, grads):
+            t.copy_(torch.from_numpy(g))
         p0 = [_np(x).astype(np.float64) for x in P]
         m0 = [_np(x).astype(np.float64) for x in M]
         v0 = [_np(x).astype(np.float64) for x in V]
-        say(f"[adamw] sizes={sizes} step={step} max_norm={max_norm}")
-        q.adamw_step(P, G, M, V, step, lr=lr, weight_decay=wd, max_grad_norm=max_norm,
-                     params_bf16=PB, grad_norm=norm_t[:1])
+        say(f"[adamw] sizes={sizes} step={step} max_norm={max_norm} plan={plan}")
+        if plan:
+            q.adamw_step_plan(pl, step, lr=lr, weight_decay=wd, max_grad_norm=max_norm,
+                              grad_norm=norm_t[:1])
+        else:
+            q.adamw_step(P, G, M, V, step, lr=lr, weight_decay=wd, max_grad_norm=max_norm,
+                         params_bf16=PB, grad_norm=norm_t[:1])
         torch.cuda.synchronize()
         norm = global_grad_norm(grads)
         assert abs(float(_np(norm_t)[0]) - norm) <= 1e-6 * norm + 1e-30
@@ -79,7 +89,8 @@ def _run(sizes, steps, lr=2e-4, wd=0.001, max_norm=0.3, seed=0, step0=0):
                                     beta2=B2, eps=E, weight_decay=f32(wd), coef=coef)
             gp, gm, gv = (_np(x).astype(np.float64) for x in (P[i], M[i], V[i]))
             g = np.asarray(grads[i], np.float64) * coef
-            u = (f32(lr) / (1 - B1 ** step)) * mr / (np.sqrt(vr / (1 - B2 ** step)) + E)
+            u = ((f32(lr) / (1 - B1 ** step)) * (B1 * np.abs(m0[i]) + (1 - B1) * np.abs(g))
+                 / (np.sqrt(vr / (1 - B2 ** step)) + E))
             bp = 16 * ULP * np.abs(u) + 2 * ULP * (np.abs(p0[i]) + np.abs(pr)) + 1e-30
             worst = np.max(np.abs(gp - pr) / bp) if gp.size else 0.0
             assert worst <= 1.0, (i, worst)
@@ -91,18 +102,27 @@ def _run(sizes, steps, lr=2e-4, wd=0.001, max_norm=0.3, seed=0, step0=0):
                 assert torch.equal(PB[i].view(torch.int16), ref.view(torch.int16)), i
 
 
+@pytest.mark.parametrize("plan", [False, True])
 @pytest.mark.parametrize("max_norm", [0.3, 0.0, 1e6])
-def test_multi_tensor_steps(max_norm):
-    _run([1, 3, 4, 5, 257, 4096 * 64 + 3, 0, 11008], [1, 2, 3], max_norm=max_norm)
+def test_multi_tensor_steps(max_norm, plan):
+    _run([1, 3, 4, 5, 257, 4096 * 64 + 3, 0, 11008], [1, 2, 3], max_norm=max_norm, plan=plan)
 
 
-def test_late_step_and_existing_moments():
-    _run([64 * 4096, 11008 * 64], [1000, 1001], step0=1, seed=3)
+@pytest.mark.parametrize("plan", [False, True])
+def test_late_step_and_existing_moments(plan):
+    _run([64 * 4096, 11008 * 64], [1000, 1001], step0=1, seed=3, plan=plan)
 
 
-def test_more_tensors_than_one_launch_holds():
-    # 100 tensors: three launches share one global norm
-    _run([17 + (i * 37) % 300 for i in range(100)], [1, 2], seed=5)
+@pytest.mark.parametrize("plan", [False, True])
+def test_more_tensors_than_one_launch_holds(plan):
+    # 100 tensors: three kernel-argument launches share one global norm; one
+    # launch over the prepared list
+    _run([17 + (i * 37) % 300 for i in range(100)], [1, 2], seed=5, plan=plan)
+
+
+def test_prepared_list_of_the_page_sized_adapter_set():
+    # 256 tensors as in LLaMA-7B's attention adapters, shrunk to 4096 x 8 each
+    _run([4096 * 8] * 256, [1, 2], seed=8, plan=True)
 
 
 def test_no_decay_no_clip_repeatable():
@@ -123,4 +143,22 @@ def test_empty_list_and_zero_sizes():
     q.adamw_step([], [], [], [], 1)
     e = torch.empty(0, dtype=torch.float32, device=dev)
     q.adamw_step([e], [e], [e], [e], 1)
+    pl = q.AdamWPlan([e], [e], [e], [e])
+    norm = torch.full((1,), 7.0, device=dev)
+    q.adamw_step_plan(pl, 1, grad_norm=norm)
     torch.cuda.synchronize()
+    assert float(norm.cpu()[0]) == 0.0
+
+
+def test_prepared_list_repeatable():
+    dev = torch.device("cuda:0")
+    outs = []
+    for _ in range(2):
+        state = _state(np.random.default_rng(9), 100003, 0)
+        p, g, m, v = (torch.from_numpy(x).to(dev) for x in state)
+        pl = q.AdamWPlan([p], [g], [m], [v])
+        q.adamw_step_plan(pl, 1, lr=1e-3, max_grad_norm=0.3)
+        torch.cuda.synchronize()
+        outs.append((_np(p).view(np.uint32), _np(m).view(np.uint32), _np(v).view(np.uint32)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
