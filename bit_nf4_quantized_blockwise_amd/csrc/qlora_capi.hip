@@ -271,8 +271,8 @@ qlora_status lora_down_impl(const uint16_t* X, int64_t M, int64_t K, const uint1
                             hipStream_t st) {
   if (M == 0) return QLORA_OK;
   if (use_gemv(M)) {
-    hipLaunchKernelGGL(lora_down_small_kernel, dim3((unsigned)r), dim3(256), 0, st, X, (int)M, K,
-                       A, (int)r, U);
+    hipLaunchKernelGGL(lora_down_small_kernel, dim3((unsigned)r, (unsigned)M), dim3(kDownThreads), 0,
+                       st, X, K, A, (int)r, U);
     return launched();
   }
   GemmArgs g{};
@@ -313,18 +313,15 @@ void launch_gemv(const GemvArgs& a, dim3 grid, int groups, hipStream_t st) {
 }
 
 // Few-token forward: U (pitch r) and B (pitch r) are read as given.
-// A non-null A asks the kernel to form U = X·Aᵀ itself (see gemv_forms_u) and
-// store it in U; otherwise U is read.
 qlora_status gemv_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* U,
                        const uint16_t* B, int32_t r, float s, uint16_t* Y, char* ws,
-                       hipStream_t st, const uint16_t* A = nullptr) {
+                       hipStream_t st) {
   const int64_t N = w->n_out, K = w->k_in;
   const GemvPlan p = gemv_plan(M, N, K);
   GemvArgs a{};
   a.x = X; a.M = (int32_t)M; a.K = K; a.N = N;
   a.packed = w->packed; a.qabsmax = w->qabsmax; a.c2 = w->c2;
   a.u = U; a.r = r; a.b = B; a.s = s;
-  a.a = A; a.u_out = A ? const_cast<uint16_t*>(U) : nullptr;
   a.y = Y; a.part = reinterpret_cast<float*>(ws); a.ksplit = p.ksplit;
   const dim3 grid((unsigned)p.gx, (unsigned)p.ksplit);
   if (p.mg == 1) {
@@ -345,14 +342,6 @@ qlora_status gemv_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, 
   if (e != QLORA_OK || p.ksplit == 1) return e;
   return run_reduce(a.part, M * N, p.ksplit, M, N, M, N, N, 1.0f, ReduceOut{Y, nullptr, N, 0},
                     ReduceOut{nullptr, nullptr, 0, 0}, st);
-}
-
-// The few-token kernel forms U itself when one workgroup covers all of k
-// (no split) and the rank fits one 16-column operand group.  Every workgroup
-// then reads all of A (from L2): that costs more than a separate launch for
-// one to four tokens and less from five on.
-bool gemv_forms_u(int64_t M, int64_t N, int64_t K, int32_t r) {
-  return use_gemv(M) && M >= 5 && r <= 16 && gemv_plan(M, N, K).ksplit == 1;
 }
 
 qlora_status matmul_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M,
@@ -388,9 +377,6 @@ float scale_of(float alpha, int32_t r) { return alpha / (float)r; }
 qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* Xl,
                              int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float s,
                              uint16_t* Y, uint16_t* U, char* ws, const FwdWs& L, hipStream_t st) {
-  // the few-token kernel can form U itself, from the same tokens it multiplies
-  if (X == Xl && gemv_forms_u(M, w->n_out, w->k_in, r))
-    return gemv_impl(w, X, M, U, B, r, s, Y, ws, st, A);
   const bool pad = r % 8 != 0 && !use_gemv(M);
   uint16_t* Up = pad ? reinterpret_cast<uint16_t*>(ws + L.pad_u) : nullptr;
   qlora_status e = lora_down_impl(Xl, M, w->k_in, A, r, U, Up, L.rp, ws, L, st);

@@ -63,7 +63,6 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 64];
   __shared__ float red[kGemvWaves][G][MG][32][4];  // per-wave partial sums, reduced once at the end
   __shared__ uint16_t ush[16 * 256];         // U rows for the adapter term (M <= 16, r <= 256)
-  __shared__ float ured[kGemvWaves][MG][32][4];  // per-wave partial U when it is formed here
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
@@ -183,42 +182,6 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   for (int st = 0; st < D; ++st) load(st);  // rows past N read as zero
   load_scales(0, sA);
 
-
-  // U = X·Aᵀ (r <= 16) with the same operands: the rows of A stand in for a
-  // 16-column group of weights (already bf16, no table), each wave over its
-  // own slice of k; rows r and r + 8 of the result (the two blocks of a
-  // chunk) are folded and the waves summed at the end.
-  const bool form_u = g.a != nullptr;  // uniform
-  if (form_u) {
-    const __amdgpu_buffer_rsrc_t ar = make_rsrc(g.a, (int64_t)g.r * K * 2);
-    floatx4 ua[MG];
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg) ua[mg] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int64_t kq = (chunk0 + c) * 128 + 32 * qd;
-      u32x4 av[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        av[j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       ar, kq + 8 * j < K ? (int)(((int64_t)c16 * K + kq + 8 * j) * 2) : 0x7ffffff0, 0, 0));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int mg = 0; mg < MG; ++mg)
-          ua[mg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[mg][c][j]),
-                                                           __builtin_bit_cast(bf16x8, av[j]), ua[mg],
-                                                           0, 0, 0);
-    }
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ua[mg][i] += __shfl_xor(ua[mg][i], 32);
-        if (lane < 32) ured[w][mg][lane][i] = ua[mg][i];
-      }
-  }
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     Scales& sc = (gi & 1) ? sB : sA;
@@ -270,31 +233,30 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   // rank-r dot product reads LDS instead of issuing r dependent global loads.
   const bool lora = blockIdx.y == 0 && g.r > 0;
   uint16_t* bsh = reinterpret_cast<uint16_t*>(lut);  // [G·16][r]; r <= 256 fits the table
+  const int nb = G * 16 * g.r;  // B rows nw0 .. nw0 + 16 G are contiguous
+  const int64_t bvalid = (N - nw0) * g.r;
+  const bool bvec = (g.r & 7) == 0;  // 16-byte pieces (B is 16-byte aligned)
+  // The first piece of B and of U per lane is fetched before the barrier, so
+  // its latency overlaps the wait for the workgroup's slowest wave.
+  u32x4 b_first = u32x4{0u, 0u, 0u, 0u};
+  uint16_t u_first = 0;
+  if (lora) {
+    if (bvec && tid * 8 < nb && tid * 8 < bvalid)
+      b_first = *reinterpret_cast<const u32x4*>(g.b + nw0 * g.r + tid * 8);
+    if (tid < M * g.r) u_first = g.u[tid];
+  }
   __syncthreads();  // every wave is done with the table
   if (lora) {
-    const int nb = G * 16 * g.r;  // B rows nw0 .. nw0 + 16 G are contiguous
-    const int64_t bvalid = (N - nw0) * g.r;
-    if ((g.r & 7) == 0) {  // 16-byte pieces (B is 16-byte aligned)
-      for (int i = tid * 8; i < nb; i += NT * 8)
+    if (bvec) {
+      if (tid * 8 < nb) *reinterpret_cast<u32x4*>(bsh + tid * 8) = b_first;
+      for (int i = (tid + NT) * 8; i < nb; i += NT * 8)
         *reinterpret_cast<u32x4*>(bsh + i) =
             i < bvalid ? *reinterpret_cast<const u32x4*>(g.b + nw0 * g.r + i) : u32x4{0u, 0u, 0u, 0u};
     } else {
       for (int i = tid; i < nb; i += NT) bsh[i] = i < bvalid ? g.b[nw0 * g.r + i] : (uint16_t)0;
     }
-    if (form_u) {
-      // U[tok][j] summed over the waves in a fixed order, rounded to bf16
-      // (the stored U the backward pass reads); workgroup 0 writes it out
-      for (int i = tid; i < M * g.r; i += NT) {
-        const int tok = i / g.r, j = i % g.r, mg = tok >> 3, t8 = tok & 7;
-        float v = 0.0f;
-        for (int ww = 0; ww < kGemvWaves; ++ww) v += ured[ww][mg][j + 16 * (t8 >> 2)][t8 & 3];
-        const uint16_t ub = bf16_rne_bits(v);
-        ush[i] = ub;
-        if (blockIdx.x == 0) g.u_out[i] = ub;
-      }
-    } else {
-      for (int i = tid; i < M * g.r; i += NT) ush[i] = g.u[i];
-    }
+    if (tid < M * g.r) ush[tid] = u_first;
+    for (int i = tid + NT; i < M * g.r; i += NT) ush[i] = g.u[i];
   }
   __syncthreads();
   for (int o = tid; o < G * MG * 128; o += NT) {
@@ -321,57 +283,36 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   }
 }
 
-// U[m][j] = Σ_k X[m][k] · A[j][k] for M <= 16 tokens: one workgroup per rank
-// index j; every load issued up front, then a fixed-order reduction through
-// LDS (no shuffle chains).
-__global__ __launch_bounds__(256) void lora_down_small_kernel(const uint16_t* __restrict__ x, int M,
-                                                              int64_t K, const uint16_t* __restrict__ a,
-                                                              int r, uint16_t* __restrict__ u) {
-  __shared__ float red[16][257];
-  const int j = blockIdx.x, tid = threadIdx.x;
-  float acc[16];
+// U[m][j] = Σ_k X[m][k] · A[j][k] for few tokens: one workgroup per (j, m),
+// 1024 lanes of 8 k each per pass, so a pass over k = 8192 is one 16-byte
+// load of A and one of X per lane, all in flight together.  Each lane sums
+// its products in k order; the lanes of a wave meet in a fixed butterfly and
+// the 16 waves in wave order, so runs are bitwise repeatable.
+__global__ __launch_bounds__(kDownThreads) void lora_down_small_kernel(
+    const uint16_t* __restrict__ x, int64_t K, const uint16_t* __restrict__ a, int r,
+    uint16_t* __restrict__ u) {
+  constexpr int NW = kDownThreads / 64;
+  __shared__ float red[NW];
+  const int j = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float acc = 0.0f;
+  for (int64_t k = (int64_t)tid * 8; k < K; k += kDownThreads * 8) {
+    const u32x4 av = *reinterpret_cast<const u32x4*>(a + (int64_t)j * K + k);
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + k);
 #pragma unroll
-  for (int m = 0; m < 16; ++m) acc[m] = 0.0f;
-  for (int64_t k0 = (int64_t)tid * 8; k0 < K; k0 += 4 * 256 * 8) {
-    u32x4 av[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t k = k0 + (int64_t)s * 256 * 8;
-      av[s] = k < K ? *reinterpret_cast<const u32x4*>(a + (int64_t)j * K + k) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      if (m >= M) continue;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int64_t k = k0 + (int64_t)s * 256 * 8;
-        if (k >= K) continue;
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + k);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          acc[m] += bits_to_float(xv[d] << 16) * bits_to_float(av[s][d] << 16);
-          acc[m] += bits_to_float(xv[d] & 0xffff0000u) * bits_to_float(av[s][d] & 0xffff0000u);
-        }
-      }
+    for (int d = 0; d < 4; ++d) {
+      acc += bits_to_float(xv[d] << 16) * bits_to_float(av[d] << 16);
+      acc += bits_to_float(xv[d] & 0xffff0000u) * bits_to_float(av[d] & 0xffff0000u);
     }
   }
 #pragma unroll
-  for (int m = 0; m < 16; ++m) red[m][tid] = acc[m];
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) red[w] = acc;
   __syncthreads();
-  {  // 256 threads: (m, part) sums 16 entries
-    const int m = tid >> 4, part = tid & 15;
+  if (tid == 0) {
     float v = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v += red[m][part * 16 + i];
-    __syncthreads();
-    red[m][part] = v;
-  }
-  __syncthreads();
-  if (tid < M) {
-    float v = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v += red[tid][i];
-    u[(int64_t)tid * r + j] = bf16_rne_bits(v);
+    for (int i = 0; i < NW; ++i) v += red[i];
+    u[(int64_t)m * r + j] = bf16_rne_bits(v);
   }
 }
 

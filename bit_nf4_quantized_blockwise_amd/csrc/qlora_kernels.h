@@ -63,10 +63,7 @@ struct GemvArgs {
   const uint8_t* packed;  // W[N][K] NF4 + DQ
   const int8_t* qabsmax;
   const float* c2;
-  const uint16_t* u;  // [M][r] bf16, pitch r (read when a == nullptr)
-  const uint16_t* a;  // [r][K] bf16: when set, U = X·Aᵀ is formed in the kernel (r <= 16,
-                      // one split) and written to u_out by workgroup 0
-  uint16_t* u_out;
+  const uint16_t* u;  // [M][r] bf16, pitch r
   int32_t r;
   const uint16_t* b;  // [N][r] bf16, pitch r
   float s;
@@ -84,8 +81,9 @@ __global__ void nf4_gemv_kernel(GemvArgs g);
 
 // xd = mask ⊙ x over n / 8 blocks of 8 bf16 (LoRA dropout, see qlora_philox.h).
 __global__ void lora_dropout_kernel(const uint16_t* x, int64_t nblk, DropoutKey d, uint16_t* xd);
-__global__ void lora_down_small_kernel(const uint16_t* x, int M, int64_t K, const uint16_t* a,
-                                       int r, uint16_t* u);
+constexpr int kDownThreads = 1024;  // lanes of the few-token U = X·Aᵀ kernel
+__global__ void lora_down_small_kernel(const uint16_t* x, int64_t K, const uint16_t* a, int r,
+                                       uint16_t* u);
 
 __global__ void quantize_nf4_kernel(const float* w, int64_t n, int64_t nblocks, uint8_t* packed,
                                     float* absmax);
