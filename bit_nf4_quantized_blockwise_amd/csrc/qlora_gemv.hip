@@ -37,6 +37,10 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t byt
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
 }
 
+// Workgroup barrier that waits for this wave's LDS operations only (global
+// loads stay in flight across it).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ inline uint16_t bf16_rne_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
@@ -57,22 +61,66 @@ __device__ inline uint32_t level_bits(int i) { return level_bits_tree<0, 16>(i);
 
 template <int CPW, int MG, int G, bool QV>
 __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
+  // LDS: the codebook table (64 KB), then the per-wave partial sums (reduced
+  // once at the end), then the U rows of the adapter term.  The token
+  // staging area (the workgroup's k range of X, up to 8 tokens, loaded
+  // densely once and read back in operand order) lies over the partial sums
+  // for up to 4 tokens and over the table and the partial sums beyond, so
+  // there the table is filled after the operands have been read.
+  constexpr int NT = 64 * kGemvWaves;
+  constexpr int kLut = 256 * 64 * 4;
+  constexpr int kSpan = kGemvWaves * CPW * 128;  // k range of one workgroup
+  constexpr int kRedBytes = kGemvWaves * G * MG * 32 * 4 * 4;
+  constexpr int kStage4 = MG == 1 ? 4 * kSpan * 2 : 0;   // up to 4 tokens, after the table
+  constexpr int kStage8 = MG == 1 ? 8 * kSpan * 2 : 0;   // up to 8 tokens, from the start
+  constexpr int kRedRegion = kRedBytes > kStage4 ? (kRedBytes > kStage8 - kLut ? kRedBytes : kStage8 - kLut)
+                                                 : (kStage4 > kStage8 - kLut ? kStage4 : kStage8 - kLut);
+  __shared__ __attribute__((aligned(16))) char smem[kLut + kRedRegion];
   // byte e -> the two bf16 levels of its nibbles, 64 copies: entry e of lane
   // l at byte 256 e + 4 l, so a lookup address is one v_perm of the packed
   // dword and the lane's offset, and the 64 lanes hit 64 different banks.
-  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 64];
-  __shared__ float red[kGemvWaves][G][MG][32][4];  // per-wave partial sums, reduced once at the end
-  __shared__ uint16_t ush[16 * 256];         // U rows for the adapter term (M <= 16, r <= 256)
+  uint32_t* lut = reinterpret_cast<uint32_t*>(smem);
+  char* red_stage = smem + kLut;
+  float(*red)[G][MG][32][4] = reinterpret_cast<float(*)[G][MG][32][4]>(red_stage);
+  // U rows for the adapter term (M <= 16, r <= 256); its first 2 KB are the
+  // zeros that token-less lanes read while the staging area is in use
+  __shared__ __attribute__((aligned(16))) uint16_t ush[16 * 256];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
+  const int64_t K = g.K, N = g.N;
+  const int M = g.M;
+  const int64_t chunk0 = ((int64_t)blockIdx.y * kGemvWaves + w) * CPW;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(g.x, (int64_t)M * K * 2);
 
-  constexpr int NT = 64 * kGemvWaves;
+  // One token group (M <= 8): the workgroup's tokens come in as dense 16-byte
+  // loads (about M·CPW / 4 per lane) instead of 4·CPW mostly empty ones per
+  // wave, so the 256 workgroups put far fewer requests on the same lines of
+  // X.  The loads go out first.
+  const bool staged = MG == 1;
+  const bool early_lut = !staged || M <= 4;  // uniform
+  constexpr int kPieces = MG == 1 ? 8 * kSpan / 8 / NT : 1;  // 16-byte pieces per lane at 8 tokens
+  const int rounds = (M * (kSpan / 8) + NT - 1) / NT;      // the rounds that carry tokens
+  const int64_t kw0 = (int64_t)blockIdx.y * kSpan;
+  u32x4 xs[kPieces];
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      if (i < rounds) {
+        const int p = tid + NT * i, tok = p / (kSpan / 8);
+        const int64_t k = kw0 + (int64_t)(p % (kSpan / 8)) * 8;
+        const bool valid = tok < M && k < K;
+        xs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              xr, valid ? (int)(((int64_t)tok * K + k) * 2) : 0x7ffffff0, 0, 0));
+      }
+    }
+  }
+
   // Table fill: thread t writes entries e = t / 16 + (NT / 16) it (four
   // copies each), whose low nibble t / 16 mod 16 is fixed and whose high
   // nibble is t / 256 + (NT / 256) it; the levels come from literals.
   static_assert(NT % 256 == 0 && 256 * 16 % NT == 0, "table fill");
-  {
+  auto fill_table = [&]() {
     const uint32_t lo = bf16_rne_bits(bits_to_float(level_bits((tid >> 4) & 15)));
 #pragma unroll
     for (int it = 0; it < 256 * 16 / NT; ++it) {
@@ -80,30 +128,35 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
       const uint32_t v = lo | (hi << 16);
       *reinterpret_cast<u32x4*>(&lut[(tid + it * NT) * 4]) = u32x4{v, v, v, v};
     }
+  };
+  if (early_lut) fill_table();
+  char* stage = early_lut ? red_stage : smem;
+  if (staged) {
+    *reinterpret_cast<uint32_t*>(ush + 2 * tid) = 0u;  // NT · 4 B = 2 KB of zeros
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      if (i < rounds) *reinterpret_cast<u32x4*>(stage + (size_t)(tid + NT * i) * 16) = xs[i];
   }
-
-  const int64_t K = g.K, N = g.N;
-  const int M = g.M;
-  const int64_t chunk0 = ((int64_t)blockIdx.y * kGemvWaves + w) * CPW;
-
   __syncthreads();
 
   // Token operands for this wave's chunks, kept in registers for all columns.
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(g.x, (int64_t)M * K * 2);
+  // A lane carries token c16 mod 8 of block (c16 >= 8) and zeros elsewhere.
   u32x4 xa[MG][CPW][4];
+  if (!staged) {
 #pragma unroll
-  for (int mg = 0; mg < MG; ++mg)
+    for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
+      for (int c = 0; c < CPW; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t k = (chunk0 + c) * 128 + 32 * qd + 8 * j;
-        const int tok = (c16 & 7) + 8 * mg;
-        const bool valid = ((c16 < 8) == (qd < 2)) && tok < M && k < K;
-        xa[mg][c][j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       xr, valid ? (int)(((int64_t)tok * K + k) * 2) : 0x7ffffff0, 0, 0));
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int64_t k = (chunk0 + c) * 128 + 32 * qd + 8 * j;
+          const int tok = (c16 & 7) + 8 * mg;
+          const bool valid = ((c16 < 8) == (qd < 2)) && tok < M && k < K;
+          xa[mg][c][j] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         xr, valid ? (int)(((int64_t)tok * K + k) * 2) : 0x7ffffff0, 0, 0));
+        }
+  }
 
   const char* lutb = reinterpret_cast<const char*>(lut);
   const uint32_t lane4 = (uint32_t)lane * 4;
@@ -117,7 +170,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   // apart and one wave's loads overlap another's MFMAs.  Within a wave the
   // weight loads run one column group ahead: as soon as chunk c of group gi
   // has been turned into MFMA operands, its registers are reloaded with
-  // chunk c of group gi + 1, so eight 16-byte loads per lane stay in flight.
+  // chunk c of group gi + 1, so D 16-byte loads per lane stay in flight.
   const int64_t nw0 = cg0 * 16;  // first W row of this workgroup
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.packed + nw0 * (K >> 1), (N - nw0) * (K >> 1));
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(g.qabsmax + nw0 * blocks_per_row,
@@ -181,6 +234,27 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
 #pragma unroll
   for (int st = 0; st < D; ++st) load(st);  // rows past N read as zero
   load_scales(0, sA);
+  if (staged) {
+    // the lane's 4·CPW operand pieces are 16-byte reads at fixed offsets from
+    // one base: its token's row (wave slice, k-slot qd) or the zeros
+    const int tok = c16 & 7;
+    const bool valid = ((c16 < 8) == (qd < 2)) && tok < M;
+    const char* base = valid ? stage + ((size_t)tok * kSpan + (size_t)w * CPW * 128 + 32 * qd) * 2
+                             : reinterpret_cast<const char*>(ush) + 64 * qd;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xa[0][c][j] = *reinterpret_cast<const u32x4*>(base + c * 256 + 16 * j);
+    // the staging area becomes the partial sums (and the table): every wave
+    // has read it first (the weight loads just issued stay in flight across
+    // these barriers)
+    lds_barrier();
+    if (!early_lut) {
+      fill_table();
+      lds_barrier();
+    }
+  }
 
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
