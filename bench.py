@@ -232,6 +232,17 @@ def _c_call(fn, *args):
     return call
 
 
+def _rotate(calls):
+    """One call per invocation, cycling through `calls` (inputs that together
+    exceed the last-level cache, so each call streams from HBM)."""
+    it = [0]
+
+    def call():
+        calls[it[0] % len(calls)]()
+        it[0] += 1
+    return call
+
+
 def _time_ms(fn, iters, warmup=2):
     import torch
     for _ in range(warmup):
@@ -336,23 +347,43 @@ def main():
     rows = {}
     if not args.no_rows:
         n = K * N
-        # quantiser (fused NF4 + DQ): reads 4 B, writes 0.5 + 1/64 + 4/16384 B per weight
+        # quantiser (fused NF4 + DQ): reads 4 B, writes 0.5 + 1/64 + 4/16384 B per weight;
+        # three input copies (541 MB, over twice the 256 MB last-level cache) rotate so
+        # every call reads its weight from HBM
         qbytes = n * 4 + n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4
         L = q.lib()
         st = q._stream(dev)
-        pk_, qa_, c2_, am_ = q.quantize_nf4_dq(W, want_absmax=True)
-        ms_q = _time_ms(_c_call(L.qlora_quantize_nf4_dq, q._ptr(W), n, q._ptr(pk_), q._ptr(qa_),
-                                q._ptr(c2_), q._ptr(am_), st), 20, warmup=5)
-        # dequantiser: reads the NF4 storage, writes bf16
+        Ws = [W] + [W * (1.0 + c * 1e-3) for c in (1, 2)]
+        qouts = [q.quantize_nf4_dq(w_, want_absmax=True) for w_ in Ws]
+        qcalls = [_c_call(L.qlora_quantize_nf4_dq, q._ptr(w_), n, q._ptr(o[0]), q._ptr(o[1]),
+                          q._ptr(o[2]), q._ptr(o[3]), st) for w_, o in zip(Ws, qouts)]
+        it = [0]
+
+        def quant_next():
+            qcalls[it[0] % len(qcalls)]()
+            it[0] += 1
+        ms_q = _time_ms(quant_next, 21, warmup=6)
+        # dequantiser: reads the NF4 storage, writes bf16; five weight and output
+        # copies (565 MB) rotate likewise
         dbytes = n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4 + 2 * n
-        wd = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
-        wst = wq.c_struct()
-        ms_d = _time_ms(_c_call(L.qlora_dequantize_nf4, ctypes.byref(wst), q._ptr(wd), st), 20,
-                        warmup=5)
+        wqs = [q.NF4Tensor(o[0], o[1], o[2], N, K) for o in qouts] + \
+            [q.quantize_weight(W * (1.0 + c * 1e-3)) for c in (3, 4)]
+        del Ws, qouts
+        wds = [torch.empty(N, K, dtype=torch.bfloat16, device=dev) for _ in wqs]
+        wsts = [w_.c_struct() for w_ in wqs]
+        dcalls = [_c_call(L.qlora_dequantize_nf4, ctypes.byref(sc), q._ptr(o), st)
+                  for sc, o in zip(wsts, wds)]
+
+        def deq_next():
+            dcalls[it[0] % len(dcalls)]()
+            it[0] += 1
+        ms_d = _time_ms(deq_next, 20, warmup=5)
+        wd = wds[0]
         rows["quantize_nf4_dq"] = dict(shape=[N, K], ms=ms_q, GBps=qbytes / ms_q / 1e6,
                                        hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS)
         rows["dequantize_nf4"] = dict(shape=[N, K], ms=ms_d, GBps=dbytes / ms_d / 1e6,
                                       hbm_frac=dbytes / ms_d / 1e6 / HBM_PEAK_GBS)
+        del wqs, wds, wsts, dcalls, qcalls
         del wd
         # few-token forward, 8192 -> 28672, r = 16; 5 weight copies (> 2x the MALL)
         g = wl.GEMV_70B
@@ -401,6 +432,9 @@ def main():
         rows["adamw_step_llama7b_lora_r64"] = adamw_row(dev)
         rows.update(variant_rows(W))
         rows["merge_adapter_11008x4096_r64"] = merge_row(W, B, A, alpha)
+        rows["single_linear_4096x4096_r8_m16"] = single_linear_row(dev)
+        rows["llama65b_layer_7proj_r64_m2048"] = layer65b_row(dev, 10)
+        rows["llama7b_weight_set_224_matrices"] = weight_set_row(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -438,6 +472,174 @@ def main():
         "wall_s": wall,
     }
     print(json.dumps(out), flush=True)
+
+
+def single_linear_row(dev):
+    """A single QLoRA linear, 4096 -> 4096, r = 8, alpha = 16, 16 tokens, forward
+    only.  Algorithmic bytes: the NF4+DQ weight plus X, A, B, U and Y, once each
+    (9,048,320 B).  64 weight copies (554 MB, over twice the 256 MB last-level
+    cache) rotate, so every forward streams its weight from HBM.  Reported back
+    to back (calls marshalled once, the queue kept full) and one launch at a
+    time (the host waits for each forward)."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
+    wlc = wl.SINGLE_LINEAR
+    M, K, N, r = wlc.M, wlc.k_in, wlc.n_out, wlc.r
+    inp = wlc.inputs()
+    W = torch.from_numpy(inp["W"]).to(dev)
+    copies = [q.quantize_weight(W if c == 0 else W * (1.0 + c * 1e-4)) for c in range(64)]
+    del W
+    X, A, B = (inp[k].to(dev) for k in ("X", "A", "B"))
+    ws = torch.empty(q.workspace_size(0, M, N, K, r), dtype=torch.uint8, device=dev)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    U = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+    L, st = q.lib(), q._stream(dev)
+    structs = [w_.c_struct() for w_ in copies]
+    calls = [_c_call(L.qlora_linear_fwd, ctypes.byref(sc), q._ptr(X), M, q._ptr(A), q._ptr(B), r,
+                     ctypes.c_float(wlc.alpha), q._ptr(Y), q._ptr(U), q._ptr(ws), ws.numel(), st)
+             for sc in structs]
+    it = [0]
+
+    def fwd():
+        calls[it[0] % len(calls)]()
+        it[0] += 1
+    ms_b2b = _time_ms(fwd, 256, warmup=64)
+    single = []
+    for _ in range(32):
+        torch.cuda.synchronize()
+        s, e = _events()
+        s.record()
+        fwd()
+        e.record()
+        torch.cuda.synchronize()
+        single.append(s.elapsed_time(e))
+    single.sort()
+    ms_one = single[len(single) // 2]
+    nbytes = copies[0].nbytes + 2 * M * K + 2 * r * (K + N) + 2 * M * N + 2 * M * r
+    return dict(bytes=nbytes, us_back_to_back=ms_b2b * 1e3, GBps=nbytes / ms_b2b / 1e6,
+                hbm_frac=nbytes / ms_b2b / 1e6 / HBM_PEAK_GBS, us_one_launch=ms_one * 1e3,
+                TFLOPs=wlc.flops_fwd / (ms_b2b * 1e-3) / 1e12)
+
+
+def weight_set_row(dev):
+    """The LLaMA-7B weight set: 32 layers x (q, k, v, o 4096x4096; gate, up
+    4096 -> 11008; down 11008 -> 4096) = 224 matrices, 6,476,005,376 weights,
+    all resident in HBM.  One pass of the fused quantise + DQ over all 224
+    (4.5159 B per weight: 29.25 GB) and one pass of the dequantiser to bf16
+    (2.5159 B per weight: 16.29 GB), through the batch entry points (two and
+    one launches per 48 matrices) and, for comparison, one call per matrix.
+    The float32 inputs are drawn on the GPU
+    (seeded torch normals times 0.02, 0.1 % of positions set to +-8 sigma):
+    drawing 6.5 G values on the host would take minutes, and the time does not
+    depend on the values."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
+    L, st = q.lib(), q._stream(dev)
+    gen = torch.Generator(device=dev).manual_seed(wl.SEED + 2)
+    mats = []
+    for layer in range(wl.LLAMA7B_LAYERS):
+        for name, n_out, k_in in wl.LLAMA7B_MATRICES:
+            n = n_out * k_in
+            w = torch.randn(n, generator=gen, device=dev) * 0.02
+            pos = torch.rand(n, generator=gen, device=dev) < 1e-3
+            w[pos] = torch.where(torch.rand(n, generator=gen, device=dev)[pos] < 0.5, -0.16, 0.16)
+            del pos
+            nb = n // 64
+            mats.append(dict(
+                w=w, n=n, n_out=n_out, k_in=k_in,
+                packed=torch.empty(n // 2, dtype=torch.uint8, device=dev),
+                qa=torch.empty(nb, dtype=torch.int8, device=dev),
+                c2=torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev),
+                am=torch.empty(nb, dtype=torch.float32, device=dev),
+                out=torch.empty(n_out, k_in, dtype=torch.bfloat16, device=dev)))
+    total = sum(m["n"] for m in mats)
+    qcalls = [_c_call(L.qlora_quantize_nf4_dq, q._ptr(m["w"]), m["n"], q._ptr(m["packed"]),
+                      q._ptr(m["qa"]), q._ptr(m["c2"]), q._ptr(m["am"]), st) for m in mats]
+    structs = [q.NF4Weight(m["packed"].data_ptr(), m["qa"].data_ptr(), m["c2"].data_ptr(),
+                           m["n_out"], m["k_in"]) for m in mats]
+    dcalls = [_c_call(L.qlora_dequantize_nf4, ctypes.byref(sc), q._ptr(m["out"]), st)
+              for sc, m in zip(structs, mats)]
+
+    jobs = (q.QuantJob * len(mats))(*[q.QuantJob(m["w"].data_ptr(), m["n"], m["packed"].data_ptr(),
+                                                 m["qa"].data_ptr(), m["c2"].data_ptr(),
+                                                 m["am"].data_ptr()) for m in mats])
+    outs = (ctypes.c_void_p * len(mats))(*[m["out"].data_ptr() for m in mats])
+    wsa = (q.NF4Weight * len(mats))(*structs)
+    qbatch = _c_call(L.qlora_quantize_nf4_dq_batch, jobs, len(mats), st)
+    dbatch = _c_call(L.qlora_dequantize_nf4_batch, wsa, outs, len(mats), st)
+
+    def qpass():
+        for c in qcalls:
+            c()
+
+    def dpass():
+        for c in dcalls:
+            c()
+    ms_q = _time_ms(qbatch, 3, warmup=1)
+    ms_d = _time_ms(dbatch, 3, warmup=1)
+    ms_q1 = _time_ms(qpass, 3, warmup=1)
+    ms_d1 = _time_ms(dpass, 3, warmup=1)
+    nblk = total // 64
+    qbytes = total * 4 + total // 2 + nblk + sum(((m["n"] // 64 + 255) // 256) * 4 for m in mats)
+    dbytes = total // 2 + nblk + sum(((m["n"] // 64 + 255) // 256) * 4 for m in mats) + 2 * total
+    del mats, qcalls, dcalls, structs, jobs, outs, wsa, qbatch, dbatch
+    torch.cuda.empty_cache()
+    return dict(matrices=32 * len(wl.LLAMA7B_MATRICES), weights=total,
+                quantize_dq=dict(ms=ms_q, GB=qbytes / 1e9, GBps=qbytes / ms_q / 1e6,
+                                 hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS,
+                                 ms_one_call_per_matrix=ms_q1),
+                dequantize=dict(ms=ms_d, GB=dbytes / 1e9, GBps=dbytes / ms_d / 1e6,
+                                hbm_frac=dbytes / ms_d / 1e6 / HBM_PEAK_GBS,
+                                ms_one_call_per_matrix=ms_d1))
+
+
+def layer65b_row(dev, steps):
+    """The seven projections of one LLaMA-65B-shaped decoder layer (q, k, v, o
+    8192x8192; gate, up 8192 -> 22016; down 22016 -> 8192), r = 64, alpha = 16,
+    2048 tokens, forward + backward of each: 6,754.24 GFLOP per layer step.
+    Inputs drawn on the GPU (seeded torch normals: W x 0.02, A and B x 0.01,
+    X and dY x 1); the time does not depend on the values."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
+    gen = torch.Generator(device=dev).manual_seed(wl.SEED + 5)
+    per, total_ms, total_flops = {}, 0.0, 0
+    for wlc in wl.LLAMA65B_LAYER:
+        M, K, N, r = wlc.M, wlc.k_in, wlc.n_out, wlc.r
+        W = torch.randn(N, K, generator=gen, device=dev) * 0.02
+        wq = q.quantize_weight(W)
+        del W
+        bf = lambda *shape, s: (torch.randn(*shape, generator=gen, device=dev) * s).to(torch.bfloat16)
+        A, B, X, dY = bf(r, K, s=0.01), bf(N, r, s=0.01), bf(M, K, s=1.0), bf(M, N, s=1.0)
+        ws_f = torch.empty(q.workspace_size(0, M, N, K, r), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(q.workspace_size(1, M, N, K, r), dtype=torch.uint8, device=dev)
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        U = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+        dA = torch.empty(r, K, dtype=torch.float32, device=dev)
+        dB = torch.empty(N, r, dtype=torch.float32, device=dev)
+
+        def step():
+            q.linear_fwd(wq, X, A, B, wlc.alpha, workspace=ws_f, Y=Y, U=U)
+            q.linear_bwd(wq, X, dY, A, B, U, wlc.alpha, workspace=ws_b, dX=dX, dA=dA, dB=dB)
+        ms = _time_ms(step, steps, warmup=3)
+        flops = wlc.flops_fwd + wlc.flops_bwd
+        per[wlc.name] = dict(ms=ms, TFLOPs=flops / (ms * 1e-3) / 1e12)
+        total_ms += ms
+        total_flops += flops
+        del wq, A, B, X, dY, ws_f, ws_b, Y, U, dX, dA, dB
+    torch.cuda.empty_cache()
+    return dict(projections=per, ms=total_ms, GFLOP=total_flops / 1e9,
+                TFLOPs=total_flops / (total_ms * 1e-3) / 1e12,
+                mfma_frac=total_flops / (total_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
 
 
 def adamw_row(dev):
@@ -494,23 +696,30 @@ def variant_rows(W):
     rows, mse = {}, {}
     L = q.lib()
     st = q._stream(W.device)
-    out = torch.empty(n, dtype=torch.bfloat16, device=W.device)
+    # five weight copies (901 MB) rotate, so every timed call streams from HBM
+    Ws = [W] + [W * (1.0 + c * 1e-3) for c in (1, 2, 3, 4)]
+    outs = [torch.empty(n, dtype=torch.bfloat16, device=W.device) for _ in Ws]
     ws = torch.empty(q.quant_error_workspace_size(n), dtype=torch.uint8, device=W.device)
     sse = torch.empty(1, dtype=torch.float64, device=W.device)
     for code in ("int4", "nf4"):
-        packed, absmax = q.quantize_4bit(W, code)
         cd = q.CODES[code]
-        ms_e = _time_ms(_c_call(L.qlora_quant_sq_error, q._ptr(W), n, cd, q._ptr(packed),
-                                q._ptr(absmax), q._ptr(sse), q._ptr(ws), ws.numel(), st), 20,
-                        warmup=5)
+        qs = [q.quantize_4bit(w_, code) for w_ in Ws]
+        _c_call(L.qlora_quant_sq_error, q._ptr(W), n, cd, q._ptr(qs[0][0]), q._ptr(qs[0][1]),
+                q._ptr(sse), q._ptr(ws), ws.numel(), st)()
         mse[code] = float(sse.cpu()[0]) / n
         if code == "int4":
-            p2 = torch.empty_like(packed)
-            a2 = torch.empty_like(absmax)
-            ms_q = _time_ms(_c_call(L.qlora_quantize_4bit, q._ptr(W), n, cd, q._ptr(p2), q._ptr(a2),
-                                    st), 20, warmup=5)
-            ms_d = _time_ms(_c_call(L.qlora_dequantize_4bit, q._ptr(packed), q._ptr(absmax), n, cd,
-                                    q._ptr(out), st), 20, warmup=5)
+            ms_e = _time_ms(_rotate([
+                _c_call(L.qlora_quant_sq_error, q._ptr(w_), n, cd, q._ptr(p_), q._ptr(a_),
+                        q._ptr(sse), q._ptr(ws), ws.numel(), st) for w_, (p_, a_) in zip(Ws, qs)]),
+                20, warmup=5)
+            scratch = [(torch.empty_like(p_), torch.empty_like(a_)) for p_, a_ in qs]
+            ms_q = _time_ms(_rotate([
+                _c_call(L.qlora_quantize_4bit, q._ptr(w_), n, cd, q._ptr(p2), q._ptr(a2), st)
+                for w_, (p2, a2) in zip(Ws, scratch)]), 20, warmup=5)
+            ms_d = _time_ms(_rotate([
+                _c_call(L.qlora_dequantize_4bit, q._ptr(p_), q._ptr(a_), n, cd, q._ptr(o_), st)
+                for (p_, a_), o_ in zip(qs, outs)]), 20, warmup=5)
+            del scratch
             rows["quantize_int4_single"] = dict(shape=list(W.shape), ms=ms_q,
                                                 GBps=qbytes / ms_q / 1e6,
                                                 hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS)
@@ -520,6 +729,8 @@ def variant_rows(W):
             rows["quant_sq_error_int4"] = dict(shape=list(W.shape), ms=ms_e,
                                                GBps=ebytes / ms_e / 1e6,
                                                hbm_frac=ebytes / ms_e / 1e6 / HBM_PEAK_GBS)
+        del qs
+    del Ws, outs
     rows["nf4_vs_int4_mse"] = dict(mse_nf4=mse["nf4"], mse_int4=mse["int4"],
                                    improvement_pct=(1 - mse["nf4"] / mse["int4"]) * 100)
     return rows

@@ -32,6 +32,18 @@ class QloraError(RuntimeError):
         super().__init__(f"{where}: {STATUS.get(status, status)}")
 
 
+class QuantJob(ctypes.Structure):
+    """qlora_quant_job: one weight of a batched quantisation."""
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+        ("packed", ctypes.c_void_p),
+        ("qabsmax", ctypes.c_void_p),
+        ("c2", ctypes.c_void_p),
+        ("absmax", ctypes.c_void_p),
+    ]
+
+
 class NF4Weight(ctypes.Structure):
     _fields_ = [
         ("packed", ctypes.c_void_p),
@@ -70,6 +82,8 @@ _SIGNATURES = {
     "qlora_double_quant": ([_P, _I64, _I32, _P, _P, _P], _I32),
     "qlora_quantize_nf4_dq": ([_P, _I64, _P, _P, _P, _P, _P], _I32),
     "qlora_dequantize_nf4": ([_W, _P, _P], _I32),
+    "qlora_quantize_nf4_dq_batch": ([_P, _I32, _P], _I32),
+    "qlora_dequantize_nf4_batch": ([_P, _P, _I32, _P], _I32),
     "qlora_linear_fwd": ([_W, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P], _I32),
     "qlora_linear_bwd": ([_W, _P, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "qlora_lora_down": ([_P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P], _I32),
@@ -213,6 +227,39 @@ def quantize_weight(w):
     n_out, k_in = w.shape
     packed, q, c2 = quantize_nf4_dq(w)
     return NF4Tensor(packed, q, c2, n_out, k_in)
+
+
+def quantize_nf4_dq_batch(ws):
+    """Both levels for a list of float32 CUDA tensors in batched launches:
+    [(packed, qabsmax, c2, absmax)], the same bytes as quantize_nf4_dq on each."""
+    outs, jobs = [], (QuantJob * max(1, len(ws)))()
+    for i, w in enumerate(ws):
+        n = w.numel()
+        nb = _nblocks(n)
+        dev = w.device
+        o = (torch.empty(nb * 32, dtype=torch.uint8, device=dev),
+             torch.empty(nb, dtype=torch.int8, device=dev),
+             torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=dev),
+             torch.empty(nb, dtype=torch.float32, device=dev))
+        jobs[i] = QuantJob(_ptr(w), n, *(_ptr(t) for t in o))
+        outs.append(o)
+    if ws:
+        _check(lib().qlora_quantize_nf4_dq_batch(jobs, len(ws), _stream(ws[0].device)),
+               "qlora_quantize_nf4_dq_batch")
+    return outs
+
+
+def dequantize_nf4_batch(wqs, outs=None):
+    """bf16 decoded weights of a list of NF4Tensors in batched launches."""
+    if outs is None:
+        outs = [torch.empty(w.n_out, w.k_in, dtype=torch.bfloat16, device=w.packed.device)
+                for w in wqs]
+    structs = (NF4Weight * max(1, len(wqs)))(*[w.c_struct() for w in wqs])
+    ptrs = (ctypes.c_void_p * max(1, len(wqs)))(*[_ptr(o) for o in outs])
+    if wqs:
+        _check(lib().qlora_dequantize_nf4_batch(structs, ptrs, len(wqs), _stream(outs[0].device)),
+               "qlora_dequantize_nf4_batch")
+    return outs
 
 
 def dequantize_nf4(wq, out=None):

@@ -877,6 +877,100 @@ qlora_status qlora_dequantize_nf4(const qlora_nf4_weight* w, qlora_bf16* out, vo
   return launched();
 }
 
+qlora_status qlora_quantize_nf4_dq_batch(const qlora_quant_job* jobs, int32_t count, void* stream) {
+  QCHECK(count >= 0, QLORA_ERR_SHAPE);
+  if (count == 0) return QLORA_OK;
+  QCHECK(jobs != nullptr, QLORA_ERR_NULL);
+  // every job is checked before anything is enqueued
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_quant_job& j = jobs[i];
+    QCHECK(j.n >= 0, QLORA_ERR_SHAPE);
+    if (j.n == 0) continue;
+    ALIGNED_OR_NULL(j.w);
+    ALIGNED_OR_NULL(j.packed);
+    ALIGNED_OR_NULL(j.qabsmax);
+    ALIGNED_OR_NULL(j.c2);
+    ALIGNED_OR_NULL(j.absmax);
+    QCHECK(ceil_div(ceil_div(j.n, 64) * 4, 256) <= 0x7fffffff, QLORA_ERR_SHAPE);
+  }
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = as_stream(stream);
+  // launches of up to kBatchMax jobs: the first level of all of them, then the
+  // second level of all of them (each reads only its own job's scales)
+  int32_t i = 0;
+  while (i < count) {
+    QuantBatch qb{};
+    DqBatch db{};
+    int64_t wq = 0, wd = 0;
+    int32_t c = 0;
+    for (; i < count && c < kBatchMax; ++i) {
+      const qlora_quant_job& j = jobs[i];
+      if (j.n == 0) continue;
+      const int64_t nb = ceil_div(j.n, 64), ng = ceil_div(nb, 256), nwg = ceil_div(nb * 4, 256);
+      if (wq + nwg > 0x7fffffff || wd + ng > 0x7fffffff) break;  // the next launch takes it
+      qb.j[c] = QuantJob1{j.w, j.n, j.packed, j.absmax};
+      qb.wg0[c] = wq;
+      db.j[c] = DqJob{j.absmax, nb, j.qabsmax, j.c2};
+      db.wg0[c] = wd;
+      wq += nwg;
+      wd += ng;
+      ++c;
+    }
+    if (c == 0) continue;
+    qb.count = db.count = c;
+    qb.wg0[c] = wq;
+    db.wg0[c] = wd;
+    hipLaunchKernelGGL(quantize_nf4_batch_kernel, dim3((unsigned)wq), dim3(256), 0, st, qb);
+    hipLaunchKernelGGL(double_quant_batch_kernel, dim3((unsigned)wd), dim3(256), 0, st, db);
+    if ((s = launched()) != QLORA_OK) return s;
+  }
+  return QLORA_OK;
+}
+
+qlora_status qlora_dequantize_nf4_batch(const qlora_nf4_weight* weights, qlora_bf16* const* outs,
+                                        int32_t count, void* stream) {
+  QCHECK(count >= 0, QLORA_ERR_SHAPE);
+  if (count == 0) return QLORA_OK;
+  QCHECK(weights != nullptr && outs != nullptr, QLORA_ERR_NULL);
+  for (int32_t i = 0; i < count; ++i) {
+    qlora_status s = validate_weight(&weights[i]);
+    if (s != QLORA_OK) return s;
+    const int64_t n = weights[i].n_out * weights[i].k_in;
+    QCHECK(n % 64 == 0, QLORA_ERR_SHAPE);
+    if (n == 0) continue;
+    ALIGNED_OR_NULL(outs[i]);
+    QCHECK(ceil_div(n / 8, 1024) <= 0x7fffffff, QLORA_ERR_SHAPE);
+  }
+  qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = as_stream(stream);
+  int32_t i = 0;
+  while (i < count) {
+    DeqBatch b{};
+    int64_t wg = 0;
+    int32_t c = 0;
+    for (; i < count && c < kBatchMax; ++i) {
+      const qlora_nf4_weight& w = weights[i];
+      const int64_t ndw = w.n_out * w.k_in / 8;
+      if (ndw == 0) continue;
+      const int64_t nwg = ceil_div(ndw, 1024);
+      if (wg + nwg > 0x7fffffff) break;  // the next launch takes it
+      b.j[c] = DeqJob{reinterpret_cast<const uint32_t*>(w.packed), w.qabsmax, w.c2,
+                      reinterpret_cast<u32x4*>(outs[i]), ndw};
+      b.wg0[c] = wg;
+      wg += nwg;
+      ++c;
+    }
+    if (c == 0) continue;
+    b.count = c;
+    b.wg0[c] = wg;
+    hipLaunchKernelGGL(dequantize_nf4_batch_kernel, dim3((unsigned)wg), dim3(256), 0, st, b);
+    if ((s = launched()) != QLORA_OK) return s;
+  }
+  return QLORA_OK;
+}
+
 qlora_status qlora_lora_down(const qlora_bf16* X, int64_t M, int64_t k_in, const qlora_bf16* A,
                              int32_t r, qlora_bf16* U, void* workspace, size_t ws_bytes,
                              void* stream) {

@@ -89,6 +89,47 @@ __global__ void quantize_nf4_kernel(const float* w, int64_t n, int64_t nblocks, 
                                     float* absmax);
 __global__ void double_quant_kernel(const float* absmax, int64_t nblocks, int8_t* qabsmax,
                                     float* c2);
+
+// Lists of weights in one launch (descriptors in the kernel arguments, up to
+// kBatchMax per launch; wg0[i] = first workgroup of job i, wg0[count] = grid).
+constexpr int kBatchMax = 48;
+struct QuantJob1 {  // first level: blocks of 64 -> codes and float32 scales
+  const float* w;
+  int64_t n;
+  uint8_t* packed;
+  float* absmax;
+};
+struct QuantBatch {
+  QuantJob1 j[kBatchMax];
+  int64_t wg0[kBatchMax + 1];
+  int32_t count;
+};
+struct DqJob {  // second level: groups of 256 scales -> int8 codes and steps
+  const float* absmax;
+  int64_t nblocks;
+  int8_t* qabsmax;
+  float* c2;
+};
+struct DqBatch {
+  DqJob j[kBatchMax];
+  int64_t wg0[kBatchMax + 1];
+  int32_t count;
+};
+struct DeqJob {  // decode to bf16, 1024 packed dwords per workgroup
+  const uint32_t* packed;
+  const int8_t* qabsmax;
+  const float* c2;
+  u32x4* out;
+  int64_t ndwords;
+};
+struct DeqBatch {
+  DeqJob j[kBatchMax];
+  int64_t wg0[kBatchMax + 1];
+  int32_t count;
+};
+__global__ void quantize_nf4_batch_kernel(QuantBatch b);
+__global__ void double_quant_batch_kernel(DqBatch b);
+__global__ void dequantize_nf4_batch_kernel(DeqBatch b);
 __global__ void quantize_nf4_dq_kernel(const float* w, int64_t n, int64_t nblocks, uint8_t* packed,
                                        int8_t* qabsmax, float* c2, float* absmax_out);
 __global__ void dequantize_nf4_kernel(const uint32_t* packed, const int8_t* qabsmax, const float* c2,

@@ -223,25 +223,66 @@ __device__ inline void load_16(const uint16_t* __restrict__ w, int64_t n, int64_
   }
 }
 
-// packed[nblocks*32], absmax[nblocks]; 64 blocks per 256-thread workgroup.
+// packed[nblocks*32], absmax[nblocks]; 64 blocks per 256-thread workgroup,
+// workgroup wg taking blocks 64 wg .. 64 wg + 63.  The workgroup's 4096
+// elements come in as 4 loads per lane, load j of lane t being the float4 at
+// element 4 (256 j + t): every load is contiguous across the wave, and 16
+// consecutive lanes hold one block.  Lane i of a block computes threshold i
+// (T_15 = +inf) and each value reads the one it needs from that lane.
 template <int CODE>
 __device__ inline void quantize_blocks(const float* __restrict__ w, int64_t n, int64_t nblocks,
-                                       uint8_t* __restrict__ packed, float* __restrict__ absmax) {
-  __shared__ float thr[64 * kTStride];
+                                       uint8_t* __restrict__ packed, float* __restrict__ absmax,
+                                       int64_t wg) {
   __shared__ uint8_t bk[kNBuckets];
   const int t = threadIdx.x;
   if (t < kNBuckets) bk[t] = kBuckets<CODE>.first[t];
   __syncthreads();
-  const int64_t gt = (int64_t)blockIdx.x * 256 + t;
-  const int64_t blk = gt >> 2;
-  const int sub = (int)(gt & 3);
-  if (blk >= nblocks) return;  // the 4 lanes of a block leave together
-  float v[16];
-  load_16(w, n, blk, sub, v);
-  u32x2 bytes;
-  const float m = quantize_16v<CODE>(v, sub, thr + (t >> 2) * kTStride, bk, bytes);
-  *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
-  if (sub == 0) absmax[blk] = m;
+  const int64_t e0 = wg * 4096;
+  floatx4 x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t e = e0 + 4 * (256 * j + t);
+    if (e + 4 <= n) {
+      x[j] = *reinterpret_cast<const floatx4*>(w + e);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[j][u] = (e + u < n) ? w[e + u] : 0.0f;
+    }
+  }
+  const int lb = t & 15;                     // lane within its block
+  const int src0 = t & 48;                   // the block's first lane within the wave
+  const double mid = lb < 15 ? kMid<CODE>.m[lb] : 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t blk = (e0 >> 6) + 16 * j + (t >> 4);
+    float m = fmaxf(fmaxf(fabsf(x[j][0]), fabsf(x[j][1])), fmaxf(fabsf(x[j][2]), fabsf(x[j][3])));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    m = fmaxf(m, __shfl_xor(m, 8));
+    const float thr = lb < 15 ? rd32_mul(mid, m) : __builtin_inff();
+    // the estimate only picks a bucket; a power-of-two rescale keeps 1/m finite
+    // for subnormal block maxima without changing any ratio.  32 / (m·sc) to
+    // within a couple of ulp: b = trunc(32 x + 32) in one fma, and
+    // |x| <= 1 + 2^-21 keeps b in [0, 64] (an all-zero block uses bucket 32
+    // and its codes are replaced below)
+    const bool nz = m > 0.0f;
+    const float sc = (m < 0x1p-64f) ? 0x1p64f : 1.0f;
+    const float k32 = nz ? 32.0f * __builtin_amdgcn_rcpf(m * sc) : 0.0f;
+    uint32_t code = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bkt = (int)__builtin_fmaf(x[j][u] * sc, k32, 32.0f);
+      const int k0 = bk[bkt];
+      const float tk = __shfl(thr, src0 | k0);
+      code |= ((uint32_t)k0 + ((x[j][u] > tk) ? 1u : 0u)) << (4 * u);
+    }
+    if (!nz) code = Code<CODE>::zero_word & 0xffffu;
+    if (blk < nblocks) {
+      *reinterpret_cast<uint16_t*>(packed + blk * 32 + lb * 2) = (uint16_t)code;
+      if (lb == 0) absmax[blk] = m;
+    }
+  }
 }
 
 }  // namespace
@@ -250,24 +291,25 @@ __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restri
                                                            int64_t nblocks,
                                                            uint8_t* __restrict__ packed,
                                                            float* __restrict__ absmax) {
-  quantize_blocks<kCodeNF4>(w, n, nblocks, packed, absmax);
+  quantize_blocks<kCodeNF4>(w, n, nblocks, packed, absmax, blockIdx.x);
 }
 
 __global__ __launch_bounds__(256) void quantize_int4_kernel(const float* __restrict__ w, int64_t n,
                                                             int64_t nblocks,
                                                             uint8_t* __restrict__ packed,
                                                             float* __restrict__ absmax) {
-  quantize_blocks<kCodeINT4>(w, n, nblocks, packed, absmax);
+  quantize_blocks<kCodeINT4>(w, n, nblocks, packed, absmax, blockIdx.x);
 }
 
-// One workgroup per group of 256 blocks.
-__global__ __launch_bounds__(256) void double_quant_kernel(const float* __restrict__ absmax,
-                                                           int64_t nblocks,
-                                                           int8_t* __restrict__ qabsmax,
-                                                           float* __restrict__ c2) {
+namespace {
+
+// The second level of DQ group g (256 blocks) by one 256-thread workgroup.
+__device__ inline void double_quant_group(const float* __restrict__ absmax, int64_t nblocks,
+                                          int8_t* __restrict__ qabsmax, float* __restrict__ c2,
+                                          int64_t g) {
   __shared__ float red[4];
   const int t = threadIdx.x;
-  const int64_t b = (int64_t)blockIdx.x * kGroup + t;
+  const int64_t b = g * kGroup + t;
   const float a = (b < nblocks) ? absmax[b] : 0.0f;
   float m = a;
 #pragma unroll
@@ -276,8 +318,46 @@ __global__ __launch_bounds__(256) void double_quant_kernel(const float* __restri
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float step = dq_step(m);
-  if (t == 0) c2[blockIdx.x] = step;
+  if (t == 0) c2[g] = step;
   if (b < nblocks) qabsmax[b] = (int8_t)dq_code(a, step);
+}
+
+// The job of workgroup `wg` in a batch: the last job whose first workgroup is
+// at or before it (jobs without workgroups are never picked: a later job
+// starts at the same workgroup).  Uniform, so the descriptor stays scalar.
+__device__ inline int batch_job(const int64_t* wg0, int count, int64_t wg) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (wg0[mid] <= wg)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace
+
+// One workgroup per group of 256 blocks.
+__global__ __launch_bounds__(256) void double_quant_kernel(const float* __restrict__ absmax,
+                                                           int64_t nblocks,
+                                                           int8_t* __restrict__ qabsmax,
+                                                           float* __restrict__ c2) {
+  double_quant_group(absmax, nblocks, qabsmax, c2, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256) void quantize_nf4_batch_kernel(QuantBatch b) {
+  const int i = batch_job(b.wg0, b.count, blockIdx.x);
+  const QuantJob1& J = b.j[i];
+  quantize_blocks<kCodeNF4>(J.w, J.n, (J.n + kBlock - 1) / kBlock, J.packed, J.absmax,
+                            blockIdx.x - b.wg0[i]);
+}
+
+__global__ __launch_bounds__(256) void double_quant_batch_kernel(DqBatch b) {
+  const int i = batch_job(b.wg0, b.count, blockIdx.x);
+  const DqJob& J = b.j[i];
+  double_quant_group(J.absmax, J.nblocks, J.qabsmax, J.c2, blockIdx.x - b.wg0[i]);
 }
 
 // Fused: one workgroup per DQ group (256 blocks = 16384 elements), four passes
@@ -366,6 +446,32 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_bf16_kernel(const uint16_
 // packed dwords (8192 weights); lane t takes dwords t, t + 256, t + 512,
 // t + 768, so every load (4 B per lane) and every store (16 B per lane) is
 // contiguous across the wave.  n is a multiple of 64.
+namespace {
+
+__device__ inline void dequant_chunk(const uint32_t* __restrict__ packed,
+                                     const int8_t* __restrict__ qabsmax,
+                                     const float* __restrict__ c2, int64_t ndwords,
+                                     u32x4* __restrict__ out, int64_t base, const float* cb) {
+  uint32_t p[4];
+  float ah[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = base + threadIdx.x + 256 * u;
+    p[u] = (i < ndwords) ? packed[i] : 0u;
+    const int64_t b = (i < ndwords ? i : 0) >> 3;  // 8 dwords per 64-block
+    ah[u] = c2[b >> 8] * (float)qabsmax[b];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = base + threadIdx.x + 256 * u;
+    u32x4 o;
+    o = decode8(p[u], ah[u], cb);
+    if (i < ndwords) out[i] = o;
+  }
+}
+
+}  // namespace
+
 __global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __restrict__ packed,
                                                              const int8_t* __restrict__ qabsmax,
                                                              const float* __restrict__ c2,
@@ -375,24 +481,19 @@ __global__ __launch_bounds__(256) void dequantize_nf4_kernel(const uint32_t* __r
   if (threadIdx.x < 16) cb[threadIdx.x] = bits_to_float(kNF4Bits[threadIdx.x]);
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * 1024;
-  for (int64_t base = (int64_t)blockIdx.x * 1024; base < ndwords; base += stride) {
-    uint32_t p[4];
-    float ah[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + threadIdx.x + 256 * u;
-      p[u] = (i < ndwords) ? packed[i] : 0u;
-      const int64_t b = (i < ndwords ? i : 0) >> 3;  // 8 dwords per 64-block
-      ah[u] = c2[b >> 8] * (float)qabsmax[b];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + threadIdx.x + 256 * u;
-      u32x4 o;
-      o = decode8(p[u], ah[u], cb);
-      if (i < ndwords) out[i] = o;
-    }
-  }
+  for (int64_t base = (int64_t)blockIdx.x * 1024; base < ndwords; base += stride)
+    dequant_chunk(packed, qabsmax, c2, ndwords, out, base, cb);
+}
+
+// A list of weights in one launch: workgroup wg decodes dwords 1024 (wg − first
+// workgroup of its job) onward of its job.
+__global__ __launch_bounds__(256) void dequantize_nf4_batch_kernel(DeqBatch b) {
+  __shared__ float cb[16];
+  if (threadIdx.x < 16) cb[threadIdx.x] = bits_to_float(kNF4Bits[threadIdx.x]);
+  __syncthreads();
+  const int i = batch_job(b.wg0, b.count, blockIdx.x);
+  const DeqJob& J = b.j[i];
+  dequant_chunk(J.packed, J.qabsmax, J.c2, J.ndwords, J.out, (blockIdx.x - b.wg0[i]) * 1024, cb);
 }
 
 // Single-quantisation decode of n weights (any n): ŵ = RNE_bf16(RN32(level · a)).

@@ -110,6 +110,36 @@ qlora_status qlora_quantize_nf4_dq(const float *w, int64_t n, uint8_t *packed, i
 qlora_status qlora_dequantize_nf4(const qlora_nf4_weight *w /* host struct */, qlora_bf16 *out,
                                   void *stream);
 
+/* Lists of weights, for quantising or decoding a whole model's weight set
+ * (the LLaMA-7B set of "QLoRAの理論と実装" §5-2 is 224 matrices) without a
+ * launch per matrix, whose fixed cost dominates for 4096x4096 weights.
+ *
+ * qlora_quantize_nf4_dq_batch: for each job, exactly the bytes of
+ *   qlora_quantize_nf4_dq(w, n, packed, qabsmax, c2, absmax, stream); absmax
+ *   is required here (it carries the first-level scales between the two
+ *   levels).  Two launches per up to 48 jobs.
+ * qlora_dequantize_nf4_batch: for each i, exactly qlora_dequantize_nf4(
+ *   &weights[i], outs[i], stream).  One launch per up to 48 weights.
+ * jobs, weights and outs are HOST arrays of count entries (count >= 0, else
+ * QLORA_ERR_SHAPE; NULL with count > 0: QLORA_ERR_NULL); the buffers they
+ * name are device memory with the shapes, alignment and error behaviour of
+ * the single-matrix calls.  Every entry is validated before anything is
+ * enqueued; entries with n = 0 are skipped.  The outputs of different jobs
+ * must not overlap. */
+typedef struct {
+  const float *w;     /* n float32 weights                          */
+  int64_t n;
+  uint8_t *packed;    /* ceil(n/64)*32 bytes                        */
+  int8_t *qabsmax;    /* ceil(n/64) DQ codes                        */
+  float *c2;          /* ceil(n/16384) second-level steps           */
+  float *absmax;      /* ceil(n/64) first-level scales (written)    */
+} qlora_quant_job;
+qlora_status qlora_quantize_nf4_dq_batch(const qlora_quant_job *jobs /* host */, int32_t count,
+                                         void *stream);
+qlora_status qlora_dequantize_nf4_batch(const qlora_nf4_weight *weights /* host */,
+                                        qlora_bf16 *const *outs /* host array of device pointers */,
+                                        int32_t count, void *stream);
+
 /* ---- LoRA dropout -------------------------------------------------------- */
 
 /* The training example's lora_dropout ("QLoRAの理論と実装", LoraConfig: 0.05)

@@ -104,11 +104,42 @@ def test_linear_argument_errors(L):
     assert d(ctypes.byref(q.NF4Weight(FAKE, FAKE, FAKE, 4, 16)), MIS, None) == ALIGN
 
 
+def test_batch_argument_errors(L):
+    qb, db = L.qlora_quantize_nf4_dq_batch, L.qlora_dequantize_nf4_batch
+    assert qb(None, 0, None) == OK
+    assert qb(None, -1, None) == SHAPE
+    assert qb(None, 2, None) == NULL
+    jobs = (q.QuantJob * 2)(q.QuantJob(FAKE, 100, FAKE, FAKE, FAKE, FAKE),
+                            q.QuantJob(FAKE, 64, FAKE, FAKE, FAKE, None))
+    assert qb(jobs, 2, None) == NULL  # the first-level scales need a buffer
+    jobs[1] = q.QuantJob(FAKE, 64, FAKE, MIS, FAKE, FAKE)
+    assert qb(jobs, 2, None) == ALIGN
+    jobs[1] = q.QuantJob(FAKE, -5, FAKE, FAKE, FAKE, FAKE)
+    assert qb(jobs, 2, None) == SHAPE
+    assert db(None, None, 0, None) == OK
+    assert db(None, None, -1, None) == SHAPE
+    assert db(None, None, 1, None) == NULL
+    ws = (q.NF4Weight * 2)(q.NF4Weight(FAKE, FAKE, FAKE, 4, 16), q.NF4Weight(FAKE, FAKE, FAKE, 3, 5))
+    outs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert db(ws, outs, 2, None) == SHAPE
+    ws[1] = q.NF4Weight(FAKE, FAKE, FAKE, 4, 16)
+    outs[1] = MIS
+    assert db(ws, outs, 2, None) == ALIGN
+    ws[1] = q.NF4Weight(None, FAKE, FAKE, 4, 16)
+    outs[1] = FAKE
+    assert db(ws, outs, 2, None) == NULL
+
+
 def test_valid_arguments_without_gpu_report_device(L):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert L.qlora_quantize_nf4(FAKE, 100, 64, FAKE, FAKE, None) == DEV
+    jobs = (q.QuantJob * 2)(q.QuantJob(FAKE, 100, FAKE, FAKE, FAKE, FAKE),
+                            q.QuantJob(None, 0, None, None, None, None))  # an empty job is skipped
+    assert L.qlora_quantize_nf4_dq_batch(jobs, 2, None) == DEV
+    ws = (q.NF4Weight * 1)(q.NF4Weight(FAKE, FAKE, FAKE, 4, 16))
+    assert L.qlora_dequantize_nf4_batch(ws, (ctypes.c_void_p * 1)(FAKE), 1, None) == DEV
     assert L.qlora_linear_fwd(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, 1 << 30,
                               None) == DEV
 

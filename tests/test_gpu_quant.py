@@ -202,3 +202,38 @@ def test_weight_beyond_two_to_the_31_elements():
         assert np.array_equal(f32_bits(absmax[s0 // 64:s1 // 64]), oa.view(np.uint32)), g
         ref = dequantize_nf4(op, oq, oc2, G)
         assert np.array_equal(bf16_bits(out.view(-1)[s0:s1]), ref), g
+
+
+def test_batches_match_single_calls_and_oracle():
+    """53 weights (two launches of up to 48 jobs), ragged tails and an empty one:
+    every byte of the batched quantiser and decoder equals the single-matrix
+    calls; one ragged weight is also compared with the oracle."""
+    rng = np.random.default_rng(77)
+    sizes = [64, 100, 0, 16384 + 64, 4096 * 64, 255 * 64 + 17] + \
+        [64 * (1 + (i * 37) % 700) for i in range(47)]
+    say(f"[quant] batches of {len(sizes)} weights")
+    flats = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+    ws = [to_dev(f) for f in flats]
+    got = q.quantize_nf4_dq_batch(ws)
+    torch.cuda.synchronize()
+    for w, g in zip(ws, got):
+        ref = q.quantize_nf4_dq(w, want_absmax=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(u8(g[0]), u8(ref[0]))
+        assert np.array_equal(u8(g[1]), u8(ref[1]))
+        assert np.array_equal(f32_bits(g[2]), f32_bits(ref[2]))
+        assert np.array_equal(f32_bits(g[3]), f32_bits(ref[3]))
+    op, oa = quantize_nf4(flats[1])
+    oq, oc2 = double_quant(oa)
+    assert np.array_equal(u8(got[1][0]), op)
+    assert np.array_equal(u8(got[1][1]).view(np.int8), oq)
+    assert np.array_equal(f32_bits(got[1][2]), oc2.view(np.uint32))
+    wqs = [q.NF4Tensor(g[0], g[1], g[2], n // 64, 64) for n, g in zip(sizes, got) if n % 64 == 0]
+    outs = q.dequantize_nf4_batch(wqs)
+    torch.cuda.synchronize()
+    for wq, o in zip(wqs, outs):
+        assert np.array_equal(bf16_bits(o), bf16_bits(q.dequantize_nf4(wq)))
+    i3 = [n for n in sizes if n % 64 == 0].index(16384 + 64)
+    p3, a3 = quantize_nf4(flats[3])
+    q3, c3 = double_quant(a3)
+    assert np.array_equal(bf16_bits(outs[i3]).ravel(), dequantize_nf4(p3, q3, c3, sizes[3]))
