@@ -796,7 +796,70 @@ def cpu_baseline(inp, wlc):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds_per_step": dt, "steps": reps,
             "sample": f"full steps of {wlc.name} repeated for about 10 s: decode + fp64 "
-                      "forward + backward, all 4096 tokens (numpy, float64)"}
+                      "forward + backward, all 4096 tokens (numpy, float64)",
+            "per_config": oracle_per_config(flops / dt)}
+
+
+def oracle_per_config(rate_step):
+    """The oracle's wall time on the other workloads, each bounded to a few
+    seconds: measured in full where that fits, else on a stated sample and
+    extrapolated (labelled).  rate_step: the oracle's float64 flop rate on the
+    training step, measured above."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from oracle.linear import linear_fwd, lora_scale
+    from oracle.quant import bf16_to_f64, dequantize_nf4, double_quant, quantize_nf4
+
+    f64 = lambda t: t.to(torch.float64).numpy()
+    out = {}
+    # single linear: quantise + DQ, decode and the 16-token forward, in full
+    w1 = wl.SINGLE_LINEAR
+    inp = w1.inputs()
+    t0 = time.perf_counter()
+    p1, a1 = quantize_nf4(inp["W"].ravel())
+    q1, c1 = double_quant(a1)
+    w64 = bf16_to_f64(dequantize_nf4(p1, q1, c1, inp["W"].size)).reshape(w1.n_out, w1.k_in)
+    linear_fwd(f64(inp["X"]), w64, f64(inp["A"]), f64(inp["B"]), lora_scale(w1.alpha, w1.r))
+    out["single_linear_4096x4096_r8_m16"] = dict(seconds=time.perf_counter() - t0,
+                                                 what="quantise + DQ + decode + forward, in full")
+    # weight set: one 4096 x 4096 matrix (with its outliers), scaled to 6.48 G weights
+    w = wl.llama7b_weight(0, 0).ravel()
+    t0 = time.perf_counter()
+    p2, a2 = quantize_nf4(w)
+    q2, c2_ = double_quant(a2)
+    tq = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    dequantize_nf4(p2, q2, c2_, w.size)
+    td = time.perf_counter() - t0
+    total = sum(n * k for _, n, k in wl.LLAMA7B_MATRICES) * wl.LLAMA7B_LAYERS
+    out["llama7b_weight_set_224_matrices"] = dict(
+        seconds_quantize_dq=tq * total / w.size, seconds_dequantize=td * total / w.size,
+        what=f"extrapolated from layer 0's q matrix ({w.size} weights) to {total} weights")
+    # few-token forward: 1024 of the 28672 output rows of the 8192 -> 28672 weight
+    # (the first rows of the same seeded stream), M = 1, scaled to all rows
+    g = wl.GEMV_70B
+    rows = 1024
+    wr = wl.rng(g.workload, 0, 0, wl.T_W).standard_normal(rows * g.k_in, dtype=np.float32)
+    wr *= np.float32(0.02)
+    gin = g.inputs(M=1, with_dy=False)
+    t0 = time.perf_counter()
+    p4, a4 = quantize_nf4(wr)
+    q4, c4 = double_quant(a4)
+    w4 = bf16_to_f64(dequantize_nf4(p4, q4, c4, wr.size)).reshape(rows, g.k_in)
+    linear_fwd(f64(gin["X"]), w4, f64(gin["A"]), f64(gin["B"][:rows]), lora_scale(g.alpha, g.r))
+    dt = time.perf_counter() - t0
+    out["few_token_fwd_8192x28672_r16"] = dict(
+        seconds_quantize_and_forward_m1=dt * g.n_out / rows,
+        what=f"extrapolated from {rows} of {g.n_out} output rows (quantise + DQ + decode "
+             "+ forward of one token)")
+    # the LLaMA-65B layer: its flops at the training step's measured float64 rate
+    fl = sum(x.flops_fwd + x.flops_bwd for x in wl.LLAMA65B_LAYER)
+    out["llama65b_layer_7proj_r64_m2048"] = dict(
+        seconds=fl / rate_step, what="extrapolated: 6,754 GFLOP at the float64 rate measured "
+                                     "on the LLaMA-7B MLP training step (decode excluded)")
+    return out
 
 
 if __name__ == "__main__":
