@@ -63,18 +63,18 @@ template <int CPW, int MG, int G, bool QV>
 __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   // LDS: the codebook table (64 KB), then the per-wave partial sums (reduced
   // once at the end), then the U rows of the adapter term.  The token
-  // staging area (the workgroup's k range of X, up to 8 tokens, loaded
-  // densely once and read back in operand order) lies over the partial sums
-  // for up to 4 tokens and over the table and the partial sums beyond, so
-  // there the table is filled after the operands have been read.
+  // staging area (the workgroup's k range of X, all M tokens, loaded densely
+  // once and read back in operand order) lies over the partial sums for up
+  // to 4 tokens and over the table and the partial sums beyond, so there the
+  // table is filled after the operands have been read.
   constexpr int NT = 64 * kGemvWaves;
   constexpr int kLut = 256 * 64 * 4;
   constexpr int kSpan = kGemvWaves * CPW * 128;  // k range of one workgroup
   constexpr int kRedBytes = kGemvWaves * G * MG * 32 * 4 * 4;
-  constexpr int kStage4 = MG == 1 ? 4 * kSpan * 2 : 0;   // up to 4 tokens, after the table
-  constexpr int kStage8 = MG == 1 ? 8 * kSpan * 2 : 0;   // up to 8 tokens, from the start
-  constexpr int kRedRegion = kRedBytes > kStage4 ? (kRedBytes > kStage8 - kLut ? kRedBytes : kStage8 - kLut)
-                                                 : (kStage4 > kStage8 - kLut ? kStage4 : kStage8 - kLut);
+  constexpr int kStage4 = MG == 1 ? 4 * kSpan * 2 : 0;  // up to 4 tokens, after the table
+  constexpr int kStageAll = 8 * MG * kSpan * 2;         // all token groups, from the start
+  constexpr int kRedRegion = kRedBytes > kStage4 ? (kRedBytes > kStageAll - kLut ? kRedBytes : kStageAll - kLut)
+                                                 : (kStage4 > kStageAll - kLut ? kStage4 : kStageAll - kLut);
   __shared__ __attribute__((aligned(16))) char smem[kLut + kRedRegion];
   // byte e -> the two bf16 levels of its nibbles, 64 copies: entry e of lane
   // l at byte 256 e + 4 l, so a lookup address is one v_perm of the packed
@@ -93,17 +93,16 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   const int64_t chunk0 = ((int64_t)blockIdx.y * kGemvWaves + w) * CPW;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(g.x, (int64_t)M * K * 2);
 
-  // One token group (M <= 8): the workgroup's tokens come in as dense 16-byte
-  // loads (about M·CPW / 4 per lane) instead of 4·CPW mostly empty ones per
-  // wave, so the 256 workgroups put far fewer requests on the same lines of
-  // X.  The loads go out first.
-  const bool staged = MG == 1;
-  const bool early_lut = !staged || M <= 4;  // uniform
-  constexpr int kPieces = MG == 1 ? 8 * kSpan / 8 / NT : 1;  // 16-byte pieces per lane at 8 tokens
+  // The workgroup's tokens come in as dense 16-byte loads (about M·CPW / 4
+  // per lane) instead of 4·CPW·MG partly empty ones per wave, so the 256
+  // workgroups put far fewer requests on the same lines of X.  The loads go
+  // out first.
+  const bool early_lut = MG == 1 && M <= 4;  // uniform
+  constexpr int kPieces = 8 * MG * kSpan / 8 / NT;  // 16-byte pieces per lane at 8·MG tokens
   const int rounds = (M * (kSpan / 8) + NT - 1) / NT;      // the rounds that carry tokens
   const int64_t kw0 = (int64_t)blockIdx.y * kSpan;
   u32x4 xs[kPieces];
-  if (staged) {
+  {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
       if (i < rounds) {
@@ -131,7 +130,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   };
   if (early_lut) fill_table();
   char* stage = early_lut ? red_stage : smem;
-  if (staged) {
+  {
     *reinterpret_cast<uint32_t*>(ush + 2 * tid) = 0u;  // NT · 4 B = 2 KB of zeros
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
@@ -139,24 +138,11 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
   }
   __syncthreads();
 
-  // Token operands for this wave's chunks, kept in registers for all columns.
-  // A lane carries token c16 mod 8 of block (c16 >= 8) and zeros elsewhere.
+  // Token operands for this wave's chunks, kept in registers for all columns:
+  // a lane carries token c16 mod 8 (+ 8 mg) of block (c16 >= 8) and zeros
+  // elsewhere, read back from the staging area once the first weight loads
+  // are out.
   u32x4 xa[MG][CPW][4];
-  if (!staged) {
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg)
-#pragma unroll
-      for (int c = 0; c < CPW; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t k = (chunk0 + c) * 128 + 32 * qd + 8 * j;
-          const int tok = (c16 & 7) + 8 * mg;
-          const bool valid = ((c16 < 8) == (qd < 2)) && tok < M && k < K;
-          xa[mg][c][j] = __builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                         xr, valid ? (int)(((int64_t)tok * K + k) * 2) : 0x7ffffff0, 0, 0));
-        }
-  }
 
   const char* lutb = reinterpret_cast<const char*>(lut);
   const uint32_t lane4 = (uint32_t)lane * 4;
@@ -234,18 +220,22 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
 #pragma unroll
   for (int st = 0; st < D; ++st) load(st);  // rows past N read as zero
   load_scales(0, sA);
-  if (staged) {
-    // the lane's 4·CPW operand pieces are 16-byte reads at fixed offsets from
-    // one base: its token's row (wave slice, k-slot qd) or the zeros
-    const int tok = c16 & 7;
-    const bool valid = ((c16 < 8) == (qd < 2)) && tok < M;
-    const char* base = valid ? stage + ((size_t)tok * kSpan + (size_t)w * CPW * 128 + 32 * qd) * 2
-                             : reinterpret_cast<const char*>(ush) + 64 * qd;
+  {
+    // the lane's 4·CPW operand pieces per token group are 16-byte reads at
+    // fixed offsets from one base: its token's row (wave slice, k-slot qd) or
+    // the zeros
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
+    for (int mg = 0; mg < MG; ++mg) {
+      const int tok = (c16 & 7) + 8 * mg;
+      const bool valid = ((c16 < 8) == (qd < 2)) && tok < M;
+      const char* base = valid ? stage + ((size_t)tok * kSpan + (size_t)w * CPW * 128 + 32 * qd) * 2
+                               : reinterpret_cast<const char*>(ush) + 64 * qd;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xa[0][c][j] = *reinterpret_cast<const u32x4*>(base + c * 256 + 16 * j);
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xa[mg][c][j] = *reinterpret_cast<const u32x4*>(base + c * 256 + 16 * j);
+    }
     // the staging area becomes the partial sums (and the table): every wave
     // has read it first (the weight loads just issued stay in flight across
     // these barriers)
@@ -255,7 +245,6 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
       lds_barrier();
     }
   }
-
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     Scales& sc = (gi & 1) ? sB : sA;

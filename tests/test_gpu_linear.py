@@ -74,9 +74,11 @@ def _run_case(M, K, N, r, alpha, seed, bwd=True):
     (513, 128, 1032, 72, 16.0),   # rank above 64: prologue over two 64-chunks
     (257, 448, 256, 64, 16.0),
     (3, 8448, 64, 8, 16.0),       # few-token path split over k (partial sums + reduction)
-    (12, 4096, 40, 16, 32.0),     # few tokens in two groups of 8, U formed in the kernel
-    (6, 4096, 40, 32, 16.0),      # few tokens, rank too large to form U in the kernel
+    (12, 4096, 40, 16, 32.0),     # few tokens in two groups of 8
+    (6, 4096, 40, 32, 16.0),      # few tokens, rank 32
     (2, 1088, 48, 8, 16.0),       # few tokens, byte-wise scale codes, k split in two
+    (9, 8448, 40, 8, 16.0),       # two token groups, k split (partial sums + reduction)
+    (13, 1088, 48, 8, 16.0),      # two token groups, byte-wise scale codes
     (256, 512, 264, 256, 16.0),   # largest rank, many-token path
     (40, 256, 96, 256, 64.0),     # largest rank, split-K path
     (3, 512, 64, 256, 16.0),      # largest rank, few-token path
