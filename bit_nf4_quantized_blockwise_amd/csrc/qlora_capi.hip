@@ -27,7 +27,7 @@ qlora_status check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QLORA_ERR_DEVICE;
   if (dev < kMaxDevices) {
-    const int s = g_dev_ok[dev].load(std::memory_order_relaxed);
+    const int s = g_dev_ok[dev].load(std::memory_order_acquire);
     if (s == 1) return QLORA_OK;
     if (s == 2) return QLORA_ERR_DEVICE;
   }
@@ -35,8 +35,10 @@ qlora_status check_device() {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QLORA_ERR_DEVICE;
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (dev < kMaxDevices) {
+    // the CU count is published before the verdict, so a thread that sees the
+    // device checked also sees its count
     g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
-    g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
   }
   return ok ? QLORA_OK : QLORA_ERR_DEVICE;
 }
