@@ -214,6 +214,125 @@ def pmc_pass():
     print("pmc pass done", flush=True)
 
 
+HBM_SOURCES = ["qlora_quant.hip", "qlora_gemv.hip", "qlora_common.h", "qlora_kernels.h"]
+
+
+def hbm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in HBM_SOURCES:
+        with open(os.path.join(ROOT, "bit_nf4_quantized_blockwise_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_pass_hbm():
+    """Short run for the byte counters of the HBM-bound kernels: the fused
+    quantiser (two launches) and the dequantiser on the 11008 x 4096 weight,
+    the few-token forward (U launch + GEMV) at one token on the 8192 -> 28672
+    weight, three times each, and the calibration copy."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    # the few-token weight is quantised first: the summary takes the last three
+    # dispatches of each kernel
+    g = wl.GEMV_70B
+    gin = g.inputs(M=1)
+    wg = q.quantize_weight(torch.from_numpy(gin["W"]).to(dev))
+    W = torch.from_numpy(wl.LLAMA7B_MLP.inputs(with_dy=False)["W"]).to(dev)
+    for _ in range(3):
+        o = q.quantize_nf4_dq(W, want_absmax=True)
+    wq = q.NF4Tensor(o[0], o[1], o[2], W.shape[0], W.shape[1])
+    out = torch.empty(W.shape, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        q.dequantize_nf4(wq, out=out)
+    del W, out
+    X, A, B = (gin[k].to(dev) for k in ("X", "A", "B"))
+    for _ in range(3):
+        q.linear_fwd(wg, X, A, B, g.alpha)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("pmc hbm pass done", flush=True)
+
+
+def summarize_hbm(out_path, fetch_csv, write_csv):
+    """Per-launch FETCH_SIZE / WRITE_SIZE of the HBM-bound kernels (the last
+    three dispatches of each), scaled by the copy calibration, against each
+    kernel's algorithmic bytes."""
+    import csv
+
+    # qualified names: "quantize_nf4_kernel" alone would also match the dequantiser
+    keys = {"qlora::quantize_nf4_kernel(": "quantise, first level",
+            "qlora::double_quant_kernel(": "DQ, second level",
+            "qlora::dequantize_nf4_kernel(": "dequantise",
+            "qlora::lora_down_small_kernel(": "U = X·Aᵀ, 1 token",
+            "qlora::nf4_gemv_kernel<": "few-token GEMV, 1 token", "copyBuffer": "copy"}
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = next((k for k in keys if k in r["Kernel_Name"]), None)
+            if key:
+                vals.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), 0.0)
+                vals[key][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+        # the last three dispatches of each kernel are the measured ones (the
+        # calibration copies run last; earlier copies and the quantisation of
+        # the few-token weight move other buffers)
+        for k in vals:
+            last = sorted(vals[k])[-3:]
+            vals[k] = {d: vals[k][d] for d in last}
+        return {k: sum(v.values()) / len(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    kib = CALIB_BYTES / 1024.0
+    fs, ws_ = kib / f["copyBuffer"], kib / w["copyBuffer"]
+    n = 11008 * 4096
+    nb, ng = n // 64, (n // 64 + 255) // 256
+    ng70, n70 = (28672 * 8192 // 64 + 255) // 256, 28672 * 8192
+    algo = {
+        "qlora::quantize_nf4_kernel(": (4 * n, n // 2 + 4 * nb),
+        "qlora::double_quant_kernel(": (4 * nb, nb + 4 * ng),
+        "qlora::dequantize_nf4_kernel(": (n // 2 + nb + 4 * ng, 2 * n),
+        "qlora::lora_down_small_kernel(": (2 * 8192 + 2 * 16 * 8192, 2 * 16),
+        "qlora::nf4_gemv_kernel<": (n70 // 2 + n70 // 64 + 4 * ng70 + 2 * 8192 + 2 * 16 * 28672 + 2 * 16,
+                            2 * 28672),
+    }
+    with open(out_path, "w") as fh:
+        fh.write("# HBM traffic of the HBM-bound kernels: the fused quantiser (two launches) and the\n")
+        fh.write("# dequantiser on the 11008 x 4096 weight, the few-token forward at 1 token on the\n")
+        fh.write("# 8192 -> 28672 weight (r = 16).  rocprofv3 FETCH_SIZE and WRITE_SIZE per launch\n")
+        fh.write(f"# (the last three dispatches of each), each scaled by the same counter on a device copy of\n")
+        fh.write(f"# {CALIB_BYTES} bytes.  Commands (from /tmp, TMPDIR=/tmp):\n")
+        fh.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_f> -o f -- python3 <repo>/bench.py --pmc-pass-hbm\n")
+        fh.write("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_w> -o w -- python3 <repo>/bench.py --pmc-pass-hbm\n")
+        fh.write("#   python3 <repo>/bench.py --summarize-hbm <this file> <dir_f>/f_counter_collection.csv "
+                 "<dir_w>/w_counter_collection.csv\n")
+        fh.write(f"kernel_source_sha256_16 = {hbm_source_hash()}\n")
+        fh.write(f"fetch_scale = {fs:.4f}\nwrite_scale = {ws_:.4f}\n")
+        fh.write("# kernel: counted read / write bytes per launch; algorithmic read / write; counted / algorithmic\n")
+        for k, (ar, aw) in algo.items():
+            if k not in f or k not in w:
+                continue
+            cr, cw = f[k] * fs * 1024.0, w[k] * ws_ * 1024.0
+            fh.write(f"{keys[k]}: read {cr:.0f} / {ar}, write {cw:.0f} / {aw}, "
+                     f"total {(cr + cw) / (ar + aw):.3f}\n")
+        kq, kd = "qlora::quantize_nf4_kernel(", "qlora::double_quant_kernel("
+        q2 = (f.get(kq, 0) + f.get(kd, 0)) * fs * 1024.0 + (w.get(kq, 0) + w.get(kd, 0)) * ws_ * 1024.0
+        fh.write(f"quantise + DQ (both launches) counted {q2:.0f} against the fused algorithmic "
+                 f"{4 * n + n // 2 + nb + 4 * ng} (ratio {q2 / (4 * n + n // 2 + nb + 4 * ng):.3f}; the "
+                 "absmax hand-over is 8 B per 64 weights)\n")
+    print(open(out_path).read())
+
+
 def _events():
     import torch
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -270,6 +389,9 @@ def main():
                     help="write the HBM traffic summary from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "BENCH_LOG", "OUT_TXT"),
                     help="write the kernel statistics summary of a rocprofv3 --stats run")
+    ap.add_argument("--pmc-pass-hbm", action="store_true",
+                    help="only run the HBM-bound kernels and a calibration copy (counters)")
+    ap.add_argument("--summarize-hbm", nargs=3, metavar=("OUT_TXT", "FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-counters", nargs="+", metavar="PATH",
                     help="OUT_TXT then the counter CSVs of rocprofv3 --pmc runs of --pmc-pass")
     args = ap.parse_args()
@@ -290,6 +412,12 @@ def main():
 
     if args.pmc_pass:
         pmc_pass()
+        return
+    if args.pmc_pass_hbm:
+        pmc_pass_hbm()
+        return
+    if args.summarize_hbm:
+        summarize_hbm(*args.summarize_hbm)
         return
 
     import numpy as np
