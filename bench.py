@@ -149,27 +149,32 @@ def summarize_stats(stats_csv, bench_log, out_path):
     print(open(out_path).read())
 
 
-def summarize_counters(out_path, *csvs):
-    """Per-dispatch averages of the SQ counters of the forward dequant-GEMM from
-    rocprofv3 --pmc runs of --pmc-pass, with the ratios read off them."""
+FWD_GEMM = "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0>"
+DX_GEMM = "gemm_kernel<256, 256, 2, 2, 1, true, 0, 0>"
+
+
+def summarize_counters(out_path, *csvs, kernel=FWD_GEMM, what="forward dequant-GEMM",
+                       pass_flag="--pmc-pass", summary_flag="--summarize-counters"):
+    """Per-dispatch averages of the SQ counters of one GEMM kernel from
+    rocprofv3 --pmc runs of a counter pass, with the ratios read off them."""
     import csv
 
     vals = {}
     for path in csvs:
         for r in csv.DictReader(open(path)):
-            if "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0>" not in r["Kernel_Name"]:
+            if kernel not in r["Kernel_Name"]:
                 continue
             d = vals.setdefault(r["Counter_Name"], {})
             key = (path, r["Dispatch_Id"])  # a counter may appear in several runs
             d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
     avg = {k: sum(v.values()) / len(v) for k, v in vals.items()}
     with open(out_path, "w") as fh:
-        fh.write("# SQ counters of the forward dequant-GEMM (LLaMA-7B MLP: 4096 tokens, 4096 -> "
-                 "11008, r = 64),\n# per dispatch, averaged over the dispatches of --pmc-pass.  "
+        fh.write(f"# SQ counters of the {what} (LLaMA-7B MLP: 4096 tokens, 4096 -> "
+                 f"11008, r = 64),\n# per dispatch, averaged over the dispatches of {pass_flag}.  "
                  "Commands (from /tmp, TMPDIR=/tmp),\n# one rocprofv3 run per counter set:\n")
         fh.write("#   rocprofv3 --pmc <set> --output-format csv -d <dir_i> -o c -- python3 "
-                 "<repo>/bench.py --pmc-pass\n")
-        fh.write("#   python3 <repo>/bench.py --summarize-counters <this file> "
+                 f"<repo>/bench.py {pass_flag}\n")
+        fh.write(f"#   python3 <repo>/bench.py {summary_flag} <this file> "
                  "<dir_1>/c_counter_collection.csv ...\n")
         fh.write(f"kernel_source_sha256_16 = {gemm_source_hash()}\n")
         for k in sorted(avg):
@@ -185,6 +190,28 @@ def summarize_counters(out_path, *csvs):
                      f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.3f}, on LDS = "
                      f"{avg.get('SQ_WAIT_INST_LDS', 0.0) / avg['SQ_WAVE_CYCLES']:.3f}\n")
     print(open(out_path).read())
+
+
+def pmc_pass_bwd():
+    """Short run for counter collection: the backward of the LLaMA-7B MLP
+    linear (input-gradient dequant-GEMM and adapter products) three times."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    wlc = wl.LLAMA7B_MLP
+    inp = wlc.inputs()
+    wq = q.quantize_weight(torch.from_numpy(inp["W"]).to(dev))
+    X, A, B, dY = (inp[k].to(dev) for k in ("X", "A", "B", "dY"))
+    U = q.lora_down(X, A)
+    ws = torch.empty(q.workspace_size(1, wlc.M, wlc.n_out, wlc.k_in, wlc.r), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(3):
+        q.linear_bwd(wq, X, dY, A, B, U, wlc.alpha, workspace=ws)
+    torch.cuda.synchronize()
+    print("pmc bwd pass done", flush=True)
 
 
 def pmc_pass():
@@ -389,6 +416,10 @@ def main():
                     help="write the HBM traffic summary from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "BENCH_LOG", "OUT_TXT"),
                     help="write the kernel statistics summary of a rocprofv3 --stats run")
+    ap.add_argument("--pmc-pass-bwd", action="store_true",
+                    help="only run the backward (input-gradient GEMM) for counters")
+    ap.add_argument("--summarize-counters-bwd", nargs="+", metavar="PATH",
+                    help="OUT_TXT then the counter CSVs of rocprofv3 --pmc runs of --pmc-pass-bwd")
     ap.add_argument("--pmc-pass-hbm", action="store_true",
                     help="only run the HBM-bound kernels and a calibration copy (counters)")
     ap.add_argument("--summarize-hbm", nargs=3, metavar=("OUT_TXT", "FETCH_CSV", "WRITE_CSV"))
@@ -415,6 +446,14 @@ def main():
         return
     if args.pmc_pass_hbm:
         pmc_pass_hbm()
+        return
+    if args.pmc_pass_bwd:
+        pmc_pass_bwd()
+        return
+    if args.summarize_counters_bwd:
+        summarize_counters(*args.summarize_counters_bwd, kernel=DX_GEMM,
+                           what="input-gradient dequant-GEMM", pass_flag="--pmc-pass-bwd",
+                           summary_flag="--summarize-counters-bwd")
         return
     if args.summarize_hbm:
         summarize_hbm(*args.summarize_hbm)
