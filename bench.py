@@ -151,6 +151,7 @@ def summarize_stats(stats_csv, bench_log, out_path):
 
 FWD_GEMM = "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0>"
 DX_GEMM = "gemm_kernel<256, 256, 2, 2, 1, true, 0, 0>"
+GRAD_GEMM = "gemm_kernel<64, 256, 2, 2, 3, false, 1, 1>"  # dA and dB
 
 
 def summarize_counters(out_path, *csvs, kernel=FWD_GEMM, what="forward dequant-GEMM",
@@ -420,6 +421,8 @@ def main():
                     help="only run the backward (input-gradient GEMM) for counters")
     ap.add_argument("--summarize-counters-bwd", nargs="+", metavar="PATH",
                     help="OUT_TXT then the counter CSVs of rocprofv3 --pmc runs of --pmc-pass-bwd")
+    ap.add_argument("--summarize-counters-adapter", nargs="+", metavar="PATH",
+                    help="OUT_TXT then the counter CSVs of --pmc-pass-bwd (dA / dB GEMMs)")
     ap.add_argument("--pmc-pass-hbm", action="store_true",
                     help="only run the HBM-bound kernels and a calibration copy (counters)")
     ap.add_argument("--summarize-hbm", nargs=3, metavar=("OUT_TXT", "FETCH_CSV", "WRITE_CSV"))
@@ -449,6 +452,12 @@ def main():
         return
     if args.pmc_pass_bwd:
         pmc_pass_bwd()
+        return
+    if args.summarize_counters_adapter:
+        summarize_counters(*args.summarize_counters_adapter, kernel=GRAD_GEMM,
+                           what="adapter-gradient GEMMs dA = s·Vᵀ·X and dB = s·dYᵀ·U (one kernel, "
+                                "both launches averaged)", pass_flag="--pmc-pass-bwd",
+                           summary_flag="--summarize-counters-adapter")
         return
     if args.summarize_counters_bwd:
         summarize_counters(*args.summarize_counters_bwd, kernel=DX_GEMM,
