@@ -120,32 +120,52 @@ def summarize_pmc(fetch_csv, write_csv, out_path):
 
 def summarize_stats(stats_csv, bench_log, out_path):
     """Short text summary of a rocprofv3 --kernel-trace --stats run of this
-    script: per-kernel calls and durations, with the bench line it printed."""
+    script: calls and durations per kernel and launch grid (from the per-
+    dispatch trace beside the stats file: one kernel runs at several shapes,
+    and the forward dequant-GEMM's line at the bench shape is the one the
+    roofline's event timing is compared with), with the bench line it printed."""
     import csv
+    import statistics
 
-    rows = list(csv.DictReader(open(stats_csv)))
-    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        key = (r["Kernel_Name"], f"{r['Grid_Size_X']}x{r['Grid_Size_Y']}")
+        groups.setdefault(key, []).append(dur)
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
     line = [ln for ln in open(bench_log) if ln.startswith('{"metric"')][-1]
     d = json.loads(line)
+    n_tiles = ((d["config"]["tokens"] + 255) // 256) * ((d["config"]["n_out"] + 255) // 256)
+    fwd_key = next((k for k in groups if FWD_GEMM in k[0] and k[1] == f"{n_tiles * 256}x1"), None)
     with open(out_path, "w") as fh:
         fh.write("# rocprofv3 kernel statistics of bench.py (LLaMA-7B MLP QLoRA linear: 4096 "
                  "tokens,\n# 4096 -> 11008, r = 64, alpha = 16, and the other rows of the "
-                 "bench line), one MI355X.\n")
+                 "bench line), one MI355X, per kernel and launch grid.\n")
         fh.write("# commands (from /tmp, TMPDIR=/tmp):\n")
+        rows_flag = "" if d["rows"] else " --no-rows"
         fh.write("#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
-                 "python3 <repo>/bench.py --no-cpu-baseline --steps 10 --warmup 2 > <log>\n")
+                 f"python3 <repo>/bench.py --no-cpu-baseline{rows_flag} --steps 10 --warmup 2 > <log>\n")
         fh.write("#   python3 <repo>/bench.py --summarize-stats <dir>/bench_kernel_stats.csv "
                  "<log> <this file>\n")
+        if d["rows"]:
+            fh.write("# (with all rows: one kernel and grid can cover several shapes, e.g. the\n"
+                     "#  LLaMA-65B gate and up projections tile into the same 688 workgroups as\n"
+                     "#  the forward GEMM of the bench shape; --no-rows isolates the latter)\n")
         fh.write(f"# bench line under the profiler: value = {d['value']:.1f} TFLOP/s, "
                  f"ms_per_step = {d['ms_per_step']:.3f},\n")
-        fh.write(f"#   forward dequant-GEMM (events) = {d['roofline']['ms'] * 1e3:.1f} us\n\n")
-        fh.write(f"{'kernel':<80} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} "
-                 f"{'total_ms':>10}\n")
-        for r in rows:
-            fh.write(f"{r['Name'][:80]:<80} {int(r['Calls']):>6} "
-                     f"{float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
-                     f"{float(r['MaxNs']) / 1e3:>10.2f} "
-                     f"{float(r['TotalDurationNs']) / 1e6:>10.3f}\n")
+        fh.write(f"#   forward dequant-GEMM (events) = {d['roofline']['ms'] * 1e3:.1f} us\n")
+        if fwd_key and not d["rows"]:
+            v = groups[fwd_key]
+            fh.write(f"#   forward dequant-GEMM at the bench shape (trace, grid {fwd_key[1]}): "
+                     f"{len(v)} calls, mean {statistics.mean(v):.1f} us, median "
+                     f"{statistics.median(v):.1f} us\n")
+        fh.write("\n")
+        fh.write(f"{'kernel':<72} {'grid':>14} {'calls':>6} {'avg_us':>10} {'min_us':>10} "
+                 f"{'max_us':>10} {'total_ms':>10}\n")
+        for (name, grid), v in rows[:60]:
+            fh.write(f"{name[:72]:<72} {grid:>14} {len(v):>6} {statistics.mean(v):>10.2f} "
+                     f"{min(v):>10.2f} {max(v):>10.2f} {sum(v) / 1e3:>10.3f}\n")
     print(open(out_path).read())
 
 
