@@ -1,0 +1,73 @@
+"""Host logic of bench.py's profile summaries, on small synthetic rocprofv3
+CSV files: kernel matching (the dequantiser is not taken for the quantiser),
+the copy calibration (the last three copies), and per-grid kernel statistics
+(the forward GEMM's line at the bench shape)."""
+
+import csv
+import json
+
+import bench
+
+CNT_FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=CNT_FIELDS)
+        w.writeheader()
+        for d, name, v in rows:
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": v})
+
+
+def test_hbm_summary_matches_kernels_and_calibrates(tmp_path):
+    kib = bench.CALIB_BYTES / 1024.0
+    n = 11008 * 4096
+    q = "qlora::quantize_nf4_kernel(float const*, long, long, unsigned char*, float*)"
+    dq = "qlora::dequantize_nf4_kernel(unsigned int const*, signed char const*)"
+    # an early, larger copy and quantisation that the summary must skip
+    fetch = [(1, "__amd_rocclr_copyBuffer", 10 * kib), (2, q, 5 * n)] + \
+        [(3 + i, q, n * 4 / 1024 / 2.0) for i in range(3)] + \
+        [(6 + i, dq, (n // 2) / 1024 / 2.0) for i in range(3)] + \
+        [(20 + i, "__amd_rocclr_copyBuffer", kib / 2.0) for i in range(3)]
+    write = [(1, "__amd_rocclr_copyBuffer", 10 * kib), (2, q, 5 * n)] + \
+        [(3 + i, q, (n // 2) / 1024) for i in range(3)] + \
+        [(6 + i, dq, 2 * n / 1024) for i in range(3)] + \
+        [(20 + i, "__amd_rocclr_copyBuffer", kib) for i in range(3)]
+    fc, wc = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(fc, "FETCH_SIZE", fetch)
+    _counter_csv(wc, "WRITE_SIZE", write)
+    out = tmp_path / "hbm.txt"
+    bench.summarize_hbm(str(out), str(fc), str(wc))
+    txt = out.read_text()
+    assert "fetch_scale = 2.0000" in txt and "write_scale = 1.0000" in txt
+    line = [ln for ln in txt.splitlines() if ln.startswith("quantise, first level")][0]
+    assert f"read {4 * n} /" in line  # 3 measured dispatches, the early one skipped
+    assert [ln for ln in txt.splitlines() if ln.startswith("dequantise:")]
+
+
+def test_stats_summary_per_grid(tmp_path):
+    trace = tmp_path / "bench_kernel_trace.csv"
+    stats = tmp_path / "bench_kernel_stats.csv"
+    fields = ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Start_Timestamp", "End_Timestamp"]
+    with open(trace, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=fields)
+        w.writeheader()
+        t = 0
+        for i in range(4):  # the bench shape: 688 tiles of 256x256
+            w.writerow({"Kernel_Name": f"void qlora::{bench.FWD_GEMM}(qlora::GemmArgs)",
+                        "Grid_Size_X": 688 * 256, "Grid_Size_Y": 1, "Start_Timestamp": t,
+                        "End_Timestamp": t + 400_000})
+            t += 500_000
+        w.writerow({"Kernel_Name": "qlora::reduce_partials4_kernel()", "Grid_Size_X": 1024,
+                    "Grid_Size_Y": 1, "Start_Timestamp": t, "End_Timestamp": t + 5_000})
+    stats.write_text("Name,Calls\n")
+    log = tmp_path / "log.txt"
+    log.write_text(json.dumps({"metric": "m", "value": 1.0, "ms_per_step": 0.9, "rows": {},
+                               "roofline": {"ms": 0.4},
+                               "config": {"tokens": 4096, "n_out": 11008}}) + "\n")
+    out = tmp_path / "stats.txt"
+    bench.summarize_stats(str(stats), str(log), str(out))
+    txt = out.read_text()
+    assert "--no-rows" in txt
+    assert "grid 176128x1): 4 calls, mean 400.0 us" in txt
