@@ -237,3 +237,25 @@ def test_batches_match_single_calls_and_oracle():
     p3, a3 = quantize_nf4(flats[3])
     q3, c3 = double_quant(a3)
     assert np.array_equal(bf16_bits(outs[i3]).ravel(), dequantize_nf4(p3, q3, c3, sizes[3]))
+
+
+def test_batches_of_one_llama7b_layer_match_single_calls():
+    """The seven matrices of layer 0 of the LLaMA-7B weight set (with their
+    outliers) in one batch: every byte of the quantiser and every decoded
+    value equals the single-weight calls."""
+    say("[quant] batch of the 7 matrices of a LLaMA-7B layer")
+    ws = [to_dev(wl.llama7b_weight(0, m)) for m in range(len(wl.LLAMA7B_MATRICES))]
+    got = q.quantize_nf4_dq_batch([w.reshape(-1) for w in ws])
+    torch.cuda.synchronize()
+    wqs = []
+    for w, g in zip(ws, got):
+        ref = q.quantize_nf4_dq(w.reshape(-1), want_absmax=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(u8(g[0]), u8(ref[0]))
+        assert np.array_equal(u8(g[1]), u8(ref[1]))
+        assert np.array_equal(f32_bits(g[2]), f32_bits(ref[2]))
+        wqs.append(q.NF4Tensor(g[0], g[1], g[2], w.shape[0], w.shape[1]))
+    outs = q.dequantize_nf4_batch(wqs)
+    torch.cuda.synchronize()
+    for wq, o in zip(wqs, outs):
+        assert torch.equal(o.view(torch.int16), q.dequantize_nf4(wq).view(torch.int16))
