@@ -552,7 +552,7 @@ def main():
         Ws = [W] + [W * (1.0 + c * 1e-3) for c in (1, 2)]
         qouts = [q.quantize_nf4_dq(w_, want_absmax=True) for w_ in Ws]
         qcalls = [_c_call(L.qlora_quantize_nf4_dq, q._ptr(w_), n, q._ptr(o[0]), q._ptr(o[1]),
-                          q._ptr(o[2]), q._ptr(o[3]), st) for w_, o in zip(Ws, qouts)]
+                          q._ptr(o[2]), q._ptr(o[3]), None, st) for w_, o in zip(Ws, qouts)]
         it = [0]
 
         def quant_next():
@@ -756,7 +756,7 @@ def weight_set_row(dev):
                 out=torch.empty(n_out, k_in, dtype=torch.bfloat16, device=dev)))
     total = sum(m["n"] for m in mats)
     qcalls = [_c_call(L.qlora_quantize_nf4_dq, q._ptr(m["w"]), m["n"], q._ptr(m["packed"]),
-                      q._ptr(m["qa"]), q._ptr(m["c2"]), q._ptr(m["am"]), st) for m in mats]
+                      q._ptr(m["qa"]), q._ptr(m["c2"]), q._ptr(m["am"]), None, st) for m in mats]
     structs = [q.NF4Weight(m["packed"].data_ptr(), m["qa"].data_ptr(), m["c2"].data_ptr(),
                            m["n_out"], m["k_in"]) for m in mats]
     dcalls = [_c_call(L.qlora_dequantize_nf4, ctypes.byref(sc), q._ptr(m["out"]), st)
@@ -764,7 +764,7 @@ def weight_set_row(dev):
 
     jobs = (q.QuantJob * len(mats))(*[q.QuantJob(m["w"].data_ptr(), m["n"], m["packed"].data_ptr(),
                                                  m["qa"].data_ptr(), m["c2"].data_ptr(),
-                                                 m["am"].data_ptr()) for m in mats])
+                                                 m["am"].data_ptr(), None) for m in mats])
     outs = (ctypes.c_void_p * len(mats))(*[m["out"].data_ptr() for m in mats])
     wsa = (q.NF4Weight * len(mats))(*structs)
     qbatch = _c_call(L.qlora_quantize_nf4_dq_batch, jobs, len(mats), st)

@@ -41,6 +41,7 @@ class QuantJob(ctypes.Structure):
         ("qabsmax", ctypes.c_void_p),
         ("c2", ctypes.c_void_p),
         ("absmax", ctypes.c_void_p),
+        ("nonfinite_flag", ctypes.c_void_p),
     ]
 
 
@@ -78,9 +79,9 @@ _U64 = ctypes.c_uint64
 _W = ctypes.POINTER(NF4Weight)
 
 _SIGNATURES = {
-    "qlora_quantize_nf4": ([_P, _I64, _I32, _P, _P, _P], _I32),
+    "qlora_quantize_nf4": ([_P, _I64, _I32, _P, _P, _P, _P], _I32),
     "qlora_double_quant": ([_P, _I64, _I32, _P, _P, _P], _I32),
-    "qlora_quantize_nf4_dq": ([_P, _I64, _P, _P, _P, _P, _P], _I32),
+    "qlora_quantize_nf4_dq": ([_P, _I64, _P, _P, _P, _P, _P, _P], _I32),
     "qlora_dequantize_nf4": ([_W, _P, _P], _I32),
     "qlora_quantize_nf4_dq_batch": ([_P, _I32, _P], _I32),
     "qlora_dequantize_nf4_batch": ([_P, _P, _I32, _P], _I32),
@@ -186,14 +187,15 @@ def _nblocks(n):
     return (n + BLOCKSIZE - 1) // BLOCKSIZE
 
 
-def quantize_nf4(w):
-    """First level: (packed uint8, absmax float32) of a float32 CUDA tensor."""
+def quantize_nf4(w, nonfinite_flag=None):
+    """First level: (packed uint8, absmax float32) of a float32 CUDA tensor.
+    nonfinite_flag: optional int32 CUDA tensor, set to 1 on NaN / Inf input."""
     n = w.numel()
     nb = _nblocks(n)
     packed = torch.empty(nb * 32, dtype=torch.uint8, device=w.device)
     absmax = torch.empty(nb, dtype=torch.float32, device=w.device)
     _check(lib().qlora_quantize_nf4(_ptr(w), n, BLOCKSIZE, _ptr(packed), _ptr(absmax),
-                                    _stream(w.device)), "qlora_quantize_nf4")
+                                    _ptr(nonfinite_flag), _stream(w.device)), "qlora_quantize_nf4")
     return packed, absmax
 
 
@@ -207,9 +209,10 @@ def double_quant(absmax):
     return q, c2
 
 
-def quantize_nf4_dq(w, want_absmax=False, one_pass=False):
+def quantize_nf4_dq(w, want_absmax=False, one_pass=False, nonfinite_flag=None):
     """Both levels: (packed, qabsmax, c2[, absmax]).  The first-level scales
-    are always given a buffer (the faster two-launch route) unless one_pass."""
+    are always given a buffer (the faster two-launch route) unless one_pass.
+    nonfinite_flag: optional int32 CUDA tensor, set to 1 on NaN / Inf input."""
     n = w.numel()
     nb = _nblocks(n)
     dev = w.device
@@ -218,7 +221,8 @@ def quantize_nf4_dq(w, want_absmax=False, one_pass=False):
     c2 = torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=dev)
     absmax = None if one_pass else torch.empty(nb, dtype=torch.float32, device=dev)
     _check(lib().qlora_quantize_nf4_dq(_ptr(w), n, _ptr(packed), _ptr(q), _ptr(c2),
-                                       _ptr(absmax), _stream(dev)), "qlora_quantize_nf4_dq")
+                                       _ptr(absmax), _ptr(nonfinite_flag), _stream(dev)),
+           "qlora_quantize_nf4_dq")
     return (packed, q, c2, absmax) if want_absmax else (packed, q, c2)
 
 
@@ -229,9 +233,10 @@ def quantize_weight(w):
     return NF4Tensor(packed, q, c2, n_out, k_in)
 
 
-def quantize_nf4_dq_batch(ws):
+def quantize_nf4_dq_batch(ws, nonfinite_flags=None):
     """Both levels for a list of float32 CUDA tensors in batched launches:
-    [(packed, qabsmax, c2, absmax)], the same bytes as quantize_nf4_dq on each."""
+    [(packed, qabsmax, c2, absmax)], the same bytes as quantize_nf4_dq on each.
+    nonfinite_flags: optional list (entries may be None) of int32 CUDA tensors."""
     outs, jobs = [], (QuantJob * max(1, len(ws)))()
     for i, w in enumerate(ws):
         n = w.numel()
@@ -241,7 +246,8 @@ def quantize_nf4_dq_batch(ws):
              torch.empty(nb, dtype=torch.int8, device=dev),
              torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=dev),
              torch.empty(nb, dtype=torch.float32, device=dev))
-        jobs[i] = QuantJob(_ptr(w), n, *(_ptr(t) for t in o))
+        flag = nonfinite_flags[i] if nonfinite_flags is not None else None
+        jobs[i] = QuantJob(_ptr(w), n, *(_ptr(t) for t in o), _ptr(flag))
         outs.append(o)
     if ws:
         _check(lib().qlora_quantize_nf4_dq_batch(jobs, len(ws), _stream(ws[0].device)),

@@ -52,6 +52,7 @@ int device_cus() {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline int64_t rup(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -172,17 +173,22 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t bt, v, vt, ut, at, part, total;
+  size_t bt, v, vt, ut, at, dyp, part, total;
   Plan pv, pdx, pda, pdb;
-  int64_t rp, Mp;
+  int64_t rp, Mp, Np;
 };
 
+// n_out not a multiple of 8: dY is copied to a zero-padded pitch Np (its rows
+// are then 16-byte aligned for the GEMM loaders), and Bᵀ gets the same pitch.
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w{};
   w.rp = rup(r, 8);
   w.Mp = rup(std::max<int64_t>(M, 1), 8);
+  w.Np = rup(N, 8);
   size_t off = 0;
-  w.bt = off; off += align256((size_t)r * N * 2);
+  w.bt = off; off += align256((size_t)r * w.Np * 2);
+  w.dyp = off;
+  if (w.Np != N) off += align256((size_t)M * w.Np * 2);
   w.v = off; off += align256((size_t)M * w.rp * 2);
   w.vt = off; off += align256((size_t)r * w.Mp * 2);
   w.ut = off; off += align256((size_t)r * w.Mp * 2);
@@ -259,7 +265,7 @@ qlora_status validate_linear(const qlora_nf4_weight* w, int64_t M, int32_t r) {
   qlora_status s = validate_weight(w);
   if (s != QLORA_OK) return s;
   QCHECK(M >= 0, QLORA_ERR_SHAPE);
-  QCHECK(w->k_in % 64 == 0 && w->n_out % 8 == 0, QLORA_ERR_SHAPE);
+  QCHECK(w->k_in % 64 == 0, QLORA_ERR_SHAPE);
   QCHECK(w->n_out > 0 && w->k_in > 0, QLORA_ERR_SHAPE);
   QCHECK(r >= 1 && r <= QLORA_MAX_RANK, QLORA_ERR_UNSUPPORTED);
   return QLORA_OK;
@@ -459,19 +465,30 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
                       ReduceOut{nullptr, dB, (int64_t)r, 0}, kNoOut, st);
   }
 
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + L.bt);  // [r][N]
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + L.bt);  // [r][Np]
   uint16_t* V = reinterpret_cast<uint16_t*>(ws + L.v);    // [M][rp]
   uint16_t* Vt = reinterpret_cast<uint16_t*>(ws + L.vt);  // [r][Mp]
   uint16_t* Ut = reinterpret_cast<uint16_t*>(ws + L.ut);  // [r][Mp]
   uint16_t* At = reinterpret_cast<uint16_t*>(ws + L.at);  // [K][rp]
   float* part = reinterpret_cast<float*>(ws + L.part);
 
+  // dY with a 16-byte aligned row pitch (only when n_out % 8 != 0)
+  const int64_t ldy = L.Np;
+  const uint16_t* dYa = dY;
+  if (L.Np != N) {
+    uint16_t* dYp = reinterpret_cast<uint16_t*>(ws + L.dyp);
+    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(M * L.Np)), dim3(256), 0, st, dY, N, M, N,
+                       L.Np, dYp, L.Np);
+    if ((s = launched()) != QLORA_OK) return s;
+    dYa = dYp;
+  }
+
   // adapter factors in the layouts the GEMMs read
   {
-    const TransposeJob jb{B, (int64_t)r, N, (int64_t)r, N, (int64_t)r, Bt, N};
+    const TransposeJob jb{B, (int64_t)r, N, (int64_t)r, L.Np, (int64_t)r, Bt, L.Np};
     const TransposeJob ju{U, (int64_t)r, M, (int64_t)r, L.Mp, (int64_t)r, Ut, L.Mp};
     const TransposeJob ja{A, K, (int64_t)r, K, L.rp, K, At, L.rp};
-    const int64_t tiles = std::max({ceil_div(N, 64) * ceil_div(r, 64), ceil_div(L.Mp, 64) * ceil_div(r, 64),
+    const int64_t tiles = std::max({ceil_div(L.Np, 64) * ceil_div(r, 64), ceil_div(L.Mp, 64) * ceil_div(r, 64),
                                     ceil_div(L.rp, 64) * ceil_div(K, 64)});
     hipLaunchKernelGGL(transpose_pad3_kernel, dim3((unsigned)std::min<int64_t>(tiles, 1024), 3),
                        dim3(256), 0, st, jb, ju, ja);
@@ -479,10 +496,11 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
   if ((s = launched()) != QLORA_OK) return s;
 
   // V = dY·B  -> V [M][rp] (zero-padded) and Vᵀ [r][Mp] (zero-padded), bf16
+  // (over the padded pitch: both operands hold zeros past n_out)
   {
     GemmArgs g{};
-    g.a = dY; g.lda = N; g.rows = M; g.cols = r; g.red = N;
-    g.b = Bt; g.ldb = N;
+    g.a = dYa; g.lda = ldy; g.rows = M; g.cols = r; g.red = L.Np;
+    g.b = Bt; g.ldb = L.Np;
     g.out_f32 = part;
     g.ldo = (int64_t)L.pv.tiles_n * SK_NT;
     g.part_stride = M * g.ldo;
@@ -517,10 +535,11 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
       return s;
   }
 
-  // dX = dY·Ŵ + s·V·A  (with dropout: dY·Ŵ + T)
+  // dX = dY·Ŵ + s·V·A  (with dropout: dY·Ŵ + T); W rows past n_out read as
+  // zero, so a chunk of dY that straddles n_out meets zeros on both sides
   {
     GemmArgs g{};
-    g.a = dY; g.lda = N; g.rows = M; g.cols = K; g.red = N;
+    g.a = dYa; g.lda = ldy; g.rows = M; g.cols = K; g.red = N;
     g.packed = w->packed; g.qabsmax = w->qabsmax; g.c2 = w->c2; g.w_kin = K;
     g.pl = V; g.ldpl = L.rp; g.pr = At; g.ldpr = L.rp; g.rl = r; g.s = sc;
     g.s_split = needs_split(sc);
@@ -559,7 +578,7 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
   {
     GemmArgs g{};
     g.a = Ut; g.lda = L.Mp; g.rows = r; g.cols = N; g.red = M;
-    g.b = dY; g.ldb = N;
+    g.b = dYa; g.ldb = ldy;
     g.out_f32 = part; g.ldo = N; g.part_stride = (int64_t)r * N;
     if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pdb, st)) != QLORA_OK)
       return s;
@@ -655,9 +674,10 @@ size_t qlora_workspace_size(int32_t op, int64_t M, int64_t n_out, int64_t k_in, 
 }
 
 qlora_status qlora_quantize_nf4(const float* w, int64_t n, int32_t blocksize, uint8_t* packed,
-                                float* absmax, void* stream) {
+                                float* absmax, int32_t* nonfinite_flag, void* stream) {
   QCHECK(n >= 0, QLORA_ERR_SHAPE);
   QCHECK(blocksize == QLORA_BLOCKSIZE, QLORA_ERR_UNSUPPORTED);
+  QCHECK(aligned4(nonfinite_flag), QLORA_ERR_ALIGN);
   if (n == 0) return QLORA_OK;
   ALIGNED_OR_NULL(w);
   ALIGNED_OR_NULL(packed);
@@ -668,7 +688,7 @@ qlora_status qlora_quantize_nf4(const float* w, int64_t n, int32_t blocksize, ui
   const int64_t threads = nb * 4;
   QCHECK(ceil_div(threads, 256) <= 0x7fffffff, QLORA_ERR_SHAPE);
   hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0,
-                     as_stream(stream), w, n, nb, packed, absmax);
+                     as_stream(stream), w, n, nb, packed, absmax, nonfinite_flag);
   return launched();
 }
 
@@ -687,7 +707,7 @@ qlora_status qlora_quantize_4bit(const float* w, int64_t n, int32_t code, uint8_
   QCHECK(grid <= 0x7fffffff, QLORA_ERR_SHAPE);
   if (code == QLORA_CODE_NF4)
     hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
-                       w, n, nb, packed, absmax);
+                       w, n, nb, packed, absmax, static_cast<int32_t*>(nullptr));
   else
     hipLaunchKernelGGL(quantize_int4_kernel, dim3((unsigned)grid), dim3(256), 0,
                        as_stream(stream), w, n, nb, packed, absmax);
@@ -829,8 +849,10 @@ qlora_status qlora_double_quant(const float* absmax, int64_t nblocks, int32_t gr
 }
 
 qlora_status qlora_quantize_nf4_dq(const float* w, int64_t n, uint8_t* packed, int8_t* qabsmax,
-                                   float* c2, float* absmax, void* stream) {
+                                   float* c2, float* absmax, int32_t* nonfinite_flag,
+                                   void* stream) {
   QCHECK(n >= 0, QLORA_ERR_SHAPE);
+  QCHECK(aligned4(nonfinite_flag), QLORA_ERR_ALIGN);
   if (n == 0) return QLORA_OK;
   ALIGNED_OR_NULL(w);
   ALIGNED_OR_NULL(packed);
@@ -850,7 +872,7 @@ qlora_status qlora_quantize_nf4_dq(const float* w, int64_t n, uint8_t* packed, i
     // level from the scales — measured faster than the one-pass kernel
     // despite writing and re-reading 4 bytes per 64 weights.
     hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)ceil_div(nb * 4, 256)), dim3(256), 0, st,
-                       w, n, nb, packed, absmax);
+                       w, n, nb, packed, absmax, nonfinite_flag);
     hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)ng), dim3(256), 0, st,
                        (const float*)absmax, nb, qabsmax, c2);
     return launched();
@@ -859,7 +881,7 @@ qlora_status qlora_quantize_nf4_dq(const float* w, int64_t n, uint8_t* packed, i
   // flight, and every workgroup overlaps its loads with its own arithmetic)
   const int64_t grid = std::min<int64_t>(ng, 4 * (int64_t)device_cus());
   hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)grid), dim3(256), 0, st, w, n, nb,
-                     packed, qabsmax, c2, absmax);
+                     packed, qabsmax, c2, absmax, nonfinite_flag);
   return launched();
 }
 
@@ -893,6 +915,7 @@ qlora_status qlora_quantize_nf4_dq_batch(const qlora_quant_job* jobs, int32_t co
     ALIGNED_OR_NULL(j.qabsmax);
     ALIGNED_OR_NULL(j.c2);
     ALIGNED_OR_NULL(j.absmax);
+    QCHECK(aligned4(j.nonfinite_flag), QLORA_ERR_ALIGN);
     QCHECK(ceil_div(ceil_div(j.n, 64) * 4, 256) <= 0x7fffffff, QLORA_ERR_SHAPE);
   }
   qlora_status s = check_device();
@@ -911,7 +934,7 @@ qlora_status qlora_quantize_nf4_dq_batch(const qlora_quant_job* jobs, int32_t co
       if (j.n == 0) continue;
       const int64_t nb = ceil_div(j.n, 64), ng = ceil_div(nb, 256), nwg = ceil_div(nb * 4, 256);
       if (wq + nwg > 0x7fffffff || wd + ng > 0x7fffffff) break;  // the next launch takes it
-      qb.j[c] = QuantJob1{j.w, j.n, j.packed, j.absmax};
+      qb.j[c] = QuantJob1{j.w, j.n, j.packed, j.absmax, j.nonfinite_flag};
       qb.wg0[c] = wq;
       db.j[c] = DqJob{j.absmax, nb, j.qabsmax, j.c2};
       db.wg0[c] = wd;

@@ -86,7 +86,7 @@ __global__ void lora_down_small_kernel(const uint16_t* x, int64_t K, const uint1
                                        uint16_t* u);
 
 __global__ void quantize_nf4_kernel(const float* w, int64_t n, int64_t nblocks, uint8_t* packed,
-                                    float* absmax);
+                                    float* absmax, int32_t* nonfinite);
 __global__ void double_quant_kernel(const float* absmax, int64_t nblocks, int8_t* qabsmax,
                                     float* c2);
 
@@ -98,6 +98,7 @@ struct QuantJob1 {  // first level: blocks of 64 -> codes and float32 scales
   int64_t n;
   uint8_t* packed;
   float* absmax;
+  int32_t* nonfinite;  // optional flag, set to 1 on NaN / Inf input
 };
 struct QuantBatch {
   QuantJob1 j[kBatchMax];
@@ -131,7 +132,8 @@ __global__ void quantize_nf4_batch_kernel(QuantBatch b);
 __global__ void double_quant_batch_kernel(DqBatch b);
 __global__ void dequantize_nf4_batch_kernel(DeqBatch b);
 __global__ void quantize_nf4_dq_kernel(const float* w, int64_t n, int64_t nblocks, uint8_t* packed,
-                                       int8_t* qabsmax, float* c2, float* absmax_out);
+                                       int8_t* qabsmax, float* c2, float* absmax_out,
+                                       int32_t* nonfinite);
 __global__ void dequantize_nf4_kernel(const uint32_t* packed, const int8_t* qabsmax, const float* c2,
                                       int64_t ndwords, u32x4* out);
 __global__ void reduce_partials_kernel(const float* part, int64_t part_stride, int32_t nsplit,

@@ -135,6 +135,28 @@ constexpr BucketTable kBuckets = make_buckets(kMid<CODE>);
 
 constexpr int kTStride = 17;  // floats per block in the LDS threshold table (bank spread)
 
+// Power of two that brings a block maximum m > 0 into [2^-64, 2^64] for the
+// bucket estimate: 1/(m·sc) is then a normal float32.  x·sc is exact for
+// normal results; a value that underflows in it is below 2^-85 of m and lands
+// in the zero bucket either way.
+__device__ inline float estimate_scale(float m) {
+  return (m < 0x1p-64f) ? 0x1p64f : ((m > 0x1p64f) ? 0x1p-64f : 1.0f);
+}
+
+// 1 when any of the values is NaN or ±Inf (the precondition is finite input).
+__device__ inline bool any_nonfinite4(const floatx4& x) {
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) bad |= !__builtin_isfinite(x[u]);
+  return bad;
+}
+
+// Flags non-finite input: every lane that saw one stores 1 (a vector store;
+// the flag is never cleared here, the caller zeroes it beforehand).
+__device__ inline void flag_nonfinite(int32_t* flag, bool bad) {
+  if (flag != nullptr && bad) *reinterpret_cast<volatile int32_t*>(flag) = 1;
+}
+
 // One lane handles 16 consecutive elements; 4 lanes form one 64-block.
 // T: this block's 16-entry threshold row in LDS (T[15] = +inf); bk: bucket table.
 // Block absmax (over the block's 4 lanes) and the codes of 16 loaded values.
@@ -156,9 +178,10 @@ __device__ inline float quantize_16v(const float (&v)[16], int sub, float* __res
 
   uint32_t lo = Code<CODE>::zero_word, hi = Code<CODE>::zero_word;  // all-zero block
   if (m > 0.0f) {
-    // the estimate only picks a bucket; a power-of-two rescale keeps 1/m finite
-    // for subnormal block maxima without changing any ratio
-    const float sc = (m < 0x1p-64f) ? 0x1p64f : 1.0f;
+    // the estimate only picks a bucket; a power-of-two rescale keeps 1/m a
+    // normal float32 for subnormal and for huge block maxima (v_rcp_f32
+    // returns no subnormal results) without changing any ratio
+    const float sc = estimate_scale(m);
     // 32 / (m·sc) to within a couple of ulp (v_rcp: the estimate only picks a
     // bucket): b = trunc(32 x + 32) in one fma, and |x| <= 1 + 2^-21 keeps b
     // in [0, 64]
@@ -232,7 +255,7 @@ __device__ inline void load_16(const uint16_t* __restrict__ w, int64_t n, int64_
 template <int CODE>
 __device__ inline void quantize_blocks(const float* __restrict__ w, int64_t n, int64_t nblocks,
                                        uint8_t* __restrict__ packed, float* __restrict__ absmax,
-                                       int64_t wg) {
+                                       int64_t wg, int32_t* __restrict__ nonfinite) {
   __shared__ uint8_t bk[kNBuckets];
   const int t = threadIdx.x;
   if (t < kNBuckets) bk[t] = kBuckets<CODE>.first[t];
@@ -248,6 +271,12 @@ __device__ inline void quantize_blocks(const float* __restrict__ w, int64_t n, i
 #pragma unroll
       for (int u = 0; u < 4; ++u) x[j][u] = (e + u < n) ? w[e + u] : 0.0f;
     }
+  }
+  if (nonfinite != nullptr) {
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bad |= any_nonfinite4(x[j]);
+    flag_nonfinite(nonfinite, bad);
   }
   const int lb = t & 15;                     // lane within its block
   const int src0 = t & 48;                   // the block's first lane within the wave
@@ -267,7 +296,7 @@ __device__ inline void quantize_blocks(const float* __restrict__ w, int64_t n, i
     // |x| <= 1 + 2^-21 keeps b in [0, 64] (an all-zero block uses bucket 32
     // and its codes are replaced below)
     const bool nz = m > 0.0f;
-    const float sc = (m < 0x1p-64f) ? 0x1p64f : 1.0f;
+    const float sc = estimate_scale(m);
     const float k32 = nz ? 32.0f * __builtin_amdgcn_rcpf(m * sc) : 0.0f;
     uint32_t code = 0u;
 #pragma unroll
@@ -290,15 +319,16 @@ __device__ inline void quantize_blocks(const float* __restrict__ w, int64_t n, i
 __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ w, int64_t n,
                                                            int64_t nblocks,
                                                            uint8_t* __restrict__ packed,
-                                                           float* __restrict__ absmax) {
-  quantize_blocks<kCodeNF4>(w, n, nblocks, packed, absmax, blockIdx.x);
+                                                           float* __restrict__ absmax,
+                                                           int32_t* __restrict__ nonfinite) {
+  quantize_blocks<kCodeNF4>(w, n, nblocks, packed, absmax, blockIdx.x, nonfinite);
 }
 
 __global__ __launch_bounds__(256) void quantize_int4_kernel(const float* __restrict__ w, int64_t n,
                                                             int64_t nblocks,
                                                             uint8_t* __restrict__ packed,
                                                             float* __restrict__ absmax) {
-  quantize_blocks<kCodeINT4>(w, n, nblocks, packed, absmax, blockIdx.x);
+  quantize_blocks<kCodeINT4>(w, n, nblocks, packed, absmax, blockIdx.x, nullptr);
 }
 
 namespace {
@@ -351,7 +381,7 @@ __global__ __launch_bounds__(256) void quantize_nf4_batch_kernel(QuantBatch b) {
   const int i = batch_job(b.wg0, b.count, blockIdx.x);
   const QuantJob1& J = b.j[i];
   quantize_blocks<kCodeNF4>(J.w, J.n, (J.n + kBlock - 1) / kBlock, J.packed, J.absmax,
-                            blockIdx.x - b.wg0[i]);
+                            blockIdx.x - b.wg0[i], J.nonfinite);
 }
 
 __global__ __launch_bounds__(256) void double_quant_batch_kernel(DqBatch b) {
@@ -368,7 +398,8 @@ template <typename In>
 __device__ inline void quantize_dq_groups(const In* __restrict__ w, int64_t n, int64_t nblocks,
                                           uint8_t* __restrict__ packed,
                                           int8_t* __restrict__ qabsmax, float* __restrict__ c2,
-                                          float* __restrict__ absmax_out) {
+                                          float* __restrict__ absmax_out,
+                                          int32_t* __restrict__ nonfinite) {
   __shared__ float amax[kGroup];
   __shared__ float red[4];
   __shared__ float thr[64 * kTStride];
@@ -397,6 +428,13 @@ __device__ inline void quantize_dq_groups(const In* __restrict__ w, int64_t n, i
       const int64_t blk = g * kGroup + lb;
       float m = 0.0f;
       if (blk < nblocks) {
+        if (nonfinite != nullptr) {  // (registers of blocks past the end were never loaded)
+          bool bad = false;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            bad |= any_nonfinite4(floatx4{cur[4 * j], cur[4 * j + 1], cur[4 * j + 2], cur[4 * j + 3]});
+          flag_nonfinite(nonfinite, bad);
+        }
         u32x2 bytes;
         m = quantize_16v<kCodeNF4>(cur, sub, thr + (t >> 2) * kTStride, bk, bytes);
         *reinterpret_cast<u32x2*>(packed + blk * 32 + sub * 8) = bytes;
@@ -429,8 +467,9 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
                                                               uint8_t* __restrict__ packed,
                                                               int8_t* __restrict__ qabsmax,
                                                               float* __restrict__ c2,
-                                                              float* __restrict__ absmax_out) {
-  quantize_dq_groups(w, n, nblocks, packed, qabsmax, c2, absmax_out);
+                                                              float* __restrict__ absmax_out,
+                                                              int32_t* __restrict__ nonfinite) {
+  quantize_dq_groups(w, n, nblocks, packed, qabsmax, c2, absmax_out, nonfinite);
 }
 
 // The same from a bf16 weight (the merged 16-bit weight of an adapter merge).
@@ -439,7 +478,8 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_bf16_kernel(const uint16_
                                                                    uint8_t* __restrict__ packed,
                                                                    int8_t* __restrict__ qabsmax,
                                                                    float* __restrict__ c2) {
-  quantize_dq_groups(w, n, nblocks, packed, qabsmax, c2, static_cast<float*>(nullptr));
+  quantize_dq_groups(w, n, nblocks, packed, qabsmax, c2, static_cast<float*>(nullptr),
+                     static_cast<int32_t*>(nullptr));
 }
 
 // Standalone dequantisation to bf16.  A workgroup decodes 1024 consecutive

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QLORA_ABI_VERSION 1
+#define QLORA_ABI_VERSION 2
 #define QLORA_BLOCKSIZE 64   /* first-level block (NF4), elements */
 #define QLORA_DQ_GROUP 256   /* second-level group, blocks */
 #define QLORA_MAX_RANK 256
@@ -65,7 +65,7 @@ typedef enum {
  *   packed  : n_out*k_in/2 bytes; byte t = idx[2t] | idx[2t+1] << 4 (flat order)
  *   qabsmax : n_out*k_in/64 second-level codes, values in [0, 127]
  *   c2      : ceil(n_out*k_in/64/256) float32 second-level constants
- *   k_in % 64 == 0 and n_out % 8 == 0 for the linear entry points. */
+ *   k_in % 64 == 0 for the linear entry points (any n_out >= 1). */
 typedef struct {
   const uint8_t *packed;
   const int8_t *qabsmax;
@@ -83,9 +83,16 @@ typedef struct {
  *               going to the lower index; an all-zero block and every padded
  *               slot get index 8 (the exact-zero level).
  * Outputs: packed[ceil(n/64)*32] bytes (two indices per byte, even element in
- * the low nibble) and absmax[ceil(n/64)] float32.  n >= 0; blocksize must be 64. */
+ * the low nibble) and absmax[ceil(n/64)] float32.  n >= 0; blocksize must be 64.
+ * Block maxima anywhere in the finite float32 range (subnormal up to FLT_MAX)
+ * get the exact decision.
+ * nonfinite_flag (optional device int32, 4-byte aligned; NULL = not wanted):
+ * set to 1 when any w[i] is NaN or ±Inf, left untouched otherwise — the caller
+ * zeroes it beforehand.  Non-finite input breaks the finite-input
+ * precondition: its codes and scales are unspecified, the flag is the only
+ * defined result. */
 qlora_status qlora_quantize_nf4(const float *w, int64_t n, int32_t blocksize, uint8_t *packed,
-                                float *absmax, void *stream);
+                                float *absmax, int32_t *nonfinite_flag, void *stream);
 
 /* Second level ("QLoRAの理論と実装", §5-2; Qiita explainer, DQ formula).  Groups of
  * 256 consecutive blocks (the last may be short):
@@ -100,9 +107,11 @@ qlora_status qlora_double_quant(const float *absmax, int64_t nblocks, int32_t gr
 /* Both levels.  Produces exactly the bytes that qlora_quantize_nf4 followed by
  * qlora_double_quant produce.  absmax (float32 [ceil(n/64)], optional)
  * receives the first-level scales; given it, the two levels run as those two
- * launches (the faster route), without it as one pass over w. */
+ * launches (the faster route), without it as one pass over w.
+ * nonfinite_flag: optional, as for qlora_quantize_nf4. */
 qlora_status qlora_quantize_nf4_dq(const float *w, int64_t n, uint8_t *packed, int8_t *qabsmax,
-                                   float *c2, float *absmax, void *stream);
+                                   float *c2, float *absmax, int32_t *nonfinite_flag,
+                                   void *stream);
 
 /* Dequantisation ("QLoRAの理論と実装", §5-1 step 3, in the DQ order):
  *   â = RN32(c2[b/256] · qabsmax[b]);  out = RNE_bf16(RN32(c[idx] · â)).
@@ -133,6 +142,7 @@ typedef struct {
   int8_t *qabsmax;    /* ceil(n/64) DQ codes                        */
   float *c2;          /* ceil(n/16384) second-level steps           */
   float *absmax;      /* ceil(n/64) first-level scales (written)    */
+  int32_t *nonfinite_flag; /* optional (NULL): set to 1 on NaN / Inf  */
 } qlora_quant_job;
 qlora_status qlora_quantize_nf4_dq_batch(const qlora_quant_job *jobs /* host */, int32_t count,
                                          void *stream);

@@ -73,6 +73,38 @@ def oracle_weight(W):
     return dict(packed=packed, absmax=absmax, q=q, c2=c2, w_hat=w_hat, w64=bf16_to_f64(w_hat))
 
 
+def host_threads():
+    """Host threads the parity harness may use (the CPU share this process has,
+    at most 16)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_weight_parallel(W, threads=None, chunk_groups=64):
+    """oracle_weight(W) computed over flat ranges of whole DQ groups (16384
+    elements each) in a thread pool, then joined.  DQ groups are independent
+    of each other (each has its own absmax values, c2 and codes), so the
+    joined arrays are exactly the whole-weight oracle's; a CPU test checks
+    that on a ragged weight."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    flat = np.ascontiguousarray(W, dtype=np.float32).ravel()
+    step = 64 * 256 * chunk_groups
+    starts = list(range(0, flat.size, step)) or [0]
+
+    def one(s0):
+        part = flat[s0:s0 + step]
+        packed, absmax = quantize_nf4(part)
+        q, c2 = double_quant(absmax)
+        return packed, absmax, q, c2, dequantize_nf4(packed, q, c2, part.size)
+
+    with ThreadPoolExecutor(threads or host_threads()) as ex:
+        parts = list(ex.map(one, starts))
+    packed, absmax, q, c2, w_hat = (np.concatenate([p[i] for p in parts]) for i in range(5))
+    w_hat = w_hat.reshape(W.shape)
+    return dict(packed=packed, absmax=absmax, q=q, c2=c2, w_hat=w_hat)
+
+
 def oracle_rows(W, r0, r1):
     """Oracle decode of rows [r0, r1) of W computed from whole DQ groups only
     (groups are independent), so a full-size weight can be spot-checked."""

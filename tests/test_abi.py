@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_strings(L):
-    assert q.abi_version() == 1
+    assert q.abi_version() == 2
     for s in range(8):
         assert q.status_string(s).startswith(q.STATUS[s])
 
@@ -58,19 +58,21 @@ def test_workspace_size(L):
 
 def test_quantize_argument_errors(L):
     f = L.qlora_quantize_nf4
-    assert f(FAKE, 100, 32, FAKE, FAKE, None) == UNSUP
-    assert f(FAKE, -1, 64, FAKE, FAKE, None) == SHAPE
-    assert f(None, 100, 64, FAKE, FAKE, None) == NULL
-    assert f(FAKE, 100, 64, None, FAKE, None) == NULL
-    assert f(MIS, 100, 64, FAKE, FAKE, None) == ALIGN
-    assert f(FAKE, 0, 64, None, None, None) == OK  # nothing to do
+    assert f(FAKE, 100, 32, FAKE, FAKE, None, None) == UNSUP
+    assert f(FAKE, -1, 64, FAKE, FAKE, None, None) == SHAPE
+    assert f(None, 100, 64, FAKE, FAKE, None, None) == NULL
+    assert f(FAKE, 100, 64, None, FAKE, None, None) == NULL
+    assert f(MIS, 100, 64, FAKE, FAKE, None, None) == ALIGN
+    assert f(FAKE, 100, 64, FAKE, FAKE, FAKE + 2, None) == ALIGN  # the flag is an int32
+    assert f(FAKE, 0, 64, None, None, None, None) == OK  # nothing to do
     g = L.qlora_double_quant
     assert g(FAKE, 10, 128, FAKE, FAKE, None) == UNSUP
     assert g(FAKE, 10, 256, MIS, FAKE, None) == ALIGN
     assert g(FAKE, -5, 256, FAKE, FAKE, None) == SHAPE
     h = L.qlora_quantize_nf4_dq
-    assert h(FAKE, 10, FAKE, FAKE, None, None, None) == NULL
-    assert h(FAKE, 10, FAKE, FAKE, FAKE, MIS, None) == ALIGN
+    assert h(FAKE, 10, FAKE, FAKE, None, None, None, None) == NULL
+    assert h(FAKE, 10, FAKE, FAKE, FAKE, MIS, None, None) == ALIGN
+    assert h(FAKE, 10, FAKE, FAKE, FAKE, None, FAKE + 1, None) == ALIGN
 
 
 def _weight(n_out=64, k_in=128, packed=FAKE):
@@ -86,7 +88,8 @@ def test_linear_argument_errors(L):
     assert call(args(r=257)) == UNSUP
     assert call(args(M=-1)) == SHAPE
     assert call(args(w=_weight(k_in=100))) == SHAPE
-    assert call(args(w=_weight(n_out=60))) == SHAPE
+    assert call(args(w=_weight(n_out=0))) == SHAPE
+    assert call(args(w=_weight(n_out=-3))) == SHAPE
     assert call(args(w=_weight(packed=None))) == NULL
     assert call(args(w=_weight(packed=MIS))) == ALIGN
     assert call(args(X=None)) == NULL
@@ -109,12 +112,14 @@ def test_batch_argument_errors(L):
     assert qb(None, 0, None) == OK
     assert qb(None, -1, None) == SHAPE
     assert qb(None, 2, None) == NULL
-    jobs = (q.QuantJob * 2)(q.QuantJob(FAKE, 100, FAKE, FAKE, FAKE, FAKE),
-                            q.QuantJob(FAKE, 64, FAKE, FAKE, FAKE, None))
+    jobs = (q.QuantJob * 2)(q.QuantJob(FAKE, 100, FAKE, FAKE, FAKE, FAKE, None),
+                            q.QuantJob(FAKE, 64, FAKE, FAKE, FAKE, None, None))
     assert qb(jobs, 2, None) == NULL  # the first-level scales need a buffer
-    jobs[1] = q.QuantJob(FAKE, 64, FAKE, MIS, FAKE, FAKE)
+    jobs[1] = q.QuantJob(FAKE, 64, FAKE, MIS, FAKE, FAKE, None)
     assert qb(jobs, 2, None) == ALIGN
-    jobs[1] = q.QuantJob(FAKE, -5, FAKE, FAKE, FAKE, FAKE)
+    jobs[1] = q.QuantJob(FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE + 2)
+    assert qb(jobs, 2, None) == ALIGN
+    jobs[1] = q.QuantJob(FAKE, -5, FAKE, FAKE, FAKE, FAKE, None)
     assert qb(jobs, 2, None) == SHAPE
     assert db(None, None, 0, None) == OK
     assert db(None, None, -1, None) == SHAPE
@@ -134,9 +139,10 @@ def test_valid_arguments_without_gpu_report_device(L):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert L.qlora_quantize_nf4(FAKE, 100, 64, FAKE, FAKE, None) == DEV
-    jobs = (q.QuantJob * 2)(q.QuantJob(FAKE, 100, FAKE, FAKE, FAKE, FAKE),
-                            q.QuantJob(None, 0, None, None, None, None))  # an empty job is skipped
+    assert L.qlora_quantize_nf4(FAKE, 100, 64, FAKE, FAKE, None, None) == DEV
+    assert L.qlora_quantize_nf4(FAKE, 100, 64, FAKE, FAKE, FAKE, None) == DEV
+    jobs = (q.QuantJob * 2)(q.QuantJob(FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE),
+                            q.QuantJob(None, 0, None, None, None, None, None))  # an empty job is skipped
     assert L.qlora_quantize_nf4_dq_batch(jobs, 2, None) == DEV
     ws = (q.NF4Weight * 1)(q.NF4Weight(FAKE, FAKE, FAKE, 4, 16))
     assert L.qlora_dequantize_nf4_batch(ws, (ctypes.c_void_p * 1)(FAKE), 1, None) == DEV

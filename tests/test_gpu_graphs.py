@@ -138,7 +138,7 @@ def test_adamw_and_quantiser_graph():
 
     def run_quant():
         lib.qlora_quantize_nf4_dq(q._ptr(W), W.numel(), q._ptr(packed), q._ptr(qa), q._ptr(c2),
-                                  None, q._stream(dev))
+                                  None, None, q._stream(dev))
 
     run_opt()
     run_quant()

@@ -10,10 +10,8 @@ import torch
 
 import workloads as wl
 from oracle.linear import linear_bwd, linear_fwd, lora_scale
-from oracle.quant import bf16_to_f64
 
-from support import (TOL, assert_close, bf16_bits, guarded, host, oracle_rows, oracle_weight, say,
-                     to_dev)
+from support import assert_close, bf16_bits, guarded, host, oracle_weight, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +80,12 @@ def _run_case(M, K, N, r, alpha, seed, bwd=True):
     (256, 512, 264, 256, 16.0),   # largest rank, many-token path
     (40, 256, 96, 256, 64.0),     # largest rank, split-K path
     (3, 512, 64, 256, 16.0),      # largest rank, few-token path
+    (3, 256, 75, 8, 16.0),        # n_out not a multiple of 8: few-token path
+    (40, 192, 75, 8, 16.0),       # ... split-K path
+    (300, 128, 75, 16, 16.0),     # ... many-token path
+    (257, 320, 1001, 64, 16.0),   # ... many-token path, several column tiles
+    (130, 64, 13, 3, 16.0),       # ... with a rank that is not a multiple of 8
+    (21, 128, 1, 1, 2.0),         # a single output column
 ])
 def test_small_shapes(M, K, N, r, alpha):
     _run_case(M, K, N, r, alpha, seed=M + K + N + r)
@@ -198,56 +202,3 @@ def test_llama7b_mlp_full_fwd_bwd():
     assert_close("dX", _f64(dX), dXr)
     assert_close("dA", _f64(dA), dAr)
     assert_close("dB", _f64(dB), dBr)
-
-
-@pytest.mark.parametrize("M", [1, 2, 5, 8])
-def test_gemv_70b_full_sampled_outputs(M):
-    """8192 -> 28672, r = 16, few tokens: the GPU computes every output; the
-    oracle checks all tokens on output rows sampled over whole DQ groups."""
-    wlc = wl.GEMV_70B
-    say(f"[full] {wlc.name} M={M}")
-    inp = wlc.inputs(M=M)
-    W = inp["W"]
-    wq = q.quantize_weight(to_dev(W))
-    Y, U = q.linear_fwd(wq, to_dev(inp["X"]), to_dev(inp["A"]), to_dev(inp["B"]), wlc.alpha)
-    Yh = _f64(Y)
-    s = lora_scale(wlc.alpha, wlc.r)
-    X64, A64, B64 = (_f64(inp[k]) for k in ("X", "A", "B"))
-    Ur = X64 @ A64.T
-    assert_close("U", _f64(U), Ur)
-    rng = np.random.default_rng(M)
-    rows = sorted(set([0, wlc.n_out - 2] + [int(x) * 2 for x in rng.integers(0, wlc.n_out // 2, 24)]))
-    for r0 in rows:
-        o = oracle_rows(W, r0, r0 + 2)
-        Yr, _ = linear_fwd(X64, bf16_to_f64(o["w_hat"]), A64, B64[r0:r0 + 2], s)
-        ref_scale = np.max(np.abs(Yh))  # the per-tensor bound uses the whole output's scale
-        err = np.max(np.abs(Yh[:, r0:r0 + 2] - Yr))
-        assert err <= TOL * ref_scale, (r0, err, ref_scale)
-
-
-@pytest.mark.parametrize("proj", [3, 6])  # o 8192x8192, down 22016->8192
-def test_llama65b_projection_full(proj):
-    """2048 tokens, r = 64: Y and dX on sampled token rows, dA, dB and U in full."""
-    wlc = wl.LLAMA65B_LAYER[proj]
-    say(f"[full] {wlc.name}")
-    inp = wlc.inputs()
-    o = oracle_weight(inp["W"])
-    wq = q.quantize_weight(to_dev(inp["W"]))
-    Xd, Ad, Bd, dYd = (to_dev(inp[k]) for k in ("X", "A", "B", "dY"))
-    Y, U = q.linear_fwd(wq, Xd, Ad, Bd, wlc.alpha)
-    dX, dA, dB = q.linear_bwd(wq, Xd, dYd, Ad, Bd, U, wlc.alpha)
-    s = lora_scale(wlc.alpha, wlc.r)
-    X64, A64, B64, dY64 = (_f64(inp[k]) for k in ("X", "A", "B", "dY"))
-    rows = np.random.default_rng(proj).choice(wlc.M, 64, replace=False)
-    rows = np.sort(np.concatenate([rows, [0, wlc.M - 1]]))
-    Yr, _ = linear_fwd(X64[rows], o["w64"], A64, B64, s)
-    Yf = _f64(Y)
-    assert np.max(np.abs(Yf[rows] - Yr)) <= TOL * np.max(np.abs(Yr))
-    Ur = X64 @ A64.T
-    assert_close("U", _f64(U), Ur)
-    V = dY64 @ B64
-    dXr = dY64[rows] @ o["w64"] + s * (V[rows] @ A64)
-    dXf = _f64(dX)
-    assert np.max(np.abs(dXf[rows] - dXr)) <= TOL * np.max(np.abs(dXr))
-    assert_close("dA", _f64(dA), s * (V.T @ X64))
-    assert_close("dB", _f64(dB), s * (dY64.T @ Ur))

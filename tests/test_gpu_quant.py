@@ -9,7 +9,7 @@ import workloads as wl
 from oracle.codebook import nf4_codebook_f32, nf4_midpoints_f64
 from oracle.quant import block_absmax, dequantize_nf4, double_quant, quantize_nf4
 
-from support import bf16_bits, f32_bits, guarded, host, oracle_rows, oracle_weight, say, to_dev, u8
+from support import bf16_bits, f32_bits, guarded, host, oracle_weight, say, to_dev, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -154,24 +154,6 @@ def test_llama7b_shapes_full(matrix):
     assert np.array_equal(bf16_bits(out), o["w_hat"])
 
 
-def test_llama7b_last_layer_sampled_groups():
-    """Another layer's matrices at full size, checked on sampled DQ groups."""
-    for matrix in range(7):
-        W = wl.llama7b_weight(31, matrix)
-        n_out, k_in = W.shape
-        wq = q.quantize_weight(to_dev(W))
-        out = q.dequantize_nf4(wq)
-        pk, qq, cc, ww = u8(wq.packed), u8(wq.qabsmax).view(np.int8), f32_bits(wq.c2), bf16_bits(out)
-        rng = np.random.default_rng(105 + matrix)
-        for r0 in rng.integers(0, n_out - 8, 3):
-            o = oracle_rows(W, int(r0), int(r0) + 8)
-            e0 = int(r0) * k_in
-            assert np.array_equal(pk[e0 // 2:e0 // 2 + o["packed"].size], o["packed"])
-            assert np.array_equal(qq[e0 // 64:e0 // 64 + o["q"].size], o["q"])
-            assert np.array_equal(cc[o["g0"]:o["g1"]], o["c2"].view(np.uint32))
-            assert np.array_equal(ww[int(r0):int(r0) + 8], o["w_hat"])
-
-
 def test_weight_beyond_two_to_the_31_elements():
     """524,290 x 4096 float32 (2^31 + 8192 weights, 8.6 GB): 64-bit indexing in
     the quantisers and the dequantiser.  Whole DQ groups (independent of the
@@ -259,3 +241,80 @@ def test_batches_of_one_llama7b_layer_match_single_calls():
     torch.cuda.synchronize()
     for wq, o in zip(wqs, outs):
         assert torch.equal(o.view(torch.int16), q.dequantize_nf4(wq).view(torch.int16))
+
+
+def test_huge_and_tiny_block_maxima():
+    """Block maxima from subnormal up to FLT_MAX: codes, scales, DQ codes and
+    decoded bf16 (overflowing to ±Inf where RNE_bf16 does) bit-exact on every
+    route.  Above 2^126 the reciprocal of the maximum is subnormal, which the
+    bucket estimate must not meet."""
+    mids = nf4_midpoints_f64()
+    rng = np.random.default_rng(106)
+    parts = []
+    scales = [np.finfo(np.float32).max, 3e38, 1e38, 2.0 ** 127, 2.0 ** 126 * 1.5, 2.0 ** 64 * 1.5,
+              2.0 ** 64, 1e30, 1e-30, 2.0 ** -64, 3e-39, 1e-44]
+    for a in np.array(scales, dtype=np.float32):
+        vals = []
+        for m in mids:
+            t = np.float32(m * float(a))
+            for k in range(-3, 4):
+                v = t
+                for _ in range(abs(k)):
+                    v = np.nextafter(v, np.float32(np.inf) if k > 0 else np.float32(-np.inf))
+                if abs(float(v)) <= float(a):
+                    vals.append(v)
+        vals += list((rng.uniform(-1, 1, 300) * float(a)).astype(np.float32))
+        parts.append(_blocks_with_scale(a, vals))
+    # whole DQ groups of huge blocks next to ordinary ones
+    big = (rng.standard_normal(64 * 256) * 0.02).astype(np.float32)
+    big[::64] = np.float32(3.3e38)
+    parts.append(big)
+    flat = np.concatenate(parts)
+    m = -(-flat.size // 64) * 64
+    flat = np.concatenate([flat, np.zeros(m - flat.size, np.float32)])
+    packed, qa, c2, op, oq, oc2 = _compare(flat, "block maxima from 1e-44 to FLT_MAX")
+    out = q.dequantize_nf4(q.NF4Tensor(packed, qa, c2, m // 64, 64))
+    got, ref = bf16_bits(out).ravel(), dequantize_nf4(op, oq, oc2, m)
+    # Near FLT_MAX, RN32(c2·q) overflows to Inf and the zero level decodes to
+    # 0·Inf = NaN; IEEE leaves that NaN's sign and payload to the platform, so
+    # a NaN matches any NaN.  Every other value must agree bit for bit.
+    is_nan = lambda b: ((b & 0x7f80) == 0x7f80) & ((b & 0x007f) != 0)
+    assert np.array_equal(is_nan(got), is_nan(ref))
+    assert np.array_equal(got[~is_nan(got)], ref[~is_nan(ref)])
+    assert np.any(is_nan(ref)) and np.any(ref == 0x7f80)  # the overflow case is exercised
+
+
+def _flag():
+    return torch.zeros(1, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+@pytest.mark.parametrize("where", ["first", "middle", "tail"])
+def test_nonfinite_flag_is_set_on_every_route(bad, where):
+    """A NaN or ±Inf anywhere (first element, inside, in a ragged tail) sets the
+    optional flag on the first-level, the two-launch, the one-pass and the
+    batched quantiser; finite input leaves it untouched (a preset value
+    survives); no flag (NULL) is accepted."""
+    say(f"[quant] non-finite {bad} at {where}")
+    rng = np.random.default_rng(107)
+    n = 64 * 700 + 13
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    pos = {"first": 0, "middle": 64 * 333 + 17, "tail": n - 2}[where]
+    wb = w.copy()
+    wb[pos] = np.float32(bad)
+    good, poisoned = to_dev(w), to_dev(wb)
+    for src, expect in ((good, 0), (poisoned, 1)):
+        flags = [_flag() for _ in range(5)]
+        q.quantize_nf4(src, nonfinite_flag=flags[0])
+        q.quantize_nf4_dq(src, nonfinite_flag=flags[1])
+        q.quantize_nf4_dq(src, one_pass=True, nonfinite_flag=flags[2])
+        q.quantize_nf4_dq_batch([good, src], nonfinite_flags=[None, flags[3]])
+        flags[4].fill_(7)
+        q.quantize_nf4_dq_batch([src], nonfinite_flags=[flags[4]])
+        got = [int(host(f)[0]) for f in flags]
+        assert got[:4] == [expect] * 4, got
+        assert got[4] == (7 if expect == 0 else 1), got
+    # without a flag the call still runs (codes of non-finite input are unspecified)
+    q.quantize_nf4(poisoned)
+    q.quantize_nf4_dq(poisoned, one_pass=True)
+    torch.cuda.synchronize()

@@ -86,6 +86,42 @@ def test_indices_near_every_midpoint_with_random_scales():
     assert checked > 15 * 7 * 40 - 1
 
 
+@pytest.mark.parametrize("a", [np.finfo(np.float32).max, np.float32(1e38), np.float32(2.0 ** 64 * 1.5),
+                               np.float32(2.0 ** 126 * 1.25), np.float32(3e-39), np.float32(1e-44)])
+def test_indices_near_every_midpoint_at_extreme_scales(a):
+    """Block maxima at both ends of the float32 range (up to FLT_MAX, down to a
+    subnormal): the decision still follows the exact quotient (the float64
+    products m_i·a neither overflow nor lose bits)."""
+    a = np.float32(a)
+    mids = nf4_midpoints_f64()
+    vals = []
+    for m in mids:
+        vals += [v for v in _f32_neighbors(np.float32(m * float(a)), 3) if abs(float(v)) <= float(a)]
+    rng = np.random.default_rng(int(a.view(np.uint32)))
+    vals += list((rng.uniform(-1, 1, 40) * float(a)).astype(np.float32))
+    vals = np.array(vals, dtype=np.float32)
+    for s in range(0, vals.size, 63):
+        chunk = vals[s:s + 63]
+        block = np.concatenate([[a], chunk, np.zeros(63 - chunk.size, np.float32)]).astype(np.float32)
+        assert block_absmax(block)[0] == a
+        got = nf4_indices(block, block_absmax(block))
+        for j in range(1, 1 + chunk.size):
+            assert got[j] == _argmin_exact(block[j], a), (float(a), float(block[j]))
+
+
+def test_indices_invariant_under_power_of_two_scaling():
+    """w/a does not change when both are multiplied by 2^e (exactly, inside the
+    float32 range), so neither may the codes: unit-scale blocks scaled to
+    2^100 and 2^-100."""
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal(64 * 40) * 0.02).astype(np.float32)
+    ref = nf4_indices(w, block_absmax(w))
+    for e in (100, -100, 127 - 4):
+        ws = (w.astype(np.float64) * 2.0 ** e).astype(np.float32)
+        assert np.array_equal(ws.astype(np.float64) * 2.0 ** -e, w.astype(np.float64))
+        assert np.array_equal(nf4_indices(ws, block_absmax(ws)), ref), e
+
+
 def test_exact_ties_go_to_lower_index():
     mids = nf4_midpoints_f64()
     for i in [1, 3, 4, 7, 8, 11, 13, 14]:
@@ -353,3 +389,17 @@ def test_quantize_weight_shapes():
     assert r["absmax"].size == 96 * 2 and r["q"].size == 96 * 2 and r["c2"].size == 1
     assert r["w_hat"].shape == (96, 128)
     assert np.all(np.abs(bf16_to_f64(r["w_hat"]) - w) <= np.repeat(r["absmax"], 64).reshape(96, 128) * 0.13)
+
+
+def test_group_chunked_oracle_equals_whole_weight():
+    """The parity harness runs the oracle on ranges of whole DQ groups in
+    threads (DQ groups are independent); joined, that must be exactly the
+    whole-weight result, with a ragged last chunk and a short last group."""
+    from support import oracle_weight, oracle_weight_parallel
+    rng = np.random.default_rng(11)
+    W = (rng.standard_normal((37, 11008)) * 0.02).astype(np.float32)
+    W[rng.random(W.shape) < 1e-3] = np.float32(0.16)
+    a = oracle_weight(W)
+    b = oracle_weight_parallel(W, threads=3, chunk_groups=4)
+    for k in ("packed", "absmax", "q", "c2", "w_hat"):
+        assert a[k].dtype == b[k].dtype and np.array_equal(a[k], b[k]), k

@@ -75,16 +75,17 @@ class LinearWorkload:
     layer: int = 0
     matrix: int = 0
 
-    def inputs(self, M=None, with_dy=True):
+    def inputs(self, M=None, with_dy=True, with_w=True):
         """Seeded inputs: dict(W fp32 numpy, A, B, X, dY bf16 torch CPU)."""
         M = self.M if M is None else M
         key = dict(layer=self.layer, matrix=self.matrix)
         out = dict(
-            W=weight_f32(self.workload, self.n_out, self.k_in, **key),
             A=bf16_normal(self.workload, (self.r, self.k_in), 0.01, tensor=T_A, **key),
             B=bf16_normal(self.workload, (self.n_out, self.r), 0.01, tensor=T_B, **key),
             X=bf16_normal(self.workload, (M, self.k_in), 1.0, tensor=T_X, **key),
         )
+        if with_w:
+            out["W"] = weight_f32(self.workload, self.n_out, self.k_in, **key)
         if with_dy and not self.fwd_only:
             out["dY"] = bf16_normal(self.workload, (M, self.n_out), 1.0, tensor=T_DY, **key)
         return out
