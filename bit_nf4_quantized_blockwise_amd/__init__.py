@@ -86,6 +86,7 @@ _SIGNATURES = {
     "qlora_quantize_nf4_dq_batch": ([_P, _I32, _P], _I32),
     "qlora_dequantize_nf4_batch": ([_P, _P, _I32, _P], _I32),
     "qlora_linear_fwd": ([_W, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P], _I32),
+    "qlora_linear_fwd_noalloc": ([_W, _P, _I64, _P, _P, _I32, _F, _P, _P, _P], _I32),
     "qlora_linear_bwd": ([_W, _P, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "qlora_lora_down": ([_P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P], _I32),
     "qlora_nf4_matmul_fwd": ([_W, _P, _I64, _P, _P, _I32, _F, _P, _P, _SZ, _P], _I32),

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "qlora_kernels.h"
@@ -1070,6 +1071,67 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const qlora_bf16* X, in
   if (s != QLORA_OK) return s;
   return linear_fwd_impl(w, X, X, M, A, B, r, scale_of(alpha, r), Y, U,
                          static_cast<char*>(workspace), L, as_stream(stream));
+}
+
+}  // extern "C"
+
+// ---- the forward without a caller workspace -----------------------------------
+// Its scratch (split-K partial sums of U and of the 17..127-token product,
+// the zero-padded copies of U and B for ranks that are not a multiple of 8)
+// lives in this file-scope array, one copy per GPU, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address is looked up once per device (with that device
+// current) and only that address reaches kernels.
+namespace {
+
+static __device__ __attribute__((aligned(256))) char scratch[QLORA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<char*> g_scratch_dev[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`.
+qlora_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLORA_ERR_DEVICE;
+  char* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+        return QLORA_ERR_DEVICE;
+      p = static_cast<char*>(addr);
+      g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const qlora_bf16* X, int64_t M,
+                                      const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                      float alpha, qlora_bf16* Y, qlora_bf16* U, void* stream) {
+  qlora_status s = validate_linear(w, M, r);
+  if (s != QLORA_OK) return s;
+  if (M == 0) return QLORA_OK;
+  ALIGNED_OR_NULL(X);
+  ALIGNED_OR_NULL(A);
+  ALIGNED_OR_NULL(B);
+  ALIGNED_OR_NULL(Y);
+  ALIGNED_OR_NULL(U);
+  const FwdWs L = fwd_ws(M, w->n_out, w->k_in, r);
+  QCHECK(L.total <= QLORA_NOALLOC_SCRATCH_BYTES, QLORA_ERR_WORKSPACE);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  char* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != QLORA_OK) return s;
+  return linear_fwd_impl(w, X, X, M, A, B, r, scale_of(alpha, r), Y, U, ws, L, as_stream(stream));
 }
 
 qlora_status qlora_lora_dropout(const qlora_bf16* X, int64_t M, int64_t k_in, float p,

@@ -271,6 +271,26 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w /* host struct */, const
                               qlora_bf16 *dX, float *dA, float *dB, void *workspace,
                               size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory or hand over a workspace:
+ * code under HIP graph capture that must not allocate, tight serving loops,
+ * harnesses that forbid hipMalloc.  Exactly qlora_linear_fwd (same kernels,
+ * same results bit for bit), its workspace taken from a buffer of
+ * QLORA_NOALLOC_SCRATCH_BYTES that the library keeps in each GPU's memory
+ * until the process ends; nothing is allocated or freed by the call.  Returns
+ * QLORA_ERR_WORKSPACE, with nothing launched, when
+ * qlora_workspace_size(0, M, n_out, k_in, r) exceeds that size (4096 tokens
+ * of a LLaMA-7B MLP or 2048 of a LLaMA-65B projection need 8.4 MB, 16 tokens
+ * or fewer at most a few MB; 17..127 tokens with n_out above ~130,000 do not
+ * fit).  Every call on one GPU shares that GPU's buffer:
+ * calls that can overlap on one GPU (several streams, or threads without an
+ * order between them) race and must be serialised by the caller.  Nothing in
+ * the buffer has to start at zero; it keeps the last call's contents. */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight *w /* host struct */,
+                                      const qlora_bf16 *X, int64_t M, const qlora_bf16 *A,
+                                      const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *Y,
+                                      qlora_bf16 *U, void *stream);
+
 /* The forward's two launches, callable on their own (the forward is exactly
  * qlora_lora_down then qlora_nf4_matmul_fwd):
  *   qlora_lora_down:      U = X·Aᵀ, bf16 [M][r]

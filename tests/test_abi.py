@@ -1,5 +1,9 @@
 """C-ABI checks that need no GPU: the library loads, exports every function the
-header declares, and rejects bad arguments before touching a device."""
+header declares, and rejects bad arguments before touching a device.
+
+The device pointers here are fake: every call must fail validation, or be
+one that expects QLORA_ERR_DEVICE and is skipped where a GPU is present
+(with a GPU such a call would launch on the fake pointers)."""
 
 import ctypes
 import re
@@ -102,6 +106,15 @@ def test_linear_argument_errors(L):
              1 << 30, None) == NULL
     assert b(_weight(), FAKE, FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
              None) == WS
+    n = L.qlora_linear_fwd_noalloc
+    assert n(_weight(), FAKE, 16, FAKE, FAKE, 0, 16.0, FAKE, FAKE, None) == UNSUP
+    assert n(_weight(), None, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, None) == NULL
+    assert n(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, MIS, FAKE, None) == ALIGN
+    assert n(_weight(), FAKE, 0, None, None, 8, 16.0, None, None, None) == OK  # no tokens
+    # 127 tokens into 262144 outputs: the split-K partial sums exceed the buffer
+    assert q.workspace_size(0, 127, 262144, 64, 8) > (64 << 20)
+    assert n(_weight(n_out=262144, k_in=64), FAKE, 127, FAKE, FAKE, 8, 16.0, FAKE, FAKE,
+             None) == WS
     d = L.qlora_dequantize_nf4
     assert d(ctypes.byref(q.NF4Weight(FAKE, FAKE, FAKE, 3, 5)), FAKE, None) == SHAPE
     assert d(ctypes.byref(q.NF4Weight(FAKE, FAKE, FAKE, 4, 16)), MIS, None) == ALIGN
@@ -148,6 +161,10 @@ def test_valid_arguments_without_gpu_report_device(L):
     assert L.qlora_dequantize_nf4_batch(ws, (ctypes.c_void_p * 1)(FAKE), 1, None) == DEV
     assert L.qlora_linear_fwd(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE, FAKE, 1 << 30,
                               None) == DEV
+    assert L.qlora_linear_fwd_noalloc(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE,
+                                      None) == DEV
+    # an 8-byte aligned sum is accepted (it is one double)
+    assert L.qlora_quant_sq_error(FAKE, 100, 0, FAKE, FAKE, FAKE + 8, FAKE, 4096, None) == DEV
 
 
 def test_adamw_argument_errors(L):
@@ -202,7 +219,6 @@ def test_quantizer_variant_argument_errors(L):
     assert e(FAKE, 100, 3, FAKE, FAKE, FAKE, FAKE, 4096, None) == UNSUP
     assert e(FAKE, 100, 0, FAKE, FAKE, None, FAKE, 4096, None) == NULL
     assert e(FAKE, 100, 0, FAKE, FAKE, FAKE + 4, FAKE, 4096, None) == ALIGN
-    assert e(FAKE, 100, 0, FAKE, FAKE, FAKE + 8, FAKE, 4096, None) != ALIGN  # 8 bytes suffice
     assert e(FAKE, 100, 0, FAKE, FAKE, FAKE, None, 4096, None) == WS
     assert e(FAKE, 100, 0, FAKE, FAKE, FAKE, FAKE, 8, None) == WS
     assert e(MIS, 100, 0, FAKE, FAKE, FAKE, FAKE, 4096, None) == ALIGN
