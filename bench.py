@@ -1,19 +1,23 @@
 """Benchmark of the QLoRA NF4 linear hot path on one MI355X.
 
-Step = one training step of the frozen-NF4 QLoRA linear at the LLaMA-7B MLP
-shape (4096 tokens, 4096 -> 11008, r = 64, alpha = 16): forward (U = X·Aᵀ, then
-the dequant-GEMM with the LoRA prologue) and backward (V = dY·B, the
-transposed dequant-GEMM for dX, dA and dB), on resident synthetic inputs.
-`value` = algorithmic TFLOP/s of that step.  The same run also measures the
-other rows of the hot path: the fused NF4 + double-quant quantiser and the
-dequantiser (GB/s over the weight), and the few-token forward at 8192 -> 28672
-(GB/s over the weight it streams, M = 1..8, weight copies rotated past the
-256 MB Infinity Cache), the 32-bit AdamW step with gradient clipping over
-the 67M LoRA parameters of LLaMA-7B's attention projections (GB/s), and the
-single-quantisation INT4 quantiser, decoder and error pass with the
-NF4-vs-INT4 error on the 11008 x 4096 weight, the training step with LoRA
-dropout (p = 0.05) on the adapter input, and the adapter merge with
-re-quantisation at that shape.
+Step = one training step (forward + backward) of every projection of one
+LLaMA-65B-shaped decoder layer (q, k, v, o 8192 -> 8192; gate, up 8192 ->
+22016; down 22016 -> 8192), NF4 + double-quantised weights with a LoRA
+adapter r = 64, alpha = 16 on each, 2048 tokens: per projection U = X·Aᵀ
+and the dequant-GEMM with the rank-r prologue, then V = dY·B, the
+transposed dequant-GEMM for dX, dA and dB.  6,754.24 GFLOP per step on
+resident seeded synthetic inputs; `value` = algorithmic TFLOP/s of the step.
+The roofline object is the forward dequant-GEMM over the layer's seven
+launches, timed on the stream it runs on; `roofline_gemv` is the few-token
+dequant-GEMV kernel (8192 -> 28672, 1 token) against HBM.  The same run also
+measures, in `rows`, the LLaMA-7B MLP training step (4096 tokens, 4096 ->
+11008, r = 64), the fused NF4 + double-quant quantiser and the dequantiser
+(one matrix and the whole 224-matrix LLaMA-7B weight set), the few-token
+forward at 1..8 tokens, the single 16-token 4096 x 4096 linear, the 32-bit
+AdamW step over the 67M LoRA parameters of LLaMA-7B's attention projections,
+the single-quantisation INT4 quantiser, decoder and error pass, the training
+step with LoRA dropout (p = 0.05), and the adapter merge with
+re-quantisation.
 
 Prints ONE JSON line.  --gpus N > 1 is not supported (single-GPU build).
 """
@@ -35,7 +39,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # library is built without them): 256 CUs x 64 lanes x 2 flop x 2.4 GHz
 FP32_FMA_PEAK_TFLOPS = 78.6
 GEMM_SOURCES = ["qlora_gemm.hip", "qlora_common.h", "qlora_kernels.h", "qlora_philox.h"]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_gemm_fwd_llama7b_mlp.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_gemm_fwd_llama65b_layer.txt")
 CALIB_BYTES = 512 << 20  # plain device copy used to scale the byte counters
 
 
@@ -66,10 +70,22 @@ def read_traffic():
         return None
 
 
+def _layer_fwd_algo_bytes():
+    """Algorithmic bytes of the layer's seven forward dequant-GEMM launches
+    (weight storage, X, U, B and Y once each), summed."""
+    tot = 0
+    for K, N in LAYER65B_SHAPES:
+        n = N * K
+        tot += n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4 + 2 * 2048 * K + 2 * 2048 * 64 \
+            + 2 * N * 64 + 2 * 2048 * N
+    return tot
+
+
 def summarize_pmc(fetch_csv, write_csv, out_path):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the forward dequant-GEMM,
-    each scaled by what the same counter reads for a device copy of
-    CALIB_BYTES, written as a short text summary."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the forward dequant-GEMM
+    (the layer's seven launches of --pmc-pass, averaged per launch), each
+    scaled by what the same counter reads for a device copy of CALIB_BYTES,
+    written as a short text summary."""
     import csv
 
     def per_kernel(path, counter):
@@ -78,42 +94,41 @@ def summarize_pmc(fetch_csv, write_csv, out_path):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = ("gemm" if "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0>" in name else
-                   "copy" if "copyBuffer" in name else None)
+            key = ("gemm" if FWD_GEMM in name else "copy" if "copyBuffer" in name else None)
             if key:
                 vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
                 vals[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return {k: sum(v.values()) / len(v) for k, v in vals.items()}
+        return {k: (sum(v.values()) / len(v), len(v)) for k, v in vals.items()}
 
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
     kib = CALIB_BYTES / 1024.0
-    f_scale = kib / f["copy"]
-    w_scale = kib / w["copy"]
-    fetch_b = f["gemm"] * f_scale * 1024.0
-    write_b = w["gemm"] * w_scale * 1024.0
-    M, K, N, r = 4096, 4096, 11008, 64
-    algo = N * K // 2 + N * K // 64 + ((N * K // 64 + 255) // 256) * 4 + 2 * M * K \
-        + 2 * M * r + 2 * N * r + 2 * M * N
+    f_scale = kib / f["copy"][0]
+    w_scale = kib / w["copy"][0]
+    fetch_b = f["gemm"][0] * f_scale * 1024.0
+    write_b = w["gemm"][0] * w_scale * 1024.0
+    algo = _layer_fwd_algo_bytes() / 7
     with open(out_path, "w") as fh:
-        fh.write("# HBM traffic of the forward dequant-GEMM (LLaMA-7B MLP: 4096 tokens, 4096 -> 11008,\n")
-        fh.write("# r = 64), from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by the same counter\n")
-        fh.write(f"# on a device copy of {CALIB_BYTES} bytes.  Commands (from /tmp, TMPDIR=/tmp):\n")
+        fh.write("# HBM traffic of the forward dequant-GEMM over the seven projections of one\n")
+        fh.write("# LLaMA-65B layer (2048 tokens, r = 64), per launch (average of the seven shapes),\n")
+        fh.write("# from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a\n")
+        fh.write(f"# device copy of {CALIB_BYTES} bytes.  Commands (from /tmp, TMPDIR=/tmp):\n")
         fh.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_f> -o f -- python3 <repo>/bench.py --pmc-pass\n")
         fh.write("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_w> -o w -- python3 <repo>/bench.py --pmc-pass\n")
         fh.write("#   python3 <repo>/bench.py --summarize-pmc <dir_f>/f_counter_collection.csv "
                  "<dir_w>/w_counter_collection.csv <this file>\n")
         fh.write(f"kernel_source_sha256_16 = {gemm_source_hash()}\n")
-        fh.write(f"fetch_kib_per_launch_raw = {f['gemm']:.1f}\n")
-        fh.write(f"write_kib_per_launch_raw = {w['gemm']:.1f}\n")
-        fh.write(f"copy_fetch_kib_raw = {f['copy']:.1f}\n")
-        fh.write(f"copy_write_kib_raw = {w['copy']:.1f}\n")
+        fh.write(f"gemm_dispatches = {f['gemm'][1]}\n")
+        fh.write(f"fetch_kib_per_launch_raw = {f['gemm'][0]:.1f}\n")
+        fh.write(f"write_kib_per_launch_raw = {w['gemm'][0]:.1f}\n")
+        fh.write(f"copy_fetch_kib_raw = {f['copy'][0]:.1f}\n")
+        fh.write(f"copy_write_kib_raw = {w['copy'][0]:.1f}\n")
         fh.write(f"fetch_scale = {f_scale:.4f}\n")
         fh.write(f"write_scale = {w_scale:.4f}\n")
         fh.write(f"fetch_bytes_per_launch = {fetch_b:.0f}\n")
         fh.write(f"write_bytes_per_launch = {write_b:.0f}\n")
         fh.write(f"traffic_bytes_per_launch = {fetch_b + write_b:.0f}\n")
-        fh.write(f"algorithmic_bytes_per_launch = {algo}\n")
+        fh.write(f"algorithmic_bytes_per_launch = {algo:.0f}\n")
         fh.write(f"traffic_over_algorithmic = {(fetch_b + write_b) / algo:.3f}\n")
     print(open(out_path).read())
 
@@ -121,9 +136,10 @@ def summarize_pmc(fetch_csv, write_csv, out_path):
 def summarize_stats(stats_csv, bench_log, out_path):
     """Short text summary of a rocprofv3 --kernel-trace --stats run of this
     script: calls and durations per kernel and launch grid (from the per-
-    dispatch trace beside the stats file: one kernel runs at several shapes,
-    and the forward dequant-GEMM's line at the bench shape is the one the
-    roofline's event timing is compared with), with the bench line it printed."""
+    dispatch trace beside the stats file), with the bench line it printed.
+    With --no-rows every forward dequant-GEMM launch is one of the layer's
+    seven projections, each equally often, so their mean duration is the
+    per-launch figure the roofline's event timing is compared with."""
     import csv
     import statistics
 
@@ -136,30 +152,24 @@ def summarize_stats(stats_csv, bench_log, out_path):
     rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
     line = [ln for ln in open(bench_log) if ln.startswith('{"metric"')][-1]
     d = json.loads(line)
-    n_tiles = ((d["config"]["tokens"] + 255) // 256) * ((d["config"]["n_out"] + 255) // 256)
-    fwd_key = next((k for k in groups if FWD_GEMM in k[0] and k[1] == f"{n_tiles * 256}x1"), None)
+    fwd = [x for k, v in groups.items() if FWD_GEMM in k[0] for x in v]
     with open(out_path, "w") as fh:
-        fh.write("# rocprofv3 kernel statistics of bench.py (LLaMA-7B MLP QLoRA linear: 4096 "
-                 "tokens,\n# 4096 -> 11008, r = 64, alpha = 16, and the other rows of the "
-                 "bench line), one MI355X, per kernel and launch grid.\n")
+        fh.write("# rocprofv3 kernel statistics of bench.py (QLoRA linear fwd + bwd over the seven\n"
+                 "# projections of one LLaMA-65B layer, 2048 tokens, r = 64, and the other rows of\n"
+                 "# the bench line), one MI355X, per kernel and launch grid.\n")
         fh.write("# commands (from /tmp, TMPDIR=/tmp):\n")
-        rows_flag = "" if d["rows"] else " --no-rows"
+        rows_flag = "" if d["rows"] and len(d["rows"]) > 1 else " --no-rows"
         fh.write("#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
                  f"python3 <repo>/bench.py --no-cpu-baseline{rows_flag} --steps 10 --warmup 2 > <log>\n")
         fh.write("#   python3 <repo>/bench.py --summarize-stats <dir>/bench_kernel_stats.csv "
                  "<log> <this file>\n")
-        if d["rows"]:
-            fh.write("# (with all rows: one kernel and grid can cover several shapes, e.g. the\n"
-                     "#  LLaMA-65B gate and up projections tile into the same 688 workgroups as\n"
-                     "#  the forward GEMM of the bench shape; --no-rows isolates the latter)\n")
         fh.write(f"# bench line under the profiler: value = {d['value']:.1f} TFLOP/s, "
                  f"ms_per_step = {d['ms_per_step']:.3f},\n")
-        fh.write(f"#   forward dequant-GEMM (events) = {d['roofline']['ms'] * 1e3:.1f} us\n")
-        if fwd_key and not d["rows"]:
-            v = groups[fwd_key]
-            fh.write(f"#   forward dequant-GEMM at the bench shape (trace, grid {fwd_key[1]}): "
-                     f"{len(v)} calls, mean {statistics.mean(v):.1f} us, median "
-                     f"{statistics.median(v):.1f} us\n")
+        fh.write(f"#   forward dequant-GEMM per launch (events) = "
+                 f"{d['roofline']['us_per_launch']:.1f} us\n")
+        if fwd and rows_flag:
+            fh.write(f"#   forward dequant-GEMM per launch (trace, all grids): {len(fwd)} calls, "
+                     f"mean {statistics.mean(fwd):.1f} us\n")
         fh.write("\n")
         fh.write(f"{'kernel':<72} {'grid':>14} {'calls':>6} {'avg_us':>10} {'min_us':>10} "
                  f"{'max_us':>10} {'total_ms':>10}\n")
@@ -236,24 +246,25 @@ def pmc_pass_bwd():
 
 
 def pmc_pass():
-    """Short run for counter collection: the forward dequant-GEMM a few times
-    and a device copy of CALIB_BYTES (the byte counters' calibration)."""
+    """Short run for counter collection: the forward dequant-GEMM of each of
+    the LLaMA-65B layer's seven projections once (inputs drawn on the GPU:
+    the counters do not depend on the values) and a device copy of
+    CALIB_BYTES (the byte counters' calibration)."""
     import torch
 
     import bit_nf4_quantized_blockwise_amd as q
-    import workloads as wl
 
     dev = torch.device("cuda:0")
-    wlc = wl.LLAMA7B_MLP
-    inp = wlc.inputs(with_dy=False)
-    wq = q.quantize_weight(torch.from_numpy(inp["W"]).to(dev))
-    X, A, B = (inp[k].to(dev) for k in ("X", "A", "B"))
-    ws = torch.empty(q.workspace_size(0, wlc.M, wlc.n_out, wlc.k_in, wlc.r), dtype=torch.uint8,
-                     device=dev)
-    U = q.lora_down(X, A)
-    Y = torch.empty(wlc.M, wlc.n_out, dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        q.nf4_matmul_fwd(wq, X, U, B, wlc.alpha, workspace=ws, Y=Y)
+    gen = torch.Generator(device=dev).manual_seed(5)
+    M, r = 2048, 64
+    for K, N in LAYER65B_SHAPES:
+        wq = q.quantize_weight(torch.randn(N, K, generator=gen, device=dev) * 0.02)
+        bf = lambda *shape, s: (torch.randn(*shape, generator=gen, device=dev) * s).to(torch.bfloat16)
+        X, A, B = bf(M, K, s=1.0), bf(r, K, s=0.01), bf(N, r, s=0.01)
+        U = q.lora_down(X, A)
+        q.nf4_matmul_fwd(wq, X, U, B, 16.0)
+        torch.cuda.synchronize()
+        del wq, X, A, B, U
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -488,14 +499,193 @@ def main():
         summarize_hbm(*args.summarize_hbm)
         return
 
-    import numpy as np
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] LLaMA-65B layer inputs (seeded, host)", file=sys.stderr, flush=True)
+    layer = layer65b_setup(dev)
+
+    def step():
+        for P in layer:
+            P["fwd"]()
+            P["bwd"]()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s, e = _events()
+    s.record()
+    for _ in range(args.steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = s.elapsed_time(e) / args.steps
+    flops = sum(P["flops"] for P in layer)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    print(f"[bench] layer step {ms_step:.3f} ms, {tflops:.1f} TFLOP/s", file=sys.stderr,
+          flush=True)
+
+    # dominant kernel: the forward dequant-GEMM (Y = X·Ŵᵀ + s·U·Bᵀ), one launch
+    # per projection through its own entry point, timed with events on the
+    # stream it is launched on
+    per, g_ms, g_flops = {}, 0.0, 0
+    for P in layer:
+        ms_p = _time_ms(P["gemm"], args.steps, warmup=3)
+        per[P["name"]] = dict(step_ms=_time_ms(lambda: (P["fwd"](), P["bwd"]()), args.steps,
+                                               warmup=2),
+                              fwd_gemm_us=ms_p * 1e3,
+                              fwd_gemm_TFLOPs=P["gemm_flops"] / (ms_p * 1e-3) / 1e12)
+        per[P["name"]]["step_TFLOPs"] = P["flops"] / (per[P["name"]]["step_ms"] * 1e-3) / 1e12
+        g_ms += ms_p
+        g_flops += P["gemm_flops"]
+    gemm_tflops = g_flops / (g_ms * 1e-3) / 1e12
+    del layer
+    torch.cuda.empty_cache()
+
+    gemv = gemv_roofline(dev, args.steps)
+    rows = {"llama65b_layer_projections": per}
+    if not args.no_rows:
+        rows["llama7b_mlp_4096x11008_r64_m4096"] = llama7b_mlp_rows(dev, args.steps, args.warmup)
+        rows.update(other_rows(dev, args.steps))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+
+    out = {
+        "metric": "QLoRA linear fwd+bwd TFLOP/s (one LLaMA-65B decoder layer, 7 projections, "
+                  "2048 tokens, r=64)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) fp32 weights -> NF4+DQ; bf16 N(0,1) X, dY; "
+                "bf16 N(0,0.01) A, B; the parity tests' host recipe)",
+        "config": {"workload": "llama65b_layer_7proj_r64_m2048", "tokens": 2048,
+                   "projections": [[P_k, P_n] for P_k, P_n in LAYER65B_SHAPES], "r": 64,
+                   "alpha": 16.0, "flops_per_step": flops},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": FWD_GEMM + " (forward dequant-GEMM, the layer's 7 launches)",
+            "achieved": gemm_tflops,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / BF16_PEAK_TFLOPS,
+            "us_per_launch": g_ms * 1e3 / 7,
+            "flops_per_launch": g_flops / 7,
+            "traffic": read_traffic(),
+        },
+        "roofline_gemv": gemv,
+        "rows": rows,
+        "cpu_baseline": cpu,
+        "wall_s": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+LAYER65B_SHAPES = [(8192, 8192)] * 4 + [(8192, 22016)] * 2 + [(22016, 8192)]
+
+
+def layer65b_setup(dev):
+    """The seven projections of one LLaMA-65B-shaped decoder layer with the
+    parity tests' seeded host inputs (weights drawn in threads), quantised on
+    the GPU, with resident outputs and workspaces: a list of dicts holding
+    fwd(), bwd() and gemm() (the forward dequant-GEMM alone) closures."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import torch
 
     import bit_nf4_quantized_blockwise_amd as q
     import workloads as wl
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    with ThreadPoolExecutor(7) as ex:
+        inps = list(ex.map(lambda w: w.inputs(), wl.LLAMA65B_LAYER))
+    out = []
+    for wlc, inp in zip(wl.LLAMA65B_LAYER, inps):
+        M, K, N, r, alpha = wlc.M, wlc.k_in, wlc.n_out, wlc.r, wlc.alpha
+        W = torch.from_numpy(inp["W"]).to(dev)
+        wq = q.quantize_weight(W)
+        del W
+        X, A, B, dY = (inp[k].to(dev) for k in ("X", "A", "B", "dY"))
+        ws_f = torch.empty(q.workspace_size(0, M, N, K, r), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(q.workspace_size(1, M, N, K, r), dtype=torch.uint8, device=dev)
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        U = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+        dA = torch.empty(r, K, dtype=torch.float32, device=dev)
+        dB = torch.empty(N, r, dtype=torch.float32, device=dev)
+        P = dict(name=wlc.name, wq=wq, X=X, A=A, B=B, dY=dY, Y=Y, U=U, dX=dX, dA=dA, dB=dB,
+                 flops=wlc.flops_fwd + wlc.flops_bwd, gemm_flops=2 * M * K * N + 2 * M * r * N)
+        P["fwd"] = (lambda P=P, wlc=wlc, ws_f=ws_f: q.linear_fwd(
+            P["wq"], P["X"], P["A"], P["B"], wlc.alpha, workspace=ws_f, Y=P["Y"], U=P["U"]))
+        P["bwd"] = (lambda P=P, wlc=wlc, ws_b=ws_b: q.linear_bwd(
+            P["wq"], P["X"], P["dY"], P["A"], P["B"], P["U"], wlc.alpha, workspace=ws_b,
+            dX=P["dX"], dA=P["dA"], dB=P["dB"]))
+        P["gemm"] = (lambda P=P, wlc=wlc, ws_f=ws_f: q.nf4_matmul_fwd(
+            P["wq"], P["X"], P["U"], P["B"], wlc.alpha, workspace=ws_f, Y=P["Y"]))
+        out.append(P)
+    del inps
+    return out
+
+
+def gemv_roofline(dev, steps):
+    """The few-token dequant-GEMV kernel alone (8192 -> 28672, r = 16, the
+    adapter term fused; U given), one launch per call, five weight copies
+    rotating past the 256 MB last-level cache.  Algorithmic bytes per launch:
+    the NF4 + DQ weight, X, B, U and Y once each."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
+    g = wl.GEMV_70B
+    gin = g.inputs(M=1, with_w=True)
+    Wg = torch.from_numpy(gin["W"]).to(dev)
+    copies = [q.quantize_weight(Wg if c == 0 else Wg * (1.0 + c * 1e-3)) for c in range(5)]
+    del Wg
+    Ag, Bg = gin["A"].to(dev), gin["B"].to(dev)
+    res = {}
+    for m in (1, 8):
+        Xg = wl.bf16_normal(4, (m, g.k_in), 1.0, tensor=wl.T_X).to(dev)
+        Ug = q.lora_down(Xg, Ag)
+        ws = torch.empty(q.workspace_size(0, m, g.n_out, g.k_in, g.r), dtype=torch.uint8,
+                         device=dev)
+        Yg = torch.empty(m, g.n_out, dtype=torch.bfloat16, device=dev)
+        calls = [(lambda w_=w_: q.nf4_matmul_fwd(w_, Xg, Ug, Bg, g.alpha, workspace=ws, Y=Yg))
+                 for w_ in copies]
+        ms = _time_ms(_rotate(calls), 50, warmup=5)
+        nbytes = copies[0].nbytes + 2 * m * g.k_in + 2 * g.r * g.n_out + 2 * m * g.r \
+            + 2 * m * g.n_out
+        res[m] = dict(us=ms * 1e3, GBps=nbytes / ms / 1e6, bytes=nbytes)
+    del copies
+    torch.cuda.empty_cache()
+    a = res[1]
+    return {"bound": "hbm", "kernel": "nf4_gemv_kernel (8192 -> 28672, r = 16, 1 token)",
+            "achieved": a["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": a["GBps"] / HBM_PEAK_GBS, "us_per_launch": a["us"],
+            "bytes_per_launch": a["bytes"], "traffic": None,
+            "tokens_8": dict(GBps=res[8]["GBps"], frac=res[8]["GBps"] / HBM_PEAK_GBS,
+                             us_per_launch=res[8]["us"])}
+
+
+def llama7b_mlp_rows(dev, steps, warmup):
+    """The LLaMA-7B MLP linear (4096 tokens, 4096 -> 11008, r = 64): the
+    training step, its forward dequant-GEMM alone, and the forward and the
+    backward on their own."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
+
     wlc = wl.LLAMA7B_MLP
     M, K, N, r, alpha = wlc.M, wlc.k_in, wlc.n_out, wlc.r, wlc.alpha
     inp = wlc.inputs()
@@ -513,161 +703,110 @@ def main():
     def step():
         q.linear_fwd(wq, X, A, B, alpha, workspace=ws_f, Y=Y, U=U)
         q.linear_bwd(wq, X, dY, A, B, U, alpha, workspace=ws_b, dX=dX, dA=dA, dB=dB)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    s, e = _events()
-    s.record()
-    for _ in range(args.steps):
-        step()
-    e.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = s.elapsed_time(e) / args.steps
+    ms_step = _time_ms(step, steps, warmup=warmup)
     flops = wlc.flops_fwd + wlc.flops_bwd
-    tflops = flops / (ms_step * 1e-3) / 1e12
-
-    # dominant kernel: the forward dequant-GEMM (one launch: Y = X·Ŵᵀ + s·U·Bᵀ)
     gemm_flops = 2 * M * K * N + 2 * M * r * N
-    ms_gemm = _time_ms(lambda: q.nf4_matmul_fwd(wq, X, U, B, alpha, workspace=ws_f, Y=Y),
-                       args.steps, warmup=args.warmup)
-    gemm_tflops = gemm_flops / (ms_gemm * 1e-3) / 1e12
-    # the input-gradient GEMM, timed through the backward (reported for context)
+    ms_gemm = _time_ms(lambda: q.nf4_matmul_fwd(wq, X, U, B, alpha, workspace=ws_f, Y=Y), steps,
+                       warmup=3)
+    ms_fwd = _time_ms(lambda: q.linear_fwd(wq, X, A, B, alpha, workspace=ws_f, Y=Y, U=U), steps)
     ms_bwd = _time_ms(lambda: q.linear_bwd(wq, X, dY, A, B, U, alpha, workspace=ws_b, dX=dX,
-                                           dA=dA, dB=dB), args.steps)
-    ms_fwd = _time_ms(lambda: q.linear_fwd(wq, X, A, B, alpha, workspace=ws_f, Y=Y, U=U),
-                      args.steps)
+                                           dA=dA, dB=dB), steps)
+    # the same step with LoRA dropout p = 0.05 on the adapter input
+    Xdr = torch.empty_like(X)
+    ws_d = torch.empty(q.workspace_size(2, M, N, K, r), dtype=torch.uint8, device=dev)
+    it = [0]
+
+    def step_dropout():
+        it[0] += 1
+        q.linear_fwd_dropout(wq, X, A, B, alpha, 0.05, 1234, it[0], workspace=ws_f, Y=Y, U=U,
+                             Xd=Xdr)
+        q.linear_bwd_dropout(wq, Xdr, dY, A, B, U, alpha, 0.05, 1234, it[0], workspace=ws_d,
+                             dX=dX, dA=dA, dB=dB)
+    ms_dr = _time_ms(step_dropout, steps)
+    out = dict(ms=ms_step, TFLOPs=flops / (ms_step * 1e-3) / 1e12, flops_per_step=flops,
+               fwd_ms=ms_fwd, bwd_ms=ms_bwd, fwd_gemm_us=ms_gemm * 1e3,
+               fwd_gemm_TFLOPs=gemm_flops / (ms_gemm * 1e-3) / 1e12,
+               fwd_gemm_frac=gemm_flops / (ms_gemm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+               lora_dropout_0_05=dict(ms=ms_dr, TFLOPs=flops / (ms_dr * 1e-3) / 1e12,
+                                      overhead_vs_plain=ms_dr / ms_step - 1.0))
+    rows = {"train_step": out,
+            "merge_adapter_11008x4096_r64": merge_row(W, B, A, alpha)}
+    rows.update(variant_rows(W))
+    rows.update(quant_rows(W, wq, dev))
+    del W, X, A, B, dY, wq, ws_f, ws_b, Y, U, dX, dA, dB, Xdr, ws_d
+    torch.cuda.empty_cache()
+    return rows
+
+
+def quant_rows(W, wq, dev):
+    """The fused quantiser (NF4 + DQ) and the dequantiser on the 11008 x 4096
+    weight: three / five input copies rotate past the last-level cache so every
+    call streams from HBM."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+
+    N, K = W.shape
+    n = K * N
+    qbytes = n * 4 + n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4
+    L = q.lib()
+    st = q._stream(dev)
+    Ws = [W] + [W * (1.0 + c * 1e-3) for c in (1, 2)]
+    qouts = [q.quantize_nf4_dq(w_, want_absmax=True) for w_ in Ws]
+    qcalls = [_c_call(L.qlora_quantize_nf4_dq, q._ptr(w_), n, q._ptr(o[0]), q._ptr(o[1]),
+                      q._ptr(o[2]), q._ptr(o[3]), None, st) for w_, o in zip(Ws, qouts)]
+    ms_q = _time_ms(_rotate(qcalls), 21, warmup=6)
+    dbytes = n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4 + 2 * n
+    wqs = [q.NF4Tensor(o[0], o[1], o[2], N, K) for o in qouts] + \
+        [q.quantize_weight(W * (1.0 + c * 1e-3)) for c in (3, 4)]
+    del Ws, qouts
+    wds = [torch.empty(N, K, dtype=torch.bfloat16, device=dev) for _ in wqs]
+    wsts = [w_.c_struct() for w_ in wqs]
+    dcalls = [_c_call(L.qlora_dequantize_nf4, ctypes.byref(sc), q._ptr(o), st)
+              for sc, o in zip(wsts, wds)]
+    ms_d = _time_ms(_rotate(dcalls), 20, warmup=5)
+    return {"quantize_nf4_dq": dict(shape=[N, K], ms=ms_q, GBps=qbytes / ms_q / 1e6,
+                                    hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS),
+            "dequantize_nf4": dict(shape=[N, K], ms=ms_d, GBps=dbytes / ms_d / 1e6,
+                                   hbm_frac=dbytes / ms_d / 1e6 / HBM_PEAK_GBS)}
+
+
+def other_rows(dev, steps):
+    """Few-token forward at 1..8 tokens (U launch + GEMV, end to end), the
+    AdamW step, the single 16-token linear and the LLaMA-7B weight set."""
+    import torch
+
+    import bit_nf4_quantized_blockwise_amd as q
+    import workloads as wl
 
     rows = {}
-    if not args.no_rows:
-        n = K * N
-        # quantiser (fused NF4 + DQ): reads 4 B, writes 0.5 + 1/64 + 4/16384 B per weight;
-        # three input copies (541 MB, over twice the 256 MB last-level cache) rotate so
-        # every call reads its weight from HBM
-        qbytes = n * 4 + n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4
-        L = q.lib()
-        st = q._stream(dev)
-        Ws = [W] + [W * (1.0 + c * 1e-3) for c in (1, 2)]
-        qouts = [q.quantize_nf4_dq(w_, want_absmax=True) for w_ in Ws]
-        qcalls = [_c_call(L.qlora_quantize_nf4_dq, q._ptr(w_), n, q._ptr(o[0]), q._ptr(o[1]),
-                          q._ptr(o[2]), q._ptr(o[3]), None, st) for w_, o in zip(Ws, qouts)]
-        it = [0]
-
-        def quant_next():
-            qcalls[it[0] % len(qcalls)]()
-            it[0] += 1
-        ms_q = _time_ms(quant_next, 21, warmup=6)
-        # dequantiser: reads the NF4 storage, writes bf16; five weight and output
-        # copies (565 MB) rotate likewise
-        dbytes = n // 2 + n // 64 + ((n // 64 + 255) // 256) * 4 + 2 * n
-        wqs = [q.NF4Tensor(o[0], o[1], o[2], N, K) for o in qouts] + \
-            [q.quantize_weight(W * (1.0 + c * 1e-3)) for c in (3, 4)]
-        del Ws, qouts
-        wds = [torch.empty(N, K, dtype=torch.bfloat16, device=dev) for _ in wqs]
-        wsts = [w_.c_struct() for w_ in wqs]
-        dcalls = [_c_call(L.qlora_dequantize_nf4, ctypes.byref(sc), q._ptr(o), st)
-                  for sc, o in zip(wsts, wds)]
-
-        def deq_next():
-            dcalls[it[0] % len(dcalls)]()
-            it[0] += 1
-        ms_d = _time_ms(deq_next, 20, warmup=5)
-        wd = wds[0]
-        rows["quantize_nf4_dq"] = dict(shape=[N, K], ms=ms_q, GBps=qbytes / ms_q / 1e6,
-                                       hbm_frac=qbytes / ms_q / 1e6 / HBM_PEAK_GBS)
-        rows["dequantize_nf4"] = dict(shape=[N, K], ms=ms_d, GBps=dbytes / ms_d / 1e6,
-                                      hbm_frac=dbytes / ms_d / 1e6 / HBM_PEAK_GBS)
-        del wqs, wds, wsts, dcalls, qcalls
-        del wd
-        # few-token forward, 8192 -> 28672, r = 16; 5 weight copies (> 2x the MALL)
-        g = wl.GEMV_70B
-        gin = g.inputs(M=8)
-        copies = []
-        Wg = torch.from_numpy(gin["W"]).to(dev)
-        for c in range(5):
-            copies.append(q.quantize_weight(Wg if c == 0 else Wg * (1.0 + c * 1e-3)))
-        del Wg
-        Ag, Bg = gin["A"].to(dev), gin["B"].to(dev)
-        gemv = {}
-        for m in wl.GEMV_TOKENS:
-            Xg = wl.bf16_normal(4, (m, g.k_in), 1.0, tensor=wl.T_X).to(dev)
-            wsg = torch.empty(q.workspace_size(0, m, g.n_out, g.k_in, g.r), dtype=torch.uint8,
-                              device=dev)
-            Yg = torch.empty(m, g.n_out, dtype=torch.bfloat16, device=dev)
-            Ug = torch.empty(m, g.r, dtype=torch.bfloat16, device=dev)
-            it = [0]
-
-            def fwd():
-                w_ = copies[it[0] % len(copies)]
-                it[0] += 1
-                q.linear_fwd(w_, Xg, Ag, Bg, g.alpha, workspace=wsg, Y=Yg, U=Ug)
-            ms = _time_ms(fwd, 50, warmup=5)
-            gbytes = copies[0].nbytes + 2 * m * g.k_in + 2 * g.r * (g.k_in + g.n_out) \
-                + 2 * m * g.n_out + 2 * m * g.r
-            gemv[str(m)] = dict(us=ms * 1e3, GBps=gbytes / ms / 1e6,
-                                hbm_frac=gbytes / ms / 1e6 / HBM_PEAK_GBS)
-        rows["few_token_fwd_8192x28672_r16"] = gemv
-        del copies, Ag, Bg
-        # the same training step with LoRA dropout p = 0.05 on the adapter input
-        Xdr = torch.empty_like(X)
-        ws_d = torch.empty(q.workspace_size(2, M, N, K, r), dtype=torch.uint8, device=dev)
-        it = [0]
-
-        def step_dropout():
-            it[0] += 1
-            q.linear_fwd_dropout(wq, X, A, B, alpha, 0.05, 1234, it[0], workspace=ws_f, Y=Y, U=U,
-                                 Xd=Xdr)
-            q.linear_bwd_dropout(wq, Xdr, dY, A, B, U, alpha, 0.05, 1234, it[0], workspace=ws_d,
-                                 dX=dX, dA=dA, dB=dB)
-        ms_dr = _time_ms(step_dropout, args.steps)
-        rows["train_step_lora_dropout_0.05"] = dict(ms=ms_dr, TFLOPs=flops / (ms_dr * 1e-3) / 1e12,
-                                                    overhead_vs_plain=ms_dr / ms_step - 1.0)
-        del Xdr, ws_d
-        rows["adamw_step_llama7b_lora_r64"] = adamw_row(dev)
-        rows.update(variant_rows(W))
-        rows["merge_adapter_11008x4096_r64"] = merge_row(W, B, A, alpha)
-        rows["single_linear_4096x4096_r8_m16"] = single_linear_row(dev)
-        rows["llama65b_layer_7proj_r64_m2048"] = layer65b_row(dev, 10)
-        rows["llama7b_weight_set_224_matrices"] = weight_set_row(dev)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, wlc)
-
-    out = {
-        "metric": "QLoRA linear fwd+bwd TFLOP/s (LLaMA-7B MLP 4096x11008, 4096 tokens, r=64)",
-        "value": tflops,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) fp32 weight -> NF4+DQ; bf16 N(0,1) X, dY; "
-                "bf16 N(0,0.01) A, B)",
-        "config": {"workload": wlc.name, "tokens": M, "k_in": K, "n_out": N, "r": r,
-                   "alpha": alpha, "flops_per_step": flops,
-                   "fwd_ms": ms_fwd, "bwd_ms": ms_bwd},
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0> (forward dequant-GEMM)",
-            "achieved": gemm_tflops,
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": gemm_tflops / BF16_PEAK_TFLOPS,
-            "ms": ms_gemm,
-            "traffic": read_traffic(),
-        },
-        "rows": rows,
-        "cpu_baseline": cpu,
-        "wall_s": wall,
-    }
-    print(json.dumps(out), flush=True)
+    g = wl.GEMV_70B
+    gin = g.inputs(M=8)
+    Wg = torch.from_numpy(gin["W"]).to(dev)
+    copies = [q.quantize_weight(Wg if c == 0 else Wg * (1.0 + c * 1e-3)) for c in range(5)]
+    del Wg
+    Ag, Bg = gin["A"].to(dev), gin["B"].to(dev)
+    gemv = {}
+    for m in wl.GEMV_TOKENS:
+        Xg = wl.bf16_normal(4, (m, g.k_in), 1.0, tensor=wl.T_X).to(dev)
+        wsg = torch.empty(q.workspace_size(0, m, g.n_out, g.k_in, g.r), dtype=torch.uint8,
+                          device=dev)
+        Yg = torch.empty(m, g.n_out, dtype=torch.bfloat16, device=dev)
+        Ug = torch.empty(m, g.r, dtype=torch.bfloat16, device=dev)
+        calls = [(lambda w_=w_: q.linear_fwd(w_, Xg, Ag, Bg, g.alpha, workspace=wsg, Y=Yg, U=Ug))
+                 for w_ in copies]
+        ms = _time_ms(_rotate(calls), 50, warmup=5)
+        gbytes = copies[0].nbytes + 2 * m * g.k_in + 2 * g.r * (g.k_in + g.n_out) \
+            + 2 * m * g.n_out + 2 * m * g.r
+        gemv[str(m)] = dict(us=ms * 1e3, GBps=gbytes / ms / 1e6,
+                            hbm_frac=gbytes / ms / 1e6 / HBM_PEAK_GBS)
+    rows["few_token_fwd_8192x28672_r16"] = gemv
+    del copies, Ag, Bg
+    torch.cuda.empty_cache()
+    rows["adamw_step_llama7b_lora_r64"] = adamw_row(dev)
+    rows["single_linear_4096x4096_r8_m16"] = single_linear_row(dev)
+    rows["llama7b_weight_set_224_matrices"] = weight_set_row(dev)
+    return rows
 
 
 def single_linear_row(dev):
@@ -793,49 +932,6 @@ def weight_set_row(dev):
                 dequantize=dict(ms=ms_d, GB=dbytes / 1e9, GBps=dbytes / ms_d / 1e6,
                                 hbm_frac=dbytes / ms_d / 1e6 / HBM_PEAK_GBS,
                                 ms_one_call_per_matrix=ms_d1))
-
-
-def layer65b_row(dev, steps):
-    """The seven projections of one LLaMA-65B-shaped decoder layer (q, k, v, o
-    8192x8192; gate, up 8192 -> 22016; down 22016 -> 8192), r = 64, alpha = 16,
-    2048 tokens, forward + backward of each: 6,754.24 GFLOP per layer step.
-    Inputs drawn on the GPU (seeded torch normals: W x 0.02, A and B x 0.01,
-    X and dY x 1); the time does not depend on the values."""
-    import torch
-
-    import bit_nf4_quantized_blockwise_amd as q
-    import workloads as wl
-
-    gen = torch.Generator(device=dev).manual_seed(wl.SEED + 5)
-    per, total_ms, total_flops = {}, 0.0, 0
-    for wlc in wl.LLAMA65B_LAYER:
-        M, K, N, r = wlc.M, wlc.k_in, wlc.n_out, wlc.r
-        W = torch.randn(N, K, generator=gen, device=dev) * 0.02
-        wq = q.quantize_weight(W)
-        del W
-        bf = lambda *shape, s: (torch.randn(*shape, generator=gen, device=dev) * s).to(torch.bfloat16)
-        A, B, X, dY = bf(r, K, s=0.01), bf(N, r, s=0.01), bf(M, K, s=1.0), bf(M, N, s=1.0)
-        ws_f = torch.empty(q.workspace_size(0, M, N, K, r), dtype=torch.uint8, device=dev)
-        ws_b = torch.empty(q.workspace_size(1, M, N, K, r), dtype=torch.uint8, device=dev)
-        Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        U = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
-        dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
-        dA = torch.empty(r, K, dtype=torch.float32, device=dev)
-        dB = torch.empty(N, r, dtype=torch.float32, device=dev)
-
-        def step():
-            q.linear_fwd(wq, X, A, B, wlc.alpha, workspace=ws_f, Y=Y, U=U)
-            q.linear_bwd(wq, X, dY, A, B, U, wlc.alpha, workspace=ws_b, dX=dX, dA=dA, dB=dB)
-        ms = _time_ms(step, steps, warmup=3)
-        flops = wlc.flops_fwd + wlc.flops_bwd
-        per[wlc.name] = dict(ms=ms, TFLOPs=flops / (ms * 1e-3) / 1e12)
-        total_ms += ms
-        total_flops += flops
-        del wq, A, B, X, dY, ws_f, ws_b, Y, U, dX, dA, dB
-    torch.cuda.empty_cache()
-    return dict(projections=per, ms=total_ms, GFLOP=total_flops / 1e9,
-                TFLOPs=total_flops / (total_ms * 1e-3) / 1e12,
-                mfma_frac=total_flops / (total_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
 
 
 def adamw_row(dev):
@@ -965,96 +1061,130 @@ def merge_row(W, B, A, alpha):
                 ms_merge_requant_16bit=ms_mq, ms_merge_requant_4bit=ms_m4, **out)
 
 
-def cpu_baseline(inp, wlc):
-    """The oracle, untuned, on the host cores: decode the weight from its NF4 +
-    DQ storage and run the float64 forward and backward for the whole batch."""
-    import numpy as np
+def cpu_baseline():
+    """The oracle, untuned, on the host cores, BLAS threads pinned to the
+    stated count: decode the weight from its NF4 + DQ storage, then the
+    float64 forward and backward, on a bounded sample of the layer step (its
+    q projection, 8192 -> 8192, all 2048 tokens, repeated for about 10 s),
+    plus the rate of one thread on 256 of those tokens and the oracle's wall
+    time on the other workloads."""
     import torch
+    from threadpoolctl import threadpool_limits
 
+    import workloads as wl
     from oracle.linear import linear_bwd, linear_fwd, lora_scale
     from oracle.quant import bf16_to_f64, dequantize_nf4, double_quant, quantize_nf4
 
-    cores = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    wlc = wl.LLAMA65B_LAYER[0]
+    inp = wlc.inputs()
     packed, absmax = quantize_nf4(inp["W"].ravel())
     qa, c2 = double_quant(absmax)
     f64 = lambda t: t.to(torch.float64).numpy()
     X, A, B, dY = (f64(inp[k]) for k in ("X", "A", "B", "dY"))
     s = lora_scale(wlc.alpha, wlc.r)
-    reps, t0 = 0, time.perf_counter()
-    while reps == 0 or time.perf_counter() - t0 < 10.0:  # about 10 s of host work
-        w64 = bf16_to_f64(dequantize_nf4(packed, qa, c2, inp["W"].size)).reshape(wlc.n_out,
-                                                                                 wlc.k_in)
-        Y, U = linear_fwd(X, w64, A, B, s)
-        dX, dA, dB = linear_bwd(X, dY, w64, A, B, s)
-        reps += 1
-    dt = (time.perf_counter() - t0) / reps
+    shape = (wlc.n_out, wlc.k_in)
+
+    def one(Xs, dYs):
+        w64 = bf16_to_f64(dequantize_nf4(packed, qa, c2, inp["W"].size)).reshape(shape)
+        linear_fwd(Xs, w64, A, B, s)
+        linear_bwd(Xs, dYs, w64, A, B, s)
+
     flops = wlc.flops_fwd + wlc.flops_bwd
+    with threadpool_limits(cores):
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 10.0:
+            one(X, dY)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+    m1 = 256
+    f1 = flops * m1 / wlc.M
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        one(X[:m1], dY[:m1])
+        dt1 = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds_per_step": dt, "steps": reps,
-            "sample": f"full steps of {wlc.name} repeated for about 10 s: decode + fp64 "
-                      "forward + backward, all 4096 tokens (numpy, float64)",
-            "per_config": oracle_per_config(flops / dt)}
+            "seconds_per_sample": dt, "repeats": reps,
+            "sample": f"the q projection of the layer step ({wlc.name}: decode from NF4 + DQ, "
+                      "float64 forward + backward, all 2048 tokens) repeated for about 10 s, "
+                      f"numpy/OpenBLAS pinned to {cores} threads; the layer step is 12.0x its flops",
+            "one_thread": {"TFLOPs": f1 / dt1 / 1e12, "seconds": dt1,
+                           "sample": f"the same projection on {m1} of the 2048 tokens, 1 thread "
+                                     "(decode of the whole weight included)"},
+            "per_config": oracle_per_config(cores)}
 
 
-def oracle_per_config(rate_step):
-    """The oracle's wall time on the other workloads, each bounded to a few
-    seconds: measured in full where that fits, else on a stated sample and
-    extrapolated (labelled).  rate_step: the oracle's float64 flop rate on the
-    training step, measured above."""
+def oracle_per_config(cores):
+    """The oracle's wall time on the other workloads (BLAS pinned to `cores`
+    threads): measured in full where that takes a few seconds, else on a
+    stated sample and extrapolated (labelled)."""
     import numpy as np
     import torch
+    from threadpoolctl import threadpool_limits
 
     import workloads as wl
-    from oracle.linear import linear_fwd, lora_scale
+    from oracle.linear import linear_bwd, linear_fwd, lora_scale
     from oracle.quant import bf16_to_f64, dequantize_nf4, double_quant, quantize_nf4
 
     f64 = lambda t: t.to(torch.float64).numpy()
     out = {}
-    # single linear: quantise + DQ, decode and the 16-token forward, in full
-    w1 = wl.SINGLE_LINEAR
-    inp = w1.inputs()
-    t0 = time.perf_counter()
-    p1, a1 = quantize_nf4(inp["W"].ravel())
-    q1, c1 = double_quant(a1)
-    w64 = bf16_to_f64(dequantize_nf4(p1, q1, c1, inp["W"].size)).reshape(w1.n_out, w1.k_in)
-    linear_fwd(f64(inp["X"]), w64, f64(inp["A"]), f64(inp["B"]), lora_scale(w1.alpha, w1.r))
-    out["single_linear_4096x4096_r8_m16"] = dict(seconds=time.perf_counter() - t0,
-                                                 what="quantise + DQ + decode + forward, in full")
-    # weight set: one 4096 x 4096 matrix (with its outliers), scaled to 6.48 G weights
-    w = wl.llama7b_weight(0, 0).ravel()
-    t0 = time.perf_counter()
-    p2, a2 = quantize_nf4(w)
-    q2, c2_ = double_quant(a2)
-    tq = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    dequantize_nf4(p2, q2, c2_, w.size)
-    td = time.perf_counter() - t0
-    total = sum(n * k for _, n, k in wl.LLAMA7B_MATRICES) * wl.LLAMA7B_LAYERS
-    out["llama7b_weight_set_224_matrices"] = dict(
-        seconds_quantize_dq=tq * total / w.size, seconds_dequantize=td * total / w.size,
-        what=f"extrapolated from layer 0's q matrix ({w.size} weights) to {total} weights")
-    # few-token forward: 1024 of the 28672 output rows of the 8192 -> 28672 weight
-    # (the first rows of the same seeded stream), M = 1, scaled to all rows
-    g = wl.GEMV_70B
-    rows = 1024
-    wr = wl.rng(g.workload, 0, 0, wl.T_W).standard_normal(rows * g.k_in, dtype=np.float32)
-    wr *= np.float32(0.02)
-    gin = g.inputs(M=1, with_dy=False)
-    t0 = time.perf_counter()
-    p4, a4 = quantize_nf4(wr)
-    q4, c4 = double_quant(a4)
-    w4 = bf16_to_f64(dequantize_nf4(p4, q4, c4, wr.size)).reshape(rows, g.k_in)
-    linear_fwd(f64(gin["X"]), w4, f64(gin["A"]), f64(gin["B"][:rows]), lora_scale(g.alpha, g.r))
-    dt = time.perf_counter() - t0
-    out["few_token_fwd_8192x28672_r16"] = dict(
-        seconds_quantize_and_forward_m1=dt * g.n_out / rows,
-        what=f"extrapolated from {rows} of {g.n_out} output rows (quantise + DQ + decode "
-             "+ forward of one token)")
-    # the LLaMA-65B layer: its flops at the training step's measured float64 rate
-    fl = sum(x.flops_fwd + x.flops_bwd for x in wl.LLAMA65B_LAYER)
-    out["llama65b_layer_7proj_r64_m2048"] = dict(
-        seconds=fl / rate_step, what="extrapolated: 6,754 GFLOP at the float64 rate measured "
-                                     "on the LLaMA-7B MLP training step (decode excluded)")
+    with threadpool_limits(cores):
+        # single linear: quantise + DQ, decode and the 16-token forward, in full
+        w1 = wl.SINGLE_LINEAR
+        inp = w1.inputs()
+        t0 = time.perf_counter()
+        p1, a1 = quantize_nf4(inp["W"].ravel())
+        q1, c1 = double_quant(a1)
+        w64 = bf16_to_f64(dequantize_nf4(p1, q1, c1, inp["W"].size)).reshape(w1.n_out, w1.k_in)
+        linear_fwd(f64(inp["X"]), w64, f64(inp["A"]), f64(inp["B"]), lora_scale(w1.alpha, w1.r))
+        out["single_linear_4096x4096_r8_m16"] = dict(
+            seconds=time.perf_counter() - t0, what="quantise + DQ + decode + forward, in full")
+        # LLaMA-7B MLP training step: decode + forward + backward, in full
+        w3 = wl.LLAMA7B_MLP
+        inp = w3.inputs()
+        p3, a3 = quantize_nf4(inp["W"].ravel())
+        q3, c3 = double_quant(a3)
+        X, A, B, dY = (f64(inp[k]) for k in ("X", "A", "B", "dY"))
+        t0 = time.perf_counter()
+        w64 = bf16_to_f64(dequantize_nf4(p3, q3, c3, inp["W"].size)).reshape(w3.n_out, w3.k_in)
+        linear_fwd(X, w64, A, B, lora_scale(w3.alpha, w3.r))
+        linear_bwd(X, dY, w64, A, B, lora_scale(w3.alpha, w3.r))
+        dt = time.perf_counter() - t0
+        out["llama7b_mlp_4096x11008_r64_m4096"] = dict(
+            seconds=dt, TFLOPs=(w3.flops_fwd + w3.flops_bwd) / dt / 1e12,
+            what="decode + float64 forward + backward, all 4096 tokens, in full")
+        del X, A, B, dY, w64
+        # weight set: one 4096 x 4096 matrix (with its outliers), scaled to 6.48 G weights
+        w = wl.llama7b_weight(0, 0).ravel()
+        t0 = time.perf_counter()
+        p2, a2 = quantize_nf4(w)
+        q2, c2_ = double_quant(a2)
+        tq = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        dequantize_nf4(p2, q2, c2_, w.size)
+        td = time.perf_counter() - t0
+        total = sum(n * k for _, n, k in wl.LLAMA7B_MATRICES) * wl.LLAMA7B_LAYERS
+        out["llama7b_weight_set_224_matrices"] = dict(
+            seconds_quantize_dq=tq * total / w.size, seconds_dequantize=td * total / w.size,
+            what=f"extrapolated from layer 0's q matrix ({w.size} weights) to {total} weights")
+        # few-token forward: 1024 of the 28672 output rows of the 8192 -> 28672 weight
+        # (the first rows of the same seeded stream), M = 1, scaled to all rows
+        g = wl.GEMV_70B
+        rows = 1024
+        wr = wl.rng(g.workload, 0, 0, wl.T_W).standard_normal(rows * g.k_in, dtype=np.float32)
+        wr *= np.float32(0.02)
+        gin = g.inputs(M=1, with_dy=False, with_w=False)
+        t0 = time.perf_counter()
+        p4, a4 = quantize_nf4(wr)
+        q4, c4 = double_quant(a4)
+        w4 = bf16_to_f64(dequantize_nf4(p4, q4, c4, wr.size)).reshape(rows, g.k_in)
+        linear_fwd(f64(gin["X"]), w4, f64(gin["A"]), f64(gin["B"][:rows]),
+                   lora_scale(g.alpha, g.r))
+        dt = time.perf_counter() - t0
+        out["few_token_fwd_8192x28672_r16"] = dict(
+            seconds_quantize_and_forward_m1=dt * g.n_out / rows,
+            what=f"extrapolated from {rows} of {g.n_out} output rows (quantise + DQ + decode "
+                 "+ forward of one token)")
     return out
 
 

@@ -54,20 +54,34 @@ def test_stats_summary_per_grid(tmp_path):
         w = csv.DictWriter(fh, fieldnames=fields)
         w.writeheader()
         t = 0
-        for i in range(4):  # the bench shape: 688 tiles of 256x256
-            w.writerow({"Kernel_Name": f"void qlora::{bench.FWD_GEMM}(qlora::GemmArgs)",
-                        "Grid_Size_X": 688 * 256, "Grid_Size_Y": 1, "Start_Timestamp": t,
-                        "End_Timestamp": t + 400_000})
-            t += 500_000
+        for i in range(4):  # two launch grids of the forward GEMM, equally often
+            for tiles, us in ((256, 300), (688, 700)):
+                w.writerow({"Kernel_Name": f"void qlora::{bench.FWD_GEMM}(qlora::GemmArgs)",
+                            "Grid_Size_X": tiles * 256, "Grid_Size_Y": 1, "Start_Timestamp": t,
+                            "End_Timestamp": t + us * 1000})
+                t += 1_000_000
         w.writerow({"Kernel_Name": "qlora::reduce_partials4_kernel()", "Grid_Size_X": 1024,
                     "Grid_Size_Y": 1, "Start_Timestamp": t, "End_Timestamp": t + 5_000})
     stats.write_text("Name,Calls\n")
     log = tmp_path / "log.txt"
-    log.write_text(json.dumps({"metric": "m", "value": 1.0, "ms_per_step": 0.9, "rows": {},
-                               "roofline": {"ms": 0.4},
-                               "config": {"tokens": 4096, "n_out": 11008}}) + "\n")
+    log.write_text(json.dumps({"metric": "m", "value": 1.0, "ms_per_step": 0.9,
+                               "rows": {"llama65b_layer_projections": {}},
+                               "roofline": {"us_per_launch": 500.0}}) + "\n")
     out = tmp_path / "stats.txt"
     bench.summarize_stats(str(stats), str(log), str(out))
     txt = out.read_text()
     assert "--no-rows" in txt
-    assert "grid 176128x1): 4 calls, mean 400.0 us" in txt
+    assert "(trace, all grids): 8 calls, mean 500.0 us" in txt
+    assert "176128x1" in txt and "65536x1" in txt
+
+
+def test_layer_forward_algorithmic_bytes():
+    """Per launch of the forward GEMM: the NF4 + DQ weight (0.5 + 1/64 B per
+    weight and 4 B per 16384), X, U, B and Y in bf16, once each."""
+    tot = bench._layer_fwd_algo_bytes()
+    M, r = 2048, 64
+    ref = 0
+    for K, N in [(8192, 8192)] * 4 + [(8192, 22016)] * 2 + [(22016, 8192)]:
+        n = K * N
+        ref += n * 0.5 + n / 64 + 4 * n / 16384 + 2 * (M * K + M * r + N * r + M * N)
+    assert abs(tot - ref) < 1e-6 * ref
