@@ -94,6 +94,8 @@ _SIGNATURES = {
     "qlora_adamw_step": ([ctypes.POINTER(AdamWTensor), _I32, _F, _F, _F, _F, _F, _I64, _F, _P, _P,
                           _SZ, _P], _I32),
     "qlora_adamw_workspace_size": ([_I32], _SZ),
+    "qlora_adamw_step_paged": ([ctypes.POINTER(AdamWTensor), _I32, _F, _F, _F, _F, _F, _I64, _F, _P,
+                                _P, _SZ, _P, _SZ, _P], _I32),
     "qlora_adamw_plan_size": ([ctypes.POINTER(AdamWTensor), _I32], _SZ),
     "qlora_adamw_plan_init": ([ctypes.POINTER(AdamWTensor), _I32, _P, _SZ,
                                ctypes.POINTER(AdamWPlanC), _P], _I32),
@@ -503,6 +505,33 @@ def adamw_step_list(lst, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight
                                   max_grad_norm, _ptr(grad_norm), _ptr(workspace),
                                   workspace.numel(), _stream(lst.device)),
            "qlora_adamw_step")
+
+
+def adamw_step_paged(params, grads, ms_host, vs_host, step, window, lr=2e-4, beta1=0.9,
+                     beta2=0.999, eps=1e-8, weight_decay=0.001, max_grad_norm=0.3,
+                     params_bf16=None, grad_norm=None, workspace=None):
+    """adamw_step with the states m, v in pinned host memory (CPU tensors made
+    with pin_memory=True), paged through `window` (a CUDA uint8 tensor of at
+    least 16 KB).  The copies run on the current stream: synchronise it before
+    reading m or v on the host."""
+    n = len(params)
+    pbs = params_bf16 if params_bf16 is not None else [None] * n
+    arr = (AdamWTensor * max(n, 1))()
+    for i in range(n):
+        p = params[i]
+        for t in (grads[i], ms_host[i], vs_host[i]):
+            if t.numel() != p.numel():
+                raise ValueError(f"tensor {i}: sizes differ")
+        arr[i] = AdamWTensor(p.data_ptr(), grads[i].data_ptr(), ms_host[i].data_ptr(),
+                             vs_host[i].data_ptr(),
+                             pbs[i].data_ptr() if pbs[i] is not None else None, p.numel())
+    dev = params[0].device if n else window.device
+    if workspace is None:
+        workspace = torch.empty(adamw_workspace_size(n), dtype=torch.uint8, device=dev)
+    _check(lib().qlora_adamw_step_paged(arr, n, lr, beta1, beta2, eps, weight_decay, step,
+                                        max_grad_norm, _ptr(grad_norm), _ptr(window),
+                                        window.numel(), _ptr(workspace), workspace.numel(),
+                                        _stream(dev)), "qlora_adamw_step_paged")
 
 
 class AdamWPlan:

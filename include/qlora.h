@@ -342,6 +342,26 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor *tensors /* host array */
 /* Bytes of workspace qlora_adamw_step needs for `count` tensors (0 if count < 0). */
 size_t qlora_adamw_workspace_size(int32_t count);
 
+/* Paged optimizer states ("QLoRAの理論と実装", §5-3 Paged Optimizers: the
+ * optimizer states leave GPU memory when it runs short and come back to the
+ * GPU when the update needs them).  Exactly qlora_adamw_step (same bits),
+ * except that every tensor's m and v are HOST pointers into pinned memory
+ * (hipHostMalloc or another page-locked allocation; else
+ * QLORA_ERR_UNSUPPORTED) that the caller owns and that stays the states'
+ * home: they are paged in to `window` (caller-owned device memory,
+ * window_bytes >= 16384, else QLORA_ERR_WORKSPACE), updated there and paged
+ * out again, a window's worth at a time, all on `stream` (asynchronous copies;
+ * the host must not touch m and v until the stream reaches them).  The
+ * device then holds only p, g and the window — 8 bytes per parameter less
+ * than the resident step.  These GPUs run without demand paging, so the
+ * transfers are explicit; on one stream they do not overlap the update.
+ * Workspace as for qlora_adamw_step. */
+qlora_status qlora_adamw_step_paged(const qlora_adamw_tensor *tensors /* host array; m, v host */,
+                                    int32_t count, float lr, float beta1, float beta2, float eps,
+                                    float weight_decay, int64_t step, float max_grad_norm,
+                                    float *grad_norm, void *window, size_t window_bytes,
+                                    void *workspace, size_t ws_bytes, void *stream);
+
 /* A prepared tensor list for a training loop that steps the same tensors
  * every iteration: the descriptors and a chunk -> tensor map copied once into
  * a caller-owned device buffer, so that a step is one norm pass, one clip and

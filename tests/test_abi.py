@@ -195,6 +195,16 @@ def test_adamw_argument_errors(L):
     assert call(a=bad, n=1) == NULL
     bad = (T * 1)(T(FAKE, FAKE, FAKE, FAKE, None, -1))
     assert call(a=bad, n=1) == SHAPE
+    pg = L.qlora_adamw_step_paged
+
+    def paged(win=FAKE, winb=1 << 20, **kw):
+        p = dict(args, **kw)
+        return pg(arr, 2, p["lr"], p["b1"], p["b2"], p["eps"], p["wd"], p["step"], p["clip"], None,
+                  win, winb, FAKE, 1 << 20, None)
+    assert paged(win=None) == WS
+    assert paged(winb=16383) == WS
+    assert paged(win=MIS) == WS
+    assert paged(step=0) == SHAPE
     assert L.qlora_adamw_workspace_size(-1) == 0
     assert L.qlora_adamw_workspace_size(0) >= 256
     assert L.qlora_adamw_workspace_size(200) >= 5 * 256 * 8

@@ -86,6 +86,10 @@ def _run_case(M, K, N, r, alpha, seed, bwd=True):
     (257, 320, 1001, 64, 16.0),   # ... many-token path, several column tiles
     (130, 64, 13, 3, 16.0),       # ... with a rank that is not a multiple of 8
     (21, 128, 1, 1, 2.0),         # a single output column
+    (1, 11008, 4096, 16, 32.0),   # small weight split over k, U formed in the pass (ragged split)
+    (9, 2048, 1000, 72, 16.0),    # ... two token groups, five rank groups
+    (16, 4096, 4096, 256, 16.0),  # ... largest rank
+    (5, 3072, 75, 3, 16.0),       # ... rank and n_out not multiples of 8
 ])
 def test_small_shapes(M, K, N, r, alpha):
     _run_case(M, K, N, r, alpha, seed=M + K + N + r)

@@ -162,3 +162,71 @@ def test_prepared_list_repeatable():
         outs.append((_np(p).view(np.uint32), _np(m).view(np.uint32), _np(v).view(np.uint32)))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
+
+
+def _paged_vs_resident(sizes, steps, window_bytes, max_norm, seed):
+    """The paged step (m, v in pinned host memory, streamed through a device
+    window) against the resident step from the same state: p, m, v, the bf16
+    copies and the norm bit for bit, step after step."""
+    rng = np.random.default_rng(seed)
+    dev = torch.device("cuda:0")
+    st = [_state(rng, n, 1) for n in sizes]
+    P1 = [torch.from_numpy(s[0].copy()).to(dev) for s in st]
+    P2 = [x.clone() for x in P1]
+    M1 = [torch.from_numpy(s[2].copy()).to(dev) for s in st]
+    V1 = [torch.from_numpy(s[3].copy()).to(dev) for s in st]
+    M2 = [torch.from_numpy(s[2].copy()).pin_memory() for s in st]
+    V2 = [torch.from_numpy(s[3].copy()).pin_memory() for s in st]
+    G = [torch.empty(n, dtype=torch.float32, device=dev) for n in sizes]
+    PB1 = [torch.empty(n, dtype=torch.bfloat16, device=dev) if i % 2 == 0 else None
+           for i, n in enumerate(sizes)]
+    PB2 = [torch.empty_like(x) if x is not None else None for x in PB1]
+    n1, n2 = (torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(2))
+    window = torch.empty(window_bytes, dtype=torch.uint8, device=dev)
+    for step in steps:
+        say(f"[adamw paged] {len(sizes)} tensors window={window_bytes} step={step} "
+            f"max_norm={max_norm}")
+        for t in G:
+            t.copy_(torch.from_numpy((rng.standard_normal(t.numel()) * 0.3).astype(np.float32)))
+        q.adamw_step(P1, G, M1, V1, step, max_grad_norm=max_norm, params_bf16=PB1, grad_norm=n1)
+        q.adamw_step_paged(P2, G, M2, V2, step, window, max_grad_norm=max_norm, params_bf16=PB2,
+                           grad_norm=n2)
+        torch.cuda.synchronize()
+        assert torch.equal(n1.view(torch.int32), n2.view(torch.int32))
+        for i in range(len(sizes)):
+            assert torch.equal(P1[i].view(torch.int32), P2[i].view(torch.int32)), i
+            assert torch.equal(host(M1[i]).view(torch.int32), M2[i].view(torch.int32)), i
+            assert torch.equal(host(V1[i]).view(torch.int32), V2[i].view(torch.int32)), i
+            if PB1[i] is not None:
+                assert torch.equal(PB1[i].view(torch.int16), PB2[i].view(torch.int16)), i
+
+
+@pytest.mark.parametrize("window_kb", [16, 1024, 65536])
+@pytest.mark.parametrize("max_norm", [0.3, 0.0])
+def test_paged_step_equals_resident_step(window_kb, max_norm):
+    # the smallest window splits every tensor of more than 2048 elements into
+    # many pieces; the largest holds the whole set in one batch
+    _paged_vs_resident([1, 3, 4, 5, 257, 4096 * 64 + 3, 0, 11008, 100003], [1, 2, 3],
+                       window_kb * 1024, max_norm, seed=window_kb)
+
+
+def test_paged_step_more_pieces_than_one_launch_holds():
+    # 100 small tensors: batches close at 48 descriptors before the window fills
+    _paged_vs_resident([17 + (i * 37) % 300 for i in range(100)], [1, 2], 1 << 20, 0.3, seed=11)
+
+
+def test_paged_step_rejects_unpinned_states_and_small_windows():
+    dev = torch.device("cuda:0")
+    p = torch.zeros(100, device=dev)
+    g = torch.ones(100, device=dev)
+    m_pin, v_pin = torch.zeros(100).pin_memory(), torch.zeros(100).pin_memory()
+    m_pageable = torch.zeros(100)
+    win = torch.empty(16384, dtype=torch.uint8, device=dev)
+    with pytest.raises(q.QloraError) as e:
+        q.adamw_step_paged([p], [g], [m_pageable], [v_pin], 1, win)
+    assert e.value.status == 4
+    with pytest.raises(q.QloraError) as e:
+        q.adamw_step_paged([p], [g], [m_pin], [v_pin], 1, win[:16000])
+    assert e.value.status == 5
+    torch.cuda.synchronize()
+    assert torch.all(p == 0)  # nothing ran
