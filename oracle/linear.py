@@ -62,16 +62,3 @@ def linear_bwd(X, dY, W_hat, A, B, s):
     dA = s * (V.T @ X)              # (α/r)·Bᵀ·∂L/∂Y·Xᵀ
     dB = s * (dY.T @ (X @ A.T))     # (α/r)·∂L/∂Y·(A·X)ᵀ
     return dX, dA, dB
-
-
-def linear_fwd_rows(X, W_hat, A, B, s, rows):
-    """Y for a subset of token rows (same arithmetic as linear_fwd)."""
-    Y, U = linear_fwd(np.asarray(X)[rows], W_hat, A, B, s)
-    return Y, U
-
-
-def linear_bwd_dx_rows(dY, W_hat, A, B, s, rows):
-    """dX for a subset of token rows (same arithmetic as linear_bwd)."""
-    dY = np.asarray(dY, dtype=np.float64)[rows]
-    V = dY @ np.asarray(B, dtype=np.float64)
-    return dY @ np.asarray(W_hat, dtype=np.float64) + s * (V @ np.asarray(A, dtype=np.float64))
