@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlora.so")
-SOURCES = ["qlora_quant.hip", "qlora_gemm.hip", "qlora_gemv.hip", "qlora_aux.hip", "qlora_optim.hip", "qlora_merge.hip",
+SOURCES = ["qlora_quant.hip", "qlora_gemm.hip", "qlora_adapter.hip", "qlora_gemv.hip", "qlora_aux.hip", "qlora_optim.hip", "qlora_merge.hip",
            "qlora_capi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -98,13 +98,9 @@ Plan plan(int64_t rows, int64_t cols, int64_t red, int mt, int nt, bool allow_sp
 // Tile shapes of the instantiated kernels.
 constexpr int BIG_MT = 256, BIG_NT = 256;   // NF4 GEMMs, many tokens
 constexpr int SM_MT = 64, SM_NT = 256;      // NF4 GEMMs, few tokens (split-K)
-constexpr int SK_MT = 128, SK_NT = 64;      // skinny: U = X·Aᵀ, V = dY·B
-constexpr int TR_MT = 64, TR_NT = 256;      // token-reduction: dA, dB
+constexpr int TR_MT = 64, TR_NT = 256;      // dropout's masked rank-r term T = s·mask ⊙ (V·A)
 constexpr int64_t kBigM = 128;              // use the big tiles from this many tokens on
 constexpr int64_t kFewM = 16;               // up to this many tokens: the streaming GEMV
-// split-K target for the memory-bound rank-r products: one workgroup per CU
-// (more only multiplies the partial sums written and read back)
-constexpr int kSkinnyWgs = 256;
 
 bool use_big(int64_t M) { return M >= kBigM; }
 bool use_gemv(int64_t M) { return M <= kFewM; }
@@ -135,10 +131,49 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+// Rank-r products on the streaming kernels: stream tiles of 128, groups of up
+// to 128 ranks (blocks of 32), and the reduction split so that about one
+// workgroup per CU runs (each holds a 96-144 KB LDS ring).
+constexpr int kAdapterWgs = 256;
+struct AdPlan {
+  int tiles, ncg, nb, nkt, ktps, nsplit;
+  int64_t ldp;  // pitch of a partial-sum row (rows: ranks; TR: stream indices)
+};
+
+// row_pitch > 0 (the column kernel, whose reduction runs over rows): a
+// split's rows of the widest operand stay below 2^31 bytes, the reach of a
+// buffer offset.
+// wgs: workgroups to aim for (one per CU for a launch of its own, half that
+// for each of the two products sharing adapter_dy_kernel); the split count
+// rounds down, so a launch never spills a few workgroups into a second round.
+AdPlan ad_plan(int64_t nout, int64_t red, int32_t r, bool tr = false, int64_t row_pitch = 0,
+               int wgs = kAdapterWgs) {
+  AdPlan p;
+  p.tiles = (int)ceil_div(nout, kAdapterTile);
+  p.ncg = (int)ceil_div(r, 128);
+  p.nb = p.ncg > 1 ? 4 : (r <= 32 ? 1 : (r <= 64 ? 2 : 4));
+  p.nkt = (int)std::max<int64_t>(1, ceil_div(red, 64));
+  const int base = p.tiles * p.ncg;  // 0 when there are no outputs (no launch then)
+  const int s = (base == 0 || base >= wgs) ? 1 : std::min(p.nkt, wgs / base);
+  p.ktps = (int)ceil_div(p.nkt, s);
+  if (row_pitch > 0)
+    p.ktps = (int)std::min<int64_t>(p.ktps, std::max<int64_t>(1, 0x7fffffffLL / (128 * row_pitch) - 1));
+  p.nsplit = (int)ceil_div(p.nkt, p.ktps);
+  p.ldp = tr ? (int64_t)p.tiles * kAdapterTile : (int64_t)32 * p.nb * p.ncg;
+  return p;
+}
+
+// Bytes of one product's partial sums.
+size_t ad_part_bytes(const AdPlan& p, int64_t nout, bool tr = false) {
+  const int64_t rows = tr ? (int64_t)32 * p.nb * p.ncg : nout;
+  return (size_t)p.nsplit * rows * p.ldp * 4;
+}
+
 // Forward workspace layout.
 struct FwdWs {
   size_t u_part, pad_u, pad_b, y_part, total;
-  Plan pu, py;
+  AdPlan pu;
+  Plan py;
   int64_t rp;
 };
 
@@ -152,11 +187,10 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
     w.total = std::max<size_t>(g.ksplit > 1 ? align256((size_t)g.ksplit * M * N * 4) : 0, 256);
     return w;
   }
-  w.pu = plan(M, r, K, SK_MT, SK_NT, true, kSkinnyWgs);
-  const int64_t ldu = (int64_t)w.pu.tiles_n * SK_NT;
+  w.pu = ad_plan(M, K, r);
   size_t off = 0;
   w.u_part = off;
-  off += align256((size_t)w.pu.nsplit * M * ldu * 4);
+  off += align256(ad_part_bytes(w.pu, M));
   w.pad_u = w.pad_b = off;
   if (r % 8 != 0) {
     w.pad_u = off;
@@ -174,38 +208,44 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t bt, v, vt, ut, at, dyp, part, total;
-  Plan pv, pdx, pda, pdb;
-  int64_t rp, Mp, Np;
+  size_t bp, up, dyp, v, part, part_db, total;
+  AdPlan pv, pda, pdb;
+  Plan pdx;
+  int64_t rp, Np;
 };
 
 // n_out not a multiple of 8: dY is copied to a zero-padded pitch Np (its rows
-// are then 16-byte aligned for the GEMM loaders), and Bᵀ gets the same pitch.
+// are then 16-byte aligned for the loaders); a rank that is not a multiple of
+// 8 gets padded copies of B and U for the same reason.
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w{};
   w.rp = rup(r, 8);
-  w.Mp = rup(std::max<int64_t>(M, 1), 8);
   w.Np = rup(N, 8);
   size_t off = 0;
-  w.bt = off; off += align256((size_t)r * w.Np * 2);
+  w.bp = w.up = off;
+  if (w.rp != r) {
+    w.bp = off; off += align256((size_t)N * w.rp * 2);
+    w.up = off; off += align256((size_t)M * w.rp * 2);
+  }
   w.dyp = off;
   if (w.Np != N) off += align256((size_t)M * w.Np * 2);
   w.v = off; off += align256((size_t)M * w.rp * 2);
-  w.vt = off; off += align256((size_t)r * w.Mp * 2);
-  w.ut = off; off += align256((size_t)r * w.Mp * 2);
-  w.at = off; off += align256((size_t)K * w.rp * 2);
-  w.part = off;
-  w.pv = plan(M, r, N, SK_MT, SK_NT, true, kSkinnyWgs);
-  size_t part = (size_t)w.pv.nsplit * M * ((size_t)w.pv.tiles_n * SK_NT) * 4;
+  // V's and dB's partial sums live at once (one launch forms both); dX's
+  // split partials and dA's reuse V's region afterwards
+  // (dB is planned first; V gets the workgroups left in one round)
+  w.pdb = ad_plan(N, M, r, false, std::max<int64_t>(w.Np, w.rp), kAdapterWgs / 2);
+  const int db_wgs = w.pdb.tiles * w.pdb.nsplit * w.pdb.ncg;
+  w.pv = ad_plan(M, w.Np, r, false, 0, std::max(kAdapterWgs - db_wgs, kAdapterWgs / 4));
+  w.pda = ad_plan(K, M, r, true, std::max<int64_t>(K, w.rp));
+  size_t part = std::max(ad_part_bytes(w.pv, M), ad_part_bytes(w.pda, K, true));
   if (!use_big(M)) {
     w.pdx = plan(M, K, N, SM_MT, SM_NT, true);
     part = std::max(part, (size_t)w.pdx.nsplit * M * K * 4);
   }
-  w.pda = plan(r, K, M, TR_MT, TR_NT, true, kSkinnyWgs);
-  part = std::max(part, (size_t)w.pda.nsplit * r * K * 4);
-  w.pdb = plan(r, N, M, TR_MT, TR_NT, true, kSkinnyWgs);
-  part = std::max(part, (size_t)w.pdb.nsplit * r * N * 4);
+  w.part = off;
   off += align256(part);
+  w.part_db = off;
+  off += align256(ad_part_bytes(w.pdb, N));
   w.total = std::max<size_t>(off, 256);
   return w;
 }
@@ -220,29 +260,85 @@ qlora_status run_gemm(GemmArgs g, const Plan& p, hipStream_t st) {
   return launched();
 }
 
-qlora_status run_reduce(const float* part, int64_t part_stride, int nsplit, int64_t rows,
-                        int64_t cols, int64_t rows_pad, int64_t cols_pad, int64_t ldp, float scale,
-                        ReduceOut o0, ReduceOut o1, hipStream_t st) {
-  const int64_t total = rows_pad * cols_pad;
-  if (total == 0) return QLORA_OK;
-  // four columns per thread when every row of partials and outputs stays
-  // 16-byte (partials) / 8-byte (bf16 rows) aligned
+// The float4 reduction needs every row of partials and outputs 16-byte
+// (partials) / 8-byte (bf16 rows) aligned.
+bool reduce4_ok(const ReduceJob& j) {
   auto al = [](const ReduceOut& o) {
-    return o.transposed || ((o.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(o.bf16) & 7u) == 0 &&
-                            (reinterpret_cast<uintptr_t>(o.f32) & 15u) == 0);
+    return (o.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(o.bf16) & 7u) == 0 &&
+           (reinterpret_cast<uintptr_t>(o.f32) & 15u) == 0;
   };
-  if (cols_pad % 4 == 0 && ldp % 4 == 0 && part_stride % 4 == 0 &&
-      (reinterpret_cast<uintptr_t>(part) & 15u) == 0 && al(o0) && al(o1)) {
-    hipLaunchKernelGGL(reduce_partials4_kernel, dim3(grid_for(total / 4)), dim3(256), 0, st, part,
-                       part_stride, nsplit, rows, cols, rows_pad, cols_pad, ldp, scale, o0, o1);
+  return j.cols_pad % 4 == 0 && j.ldp % 4 == 0 && j.part_stride % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(j.part) & 15u) == 0 && al(j.o0) && al(j.o1);
+}
+
+qlora_status run_reduce_job(const ReduceJob& j, hipStream_t st) {
+  const int64_t total = j.rows_pad * j.cols_pad;
+  if (total == 0) return QLORA_OK;
+  if (reduce4_ok(j)) {
+    const ReduceJob none{};
+    hipLaunchKernelGGL(reduce_partials4_kernel, dim3(grid_for(total / 4), 1), dim3(256), 0, st, j,
+                       none);
     return launched();
   }
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid_for(total)), dim3(256), 0, st, part,
-                     part_stride, nsplit, rows, cols, rows_pad, cols_pad, ldp, scale, o0, o1);
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid_for(total)), dim3(256), 0, st, j.part,
+                     j.part_stride, j.nsplit, j.rows, j.cols, j.rows_pad, j.cols_pad, j.ldp,
+                     j.scale, j.o0, j.o1);
   return launched();
 }
 
-constexpr ReduceOut kNoOut{nullptr, nullptr, 0, 0};
+qlora_status run_reduce(const float* part, int64_t part_stride, int nsplit, int64_t rows,
+                        int64_t cols, int64_t rows_pad, int64_t cols_pad, int64_t ldp, float scale,
+                        ReduceOut o0, ReduceOut o1, hipStream_t st) {
+  return run_reduce_job(ReduceJob{part, part_stride, nsplit, rows, cols, rows_pad, cols_pad, ldp,
+                                  scale, o0, o1},
+                        st);
+}
+
+// Two reductions in one launch (separately when either needs the scalar kernel).
+qlora_status run_reduce2(const ReduceJob& a, const ReduceJob& b, hipStream_t st) {
+  if (!reduce4_ok(a) || !reduce4_ok(b) || a.rows_pad * a.cols_pad == 0 ||
+      b.rows_pad * b.cols_pad == 0) {
+    const qlora_status s = run_reduce_job(a, st);
+    return s != QLORA_OK ? s : run_reduce_job(b, st);
+  }
+  const int64_t t = std::max(a.rows_pad * a.cols_pad, b.rows_pad * b.cols_pad) / 4;
+  hipLaunchKernelGGL(reduce_partials4_kernel, dim3(grid_for(t), 2), dim3(256), 0, st, a, b);
+  return launched();
+}
+
+constexpr ReduceOut kNoOut{nullptr, nullptr, 0};
+
+AdapterArgs ad_args(const AdPlan& p, const uint16_t* S, int64_t lds, const uint16_t* F, int64_t ldf,
+                    int32_t r, int64_t nout, int64_t red, float* part, bool tr = false) {
+  AdapterArgs a{};
+  a.s = S; a.lds = lds; a.f = F; a.ldf = ldf; a.r = r; a.nout = nout; a.red = red;
+  a.part = part; a.ldp = p.ldp;
+  a.part_stride = (tr ? (int64_t)32 * p.nb * p.ncg : nout) * p.ldp;
+  a.tiles = p.tiles; a.kt_per_split = p.ktps; a.nkt = p.nkt;
+  return a;
+}
+
+template <bool FN>
+qlora_status run_rows(const AdapterArgs& a, const AdPlan& p, hipStream_t st) {
+  const dim3 grid((unsigned)(p.tiles * p.nsplit), (unsigned)p.ncg);
+  switch (p.nb) {
+    case 1: hipLaunchKernelGGL((adapter_rows_kernel<1, FN>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((adapter_rows_kernel<2, FN>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((adapter_rows_kernel<4, FN>), grid, dim3(256), 0, st, a); break;
+  }
+  return launched();
+}
+
+template <bool TR>
+qlora_status run_cols(const AdapterArgs& a, const AdPlan& p, hipStream_t st) {
+  const dim3 grid((unsigned)(p.tiles * p.nsplit), (unsigned)p.ncg);
+  switch (p.nb) {
+    case 1: hipLaunchKernelGGL((adapter_cols_kernel<1, TR>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((adapter_cols_kernel<2, TR>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((adapter_cols_kernel<4, TR>), grid, dim3(256), 0, st, a); break;
+  }
+  return launched();
+}
 
 // s·x is exact in bf16 for every bf16 x when s is a power of two (no
 // overflow / underflow at the magnitudes of the adapter factors).
@@ -284,20 +380,16 @@ qlora_status lora_down_impl(const uint16_t* X, int64_t M, int64_t K, const uint1
                        st, X, K, A, (int)r, U);
     return launched();
   }
-  GemmArgs g{};
-  g.a = X; g.lda = K; g.rows = M; g.cols = r; g.red = K;
-  g.b = A; g.ldb = K;
-  g.out_f32 = reinterpret_cast<float*>(ws + L.u_part);
-  g.ldo = (int64_t)L.pu.tiles_n * SK_NT;
-  g.part_stride = M * g.ldo;
-  qlora_status s = run_gemm<SK_MT, SK_NT, 4, 1, B_BF16_CR, false, O_F32>(g, L.pu, st);
+  float* part = reinterpret_cast<float*>(ws + L.u_part);
+  const AdapterArgs a = ad_args(L.pu, X, K, A, K, r, M, K, part);
+  qlora_status s = run_rows<false>(a, L.pu, st);
   if (s != QLORA_OK) return s;
-  s = run_reduce(g.out_f32, g.part_stride, L.pu.nsplit, M, r, M, r, g.ldo, 1.0f,
-                 ReduceOut{U, nullptr, r, 0}, kNoOut, st);
+  s = run_reduce(part, a.part_stride, L.pu.nsplit, M, r, M, r, a.ldp, 1.0f,
+                 ReduceOut{U, nullptr, r}, kNoOut, st);
   if (s != QLORA_OK || !Upad) return s;
   // zero-padded copy with a pitch that is a multiple of 8, for the prologue's 16-byte loads
-  return run_reduce(g.out_f32, g.part_stride, L.pu.nsplit, M, r, M, rp, g.ldo, 1.0f,
-                    ReduceOut{Upad, nullptr, rp, 0}, kNoOut, st);
+  return run_reduce(part, a.part_stride, L.pu.nsplit, M, r, M, rp, a.ldp, 1.0f,
+                    ReduceOut{Upad, nullptr, rp}, kNoOut, st);
 }
 
 template <int CPW, int MG, int G>
@@ -349,8 +441,8 @@ qlora_status gemv_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, 
   }
   qlora_status e = launched();
   if (e != QLORA_OK || p.ksplit == 1) return e;
-  return run_reduce(a.part, M * N, p.ksplit, M, N, M, N, N, 1.0f, ReduceOut{Y, nullptr, N, 0},
-                    ReduceOut{nullptr, nullptr, 0, 0}, st);
+  return run_reduce(a.part, M * N, p.ksplit, M, N, M, N, N, 1.0f, ReduceOut{Y, nullptr, N},
+                    ReduceOut{nullptr, nullptr, 0}, st);
 }
 
 qlora_status matmul_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M,
@@ -376,7 +468,7 @@ qlora_status matmul_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64
   qlora_status e = run_gemm<SM_MT, SM_NT, 1, 4, B_NF4_COLS, true, O_F32>(g, L.py, st);
   if (e != QLORA_OK) return e;
   return run_reduce(g.out_f32, g.part_stride, L.py.nsplit, M, N, M, N, N, 1.0f,
-                    ReduceOut{Y, nullptr, N, 0}, kNoOut, st);
+                    ReduceOut{Y, nullptr, N}, kNoOut, st);
 }
 
 float scale_of(float alpha, int32_t r) { return alpha / (float)r; }
@@ -459,18 +551,14 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
   qlora_status s = QLORA_OK;
 
   if (M == 0) {  // no tokens: the adapter gradients are zero
-    s = run_reduce(nullptr, 0, 0, 0, 0, (int64_t)r, K, 0, 0.0f, ReduceOut{nullptr, dA, K, 0},
+    s = run_reduce(nullptr, 0, 0, 0, 0, (int64_t)r, K, 0, 0.0f, ReduceOut{nullptr, dA, K},
                    kNoOut, st);
     if (s != QLORA_OK) return s;
     return run_reduce(nullptr, 0, 0, 0, 0, N, (int64_t)r, 0, 0.0f,
-                      ReduceOut{nullptr, dB, (int64_t)r, 0}, kNoOut, st);
+                      ReduceOut{nullptr, dB, (int64_t)r}, kNoOut, st);
   }
 
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(ws + L.bt);  // [r][Np]
   uint16_t* V = reinterpret_cast<uint16_t*>(ws + L.v);    // [M][rp]
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(ws + L.vt);  // [r][Mp]
-  uint16_t* Ut = reinterpret_cast<uint16_t*>(ws + L.ut);  // [r][Mp]
-  uint16_t* At = reinterpret_cast<uint16_t*>(ws + L.at);  // [K][rp]
   float* part = reinterpret_cast<float*>(ws + L.part);
 
   // dY with a 16-byte aligned row pitch (only when n_out % 8 != 0)
@@ -483,44 +571,41 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
     if ((s = launched()) != QLORA_OK) return s;
     dYa = dYp;
   }
-
-  // adapter factors in the layouts the GEMMs read
-  {
-    const TransposeJob jb{B, (int64_t)r, N, (int64_t)r, L.Np, (int64_t)r, Bt, L.Np};
-    const TransposeJob ju{U, (int64_t)r, M, (int64_t)r, L.Mp, (int64_t)r, Ut, L.Mp};
-    const TransposeJob ja{A, K, (int64_t)r, K, L.rp, K, At, L.rp};
-    const int64_t tiles = std::max({ceil_div(L.Np, 64) * ceil_div(r, 64), ceil_div(L.Mp, 64) * ceil_div(r, 64),
-                                    ceil_div(L.rp, 64) * ceil_div(K, 64)});
-    hipLaunchKernelGGL(transpose_pad3_kernel, dim3((unsigned)std::min<int64_t>(tiles, 1024), 3),
-                       dim3(256), 0, st, jb, ju, ja);
+  // B and U with 16-byte aligned rows (only when r % 8 != 0)
+  const uint16_t *Ba = B, *Ua = U;
+  if (L.rp != r) {
+    uint16_t* Bp = reinterpret_cast<uint16_t*>(ws + L.bp);
+    uint16_t* Up = reinterpret_cast<uint16_t*>(ws + L.up);
+    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(N * L.rp)), dim3(256), 0, st, B,
+                       (int64_t)r, N, (int64_t)r, L.rp, Bp, L.rp);
+    if ((s = launched()) != QLORA_OK) return s;
+    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(M * L.rp)), dim3(256), 0, st, U,
+                       (int64_t)r, M, (int64_t)r, L.rp, Up, L.rp);
+    if ((s = launched()) != QLORA_OK) return s;
+    Ba = Bp;
+    Ua = Up;
   }
-  if ((s = launched()) != QLORA_OK) return s;
 
-  // V = dY·B  -> V [M][rp] (zero-padded) and Vᵀ [r][Mp] (zero-padded), bf16
-  // (over the padded pitch: both operands hold zeros past n_out)
+  // One launch streams dY for both V = dY·B (over the padded pitch: dY holds
+  // zeros past n_out and B's rows end there) and dB = s·dYᵀ·U; one more sums
+  // both products' splits: V [M][rp] bf16 (zero-padded) and dB [N][r].
   {
-    GemmArgs g{};
-    g.a = dYa; g.lda = ldy; g.rows = M; g.cols = r; g.red = L.Np;
-    g.b = Bt; g.ldb = L.Np;
-    g.out_f32 = part;
-    g.ldo = (int64_t)L.pv.tiles_n * SK_NT;
-    g.part_stride = M * g.ldo;
-    if ((s = run_gemm<SK_MT, SK_NT, 4, 1, B_BF16_CR, false, O_F32>(g, L.pv, st)) != QLORA_OK)
-      return s;
-    if (L.rp == r && L.Mp == M) {  // no padding: V and Vᵀ from one pass over the partials
-      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, r, g.ldo, 1.0f,
-                          ReduceOut{V, nullptr, L.rp, 0}, ReduceOut{Vt, nullptr, L.Mp, 1}, st)) !=
-          QLORA_OK)
-        return s;
-    } else {
-      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, M, L.rp, g.ldo, 1.0f,
-                          ReduceOut{V, nullptr, L.rp, 0}, kNoOut, st)) != QLORA_OK)
-        return s;
-      // Vᵀ from the same partials: rows_pad = Mp pads the token axis with zeros
-      if ((s = run_reduce(part, g.part_stride, L.pv.nsplit, M, r, L.Mp, r, g.ldo, 1.0f,
-                          ReduceOut{Vt, nullptr, L.Mp, 1}, kNoOut, st)) != QLORA_OK)
-        return s;
+    float* part_db = reinterpret_cast<float*>(ws + L.part_db);
+    const AdapterArgs av = ad_args(L.pv, dYa, ldy, Ba, L.rp, r, M, L.Np, part);
+    const AdapterArgs ab = ad_args(L.pdb, dYa, ldy, Ua, L.rp, r, N, M, part_db);
+    const int nv = L.pv.tiles * L.pv.nsplit;
+    const dim3 grid((unsigned)(nv + L.pdb.tiles * L.pdb.nsplit), (unsigned)L.pv.ncg);
+    switch (L.pv.nb) {
+      case 1: hipLaunchKernelGGL(adapter_dy_kernel<1>, grid, dim3(256), 0, st, av, ab, nv); break;
+      case 2: hipLaunchKernelGGL(adapter_dy_kernel<2>, grid, dim3(256), 0, st, av, ab, nv); break;
+      default: hipLaunchKernelGGL(adapter_dy_kernel<4>, grid, dim3(256), 0, st, av, ab, nv); break;
     }
+    if ((s = launched()) != QLORA_OK) return s;
+    const ReduceJob jv{part, av.part_stride, L.pv.nsplit, M, r, M, L.rp, av.ldp, 1.0f,
+                       ReduceOut{V, nullptr, L.rp}, kNoOut};
+    const ReduceJob jb{part_db, ab.part_stride, L.pdb.nsplit, N, r, N, r, ab.ldp, sc,
+                       ReduceOut{nullptr, dB, (int64_t)r}, kNoOut};
+    if ((s = run_reduce2(jv, jb, st)) != QLORA_OK) return s;
   }
 
   // with dropout: T = s·mask ⊙ (V·A), [M][K] fp32 (mask and scale in the epilogue)
@@ -542,7 +627,7 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
     GemmArgs g{};
     g.a = dYa; g.lda = ldy; g.rows = M; g.cols = K; g.red = N;
     g.packed = w->packed; g.qabsmax = w->qabsmax; g.c2 = w->c2; g.w_kin = K;
-    g.pl = V; g.ldpl = L.rp; g.pr = At; g.ldpr = L.rp; g.rl = r; g.s = sc;
+    g.pl = V; g.ldpl = L.rp; g.pr = A; g.ldpr = K; g.pr_rc = 1; g.rl = r; g.s = sc;
     g.s_split = needs_split(sc);
     if (drop) {
       g.c_init = T; g.ldc = K; g.rl = 0;
@@ -557,34 +642,17 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
       if ((s = run_gemm<SM_MT, SM_NT, 1, 4, B_NF4_RED, true, O_F32>(g, L.pdx, st)) != QLORA_OK)
         return s;
       if ((s = run_reduce(part, g.part_stride, L.pdx.nsplit, M, K, M, K, K, 1.0f,
-                          ReduceOut{dX, nullptr, K, 0}, kNoOut, st)) != QLORA_OK)
+                          ReduceOut{dX, nullptr, K}, kNoOut, st)) != QLORA_OK)
         return s;
     }
   }
 
-  // dA = s·Vᵀ·X   [r][K]
+  // dA = s·Vᵀ·X   [r][K] (partial sums stored rank-major)
   {
-    GemmArgs g{};
-    g.a = Vt; g.lda = L.Mp; g.rows = r; g.cols = K; g.red = M;
-    g.b = X; g.ldb = K;
-    g.out_f32 = part; g.ldo = K; g.part_stride = (int64_t)r * K;
-    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pda, st)) != QLORA_OK)
-      return s;
-    if ((s = run_reduce(part, g.part_stride, L.pda.nsplit, r, K, r, K, K, sc,
-                        ReduceOut{nullptr, dA, K, 0}, kNoOut, st)) != QLORA_OK)
-      return s;
-  }
-
-  // dB = s·dYᵀ·U  computed as (s·Uᵀ·dY)ᵀ: rows j, cols n, written transposed into [N][r]
-  {
-    GemmArgs g{};
-    g.a = Ut; g.lda = L.Mp; g.rows = r; g.cols = N; g.red = M;
-    g.b = dYa; g.ldb = ldy;
-    g.out_f32 = part; g.ldo = N; g.part_stride = (int64_t)r * N;
-    if ((s = run_gemm<TR_MT, TR_NT, 2, 2, B_BF16_RC, false, O_F32>(g, L.pdb, st)) != QLORA_OK)
-      return s;
-    if ((s = run_reduce(part, g.part_stride, L.pdb.nsplit, r, N, r, N, N, sc,
-                        ReduceOut{nullptr, dB, (int64_t)r, 1}, kNoOut, st)) != QLORA_OK)
+    const AdapterArgs a = ad_args(L.pda, X, K, V, L.rp, r, K, M, part, true);
+    if ((s = run_cols<true>(a, L.pda, st)) != QLORA_OK) return s;
+    if ((s = run_reduce(part, a.part_stride, L.pda.nsplit, r, K, r, K, a.ldp, sc,
+                        ReduceOut{nullptr, dA, K}, kNoOut, st)) != QLORA_OK)
       return s;
   }
   return QLORA_OK;
@@ -1010,8 +1078,7 @@ qlora_status qlora_lora_down(const qlora_bf16* X, int64_t M, int64_t k_in, const
   const FwdWs L = fwd_ws(M, 8, k_in, r);
   if (!use_gemv(M)) {
     QCHECK(workspace != nullptr && aligned16(workspace), QLORA_ERR_WORKSPACE);
-    QCHECK(ws_bytes >= L.u_part + align256((size_t)L.pu.nsplit * M * L.pu.tiles_n * SK_NT * 4),
-           QLORA_ERR_WORKSPACE);
+    QCHECK(ws_bytes >= L.u_part + align256(ad_part_bytes(L.pu, M)), QLORA_ERR_WORKSPACE);
   }
   qlora_status s = check_device();
   if (s != QLORA_OK) return s;

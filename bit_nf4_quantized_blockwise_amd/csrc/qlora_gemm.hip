@@ -9,9 +9,10 @@
 //                 reduction along k_in (forward: Y = X·Ŵᵀ)
 //   B_NF4_RED   — the frozen weight traversed transposed: output col = W column
 //                 (k_in), reduction along W rows (input gradient: dX = dY·Ŵ)
-//   B_BF16_CR   — bf16 [cols][red] row-major (A or Bᵀ of the adapter)
-//   B_BF16_RC   — bf16 [red][cols] row-major (X or dY when the reduction runs
-//                 over tokens: the adapter gradients)
+//   B_BF16_RC   — bf16 [red][cols] row-major (A, for the dropout backward's
+//                 masked rank-r term T = s·mask ⊙ (V·A))
+// The rank-r products of the layer itself (U, V, dA, dB) run on their own
+// streaming kernels (qlora_adapter.hip).
 // Dequantisation happens in the loader, right before the tile is written to
 // LDS, in the order of the Qiita explainer's DQ formula:
 // ŵ = RNE_bf16(RN32(c_idx · RN32(c2 · q))) — bit-identical to the standalone
@@ -65,7 +66,7 @@ struct Buf {
   }
 };
 
-// ---- A-style loader: [rows][ld] bf16, reduction contiguous ---------------------
+// ---- [rows][ld] bf16 with the reduction contiguous (the prologue's R = B) --------
 // Thread t moves 16-byte chunks id = t + 256 i: row id / 8, chunk id % 8.
 template <int T_ROWS>
 struct RowTile {
@@ -91,16 +92,6 @@ struct RowTile {
   __device__ inline void store(char* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      const int id = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(lds + swz(id >> 3, id & 7)) = r[i];
-    }
-  }
-  // Quarter q of store(): chunks i with i % 4 == q (all of them when PER_T < 4
-  // and q == 0).
-  __device__ inline void store_part(char* lds, int tid, int q) const {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      if (i % 4 != q) continue;
       const int id = tid + 256 * i;
       *reinterpret_cast<u32x4*>(lds + swz(id >> 3, id & 7)) = r[i];
     }
@@ -677,13 +668,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       load_acc<FM, FN>(mma.acc, g, wrow0, col0 + wn * WTN, lane);
     } else if (blockIdx.y == 0 && g.rl > 0) {
       ARegs<FM> la;
-      RowTile<NT> rt;
       la.init(g.pl, g.ldpl, g.rows, wrow0, lane);
-      rt.init(g.pr, g.ldpr, g.cols, col0, tid);
+      RowTile<NT> rt;
+      if (!g.pr_rc) rt.init(g.pr, g.ldpr, g.cols, col0, tid);
       for (int64_t j0 = 0; j0 < g.rl; j0 += KT) {
         la.load(j0, g.rl);
-        rt.load(j0, g.rl, tid);
-        rt.store(Bs(0), tid);
+        if (g.pr_rc) {  // R stored by rank: 8 x 8 transposes on the way into LDS
+          RcTile<NT> rc;
+          rc.load(g.pr, g.ldpr, g.rl, g.cols, j0, col0, tid);
+          rc.store(Bs(0), tid);
+        } else {
+          rt.load(j0, g.rl, tid);
+          rt.store(Bs(0), tid);
+        }
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -705,21 +702,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 
   constexpr bool kRows = BMODE == B_NF4_RED && AMODE == A_DMA;  // row-major B, transposed reads
+  static_assert(BMODE == B_NF4_COLS || BMODE == B_NF4_RED || BMODE == B_BF16_RC, "B mode");
   using BTile = typename std::conditional<
       BMODE == B_NF4_COLS, Nf4ColsTile<NT>,
       typename std::conditional<BMODE == B_NF4_RED,
                                 typename std::conditional<kRows, Nf4RowsTile, Nf4RedTile<NT>>::type,
-                                typename std::conditional<BMODE == B_BF16_RC, RcTile<NT>,
-                                                          RowTile<NT>>::type>::type>::type;
+                                RcTile<NT>>::type>::type;
   ARegs<(AMODE == A_DIRECT) ? FM : 1> a;
   if constexpr (AMODE == A_DIRECT) a.init(g.a, g.lda, g.rows, wrow0, lane);
   BTile b0, b1;
   if constexpr (BMODE == B_NF4_COLS || BMODE == B_NF4_RED) {
     b0.init(g, col0, tid);
     b1.init(g, col0, tid);
-  } else if constexpr (BMODE == B_BF16_CR) {
-    b0.init(g.b, g.ldb, g.cols, col0, tid);
-    b1.init(g.b, g.ldb, g.cols, col0, tid);
   }
   const int64_t kend = min(g.red, (int64_t)kt_end * KT);  // this split's reduction bound
 
@@ -731,10 +725,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       bt.load(g, k0, kend);
     } else if constexpr (BMODE == B_NF4_RED) {
       bt.load(g, k0, kend, tid);
-    } else if constexpr (BMODE == B_BF16_RC) {
-      bt.load(g.b, g.ldb, kend, g.cols, k0, col0, tid);
     } else {
-      bt.load(k0, kend, tid);
+      bt.load(g.b, g.ldb, kend, g.cols, k0, col0, tid);
     }
   };
   // Quarter q of a B tile into stage st; the NF4 tiles fold their scales
@@ -965,7 +957,6 @@ QLORA_GEMM(256, 256, 2, 2, B_NF4_COLS, true, O_BF16, A_DMA)     // forward, many
 QLORA_GEMM(256, 256, 2, 2, B_NF4_RED, true, O_BF16, A_DMA)     // input gradient, many tokens
 QLORA_GEMM(64, 256, 1, 4, B_NF4_COLS, true, O_F32, A_DIRECT)    // forward, 17..127 tokens (split-K)
 QLORA_GEMM(64, 256, 1, 4, B_NF4_RED, true, O_F32, A_DIRECT)     // input gradient, 17..127 tokens
-QLORA_GEMM(128, 64, 4, 1, B_BF16_CR, false, O_F32, A_DIRECT)    // U = X·Aᵀ, V = dY·B (split-K)
-QLORA_GEMM(64, 256, 2, 2, B_BF16_RC, false, O_F32, A_DIRECT)    // dA, dB: reduction over tokens
+QLORA_GEMM(64, 256, 2, 2, B_BF16_RC, false, O_F32, A_DIRECT)    // dropout: T = s·mask ⊙ (V·A)
 
 }  // namespace qlora

@@ -7,7 +7,7 @@
 
 namespace qlora {
 
-enum BMode { B_NF4_COLS = 0, B_NF4_RED = 1, B_BF16_CR = 2, B_BF16_RC = 3 };
+enum BMode { B_NF4_COLS = 0, B_NF4_RED = 1, B_BF16_RC = 3 };
 enum OMode { O_BF16 = 0, O_F32 = 1 };
 // A operand: staged in LDS by direct-to-LDS loads, or loaded into MFMA registers
 enum AMode { A_DMA = 0, A_DIRECT = 1 };
@@ -26,6 +26,7 @@ struct GemmArgs {
   int64_t ldpl;
   const uint16_t* pr;
   int64_t ldpr;
+  int32_t pr_rc;       // 1: pr is stored [rl][cols] (row-major by rank) instead
   int32_t rl;
   float s;
   int32_t s_split;     // 1: stage s·L as two bf16 parts (s·L not exact in bf16)
@@ -45,15 +46,6 @@ struct ReduceOut {
   uint16_t* bf16;  // bf16 output or nullptr
   float* f32;      // float32 output or nullptr
   int64_t ld;
-  int32_t transposed;  // write out[col][row] instead of out[row][col]
-};
-
-// out[c][r] = in[r][c] for r < R, c < C; zero for r in [R, Rp) or c in [C, Cp).
-struct TransposeJob {
-  const uint16_t* in;
-  int64_t ldi, R, C, Rp, Cp;
-  uint16_t* out;  // nullptr: no job
-  int64_t ldo;
 };
 
 struct GemvArgs {
@@ -74,6 +66,29 @@ struct GemvArgs {
 
 template <int MT, int NT, int WM, int WN, int BMODE, bool PROLOGUE, int OMODE, int AMODE>
 __global__ void gemm_kernel(GemmArgs g);
+
+// Rank-r products (qlora_adapter.hip): fp32 partial sums of one split each.
+//   rows:  part[s][m][j] = Σ_k S[m][k]·F(k, j), F = A [r][ldf] or B [red][ldf]
+//   cols:  part[s][l][j] (or [j][l]) = Σ_m S[m][l]·Q[m][j], Q [red][ldf]
+struct AdapterArgs {
+  const uint16_t* s;  // the streamed operand (X or dY), row-major, pitch lds
+  int64_t lds;
+  const uint16_t* f;  // the factor (A, B, U or V), row-major, pitch ldf
+  int64_t ldf;
+  int32_t r;          // rows of F when F = A
+  int64_t nout;       // rows: tokens; cols: columns of S
+  int64_t red;        // rows: columns of S; cols: tokens
+  float* part;
+  int64_t ldp, part_stride;
+  int32_t tiles, kt_per_split, nkt;
+};
+constexpr int kAdapterTile = 128;  // stream indices per workgroup
+template <int NB, bool FN>
+__global__ void adapter_rows_kernel(AdapterArgs g);
+template <int NB, bool TR>
+__global__ void adapter_cols_kernel(AdapterArgs g);
+template <int NB>
+__global__ void adapter_dy_kernel(AdapterArgs gv, AdapterArgs gb, int nv);
 
 constexpr int kGemvWaves = 8;   // waves per few-token GEMV workgroup (they split the reduction)
 template <int CPW, int MG, int G, bool QV>
@@ -140,13 +155,17 @@ __global__ void reduce_partials_kernel(const float* part, int64_t part_stride, i
                                        int64_t rows, int64_t cols, int64_t rows_pad,
                                        int64_t cols_pad, int64_t ldp, float scale, ReduceOut o0,
                                        ReduceOut o1);
-__global__ void reduce_partials4_kernel(const float* part, int64_t part_stride, int32_t nsplit,
-                                       int64_t rows, int64_t cols, int64_t rows_pad,
-                                       int64_t cols_pad, int64_t ldp, float scale, ReduceOut o0,
-                                       ReduceOut o1);
-__global__ void transpose_pad3_kernel(TransposeJob j0, TransposeJob j1, TransposeJob j2);
-__global__ void transpose_pad_kernel(const uint16_t* in, int64_t ldi, int64_t R, int64_t C,
-                                     int64_t Rp, int64_t Cp, uint16_t* out, int64_t ldo);
+// One reduction: out(row, col) = scale · Σ_z part[z][row][col] (see reduce_partials_kernel).
+struct ReduceJob {
+  const float* part;
+  int64_t part_stride;
+  int32_t nsplit;
+  int64_t rows, cols, rows_pad, cols_pad, ldp;
+  float scale;
+  ReduceOut o0, o1;
+};
+// Four columns per thread; blockIdx.y picks the job (one launch for two).
+__global__ void reduce_partials4_kernel(ReduceJob j0, ReduceJob j1);
 __global__ void pad_cols_kernel(const uint16_t* in, int64_t ldi, int64_t R, int64_t C, int64_t Cp,
                                 uint16_t* out, int64_t ldo);
 

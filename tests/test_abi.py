@@ -58,6 +58,10 @@ def test_workspace_size(L):
     assert q.workspace_size(0, 16, 64, 64, 0) == 0
     assert q.workspace_size(0, 16, 64, 64, 257) == 0
     assert q.workspace_size(0, 0, 64, 64, 8) >= 256
+    # zero tokens plan every backward product without dividing by zero
+    for op in (1, 2):
+        assert q.workspace_size(op, 0, 16, 64, 4) >= 256
+        assert q.workspace_size(op, 0, 75, 128, 3) >= 256
 
 
 def test_quantize_argument_errors(L):
