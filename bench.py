@@ -4,8 +4,10 @@ Step = one training step (forward + backward) of every projection of one
 LLaMA-65B-shaped decoder layer (q, k, v, o 8192 -> 8192; gate, up 8192 ->
 22016; down 22016 -> 8192), NF4 + double-quantised weights with a LoRA
 adapter r = 64, alpha = 16 on each, 2048 tokens: per projection U = X·Aᵀ
-and the dequant-GEMM with the rank-r prologue, then V = dY·B, the
-transposed dequant-GEMM for dX, dA and dB.  6,754.24 GFLOP per step on
+(rank-r streaming kernel and its split reduction) and the dequant-GEMM with
+the rank-r prologue, then V = dY·B and dB = s·dYᵀ·U (one streaming launch and
+one reduction), the transposed dequant-GEMM for dX, and dA = s·Vᵀ·X
+(streaming kernel and reduction).  6,754.24 GFLOP per step on
 resident seeded synthetic inputs; `value` = algorithmic TFLOP/s of the step.
 The roofline object is the forward dequant-GEMM over the layer's seven
 launches, timed on the stream it runs on; `roofline_gemv` is the few-token
@@ -181,11 +183,11 @@ def summarize_stats(stats_csv, bench_log, out_path):
 
 FWD_GEMM = "gemm_kernel<256, 256, 2, 2, 0, true, 0, 0>"
 DX_GEMM = "gemm_kernel<256, 256, 2, 2, 1, true, 0, 0>"
-GRAD_GEMM = "gemm_kernel<64, 256, 2, 2, 3, false, 1, 1>"  # dA and dB
 
 
 def summarize_counters(out_path, *csvs, kernel=FWD_GEMM, what="forward dequant-GEMM",
-                       pass_flag="--pmc-pass", summary_flag="--summarize-counters"):
+                       pass_flag="--pmc-pass", summary_flag="--summarize-counters",
+                       workload="the LLaMA-65B layer's 7 projections: 2048 tokens, r = 64"):
     """Per-dispatch averages of the SQ counters of one GEMM kernel from
     rocprofv3 --pmc runs of a counter pass, with the ratios read off them."""
     import csv
@@ -200,8 +202,8 @@ def summarize_counters(out_path, *csvs, kernel=FWD_GEMM, what="forward dequant-G
             d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
     avg = {k: sum(v.values()) / len(v) for k, v in vals.items()}
     with open(out_path, "w") as fh:
-        fh.write(f"# SQ counters of the {what} (LLaMA-7B MLP: 4096 tokens, 4096 -> "
-                 f"11008, r = 64),\n# per dispatch, averaged over the dispatches of {pass_flag}.  "
+        fh.write(f"# SQ counters of the {what} ({workload}),\n"
+                 f"# per dispatch, averaged over the dispatches of {pass_flag}.  "
                  "Commands (from /tmp, TMPDIR=/tmp),\n# one rocprofv3 run per counter set:\n")
         fh.write("#   rocprofv3 --pmc <set> --output-format csv -d <dir_i> -o c -- python3 "
                  f"<repo>/bench.py {pass_flag}\n")
@@ -273,7 +275,8 @@ def pmc_pass():
     print("pmc pass done", flush=True)
 
 
-HBM_SOURCES = ["qlora_quant.hip", "qlora_gemv.hip", "qlora_common.h", "qlora_kernels.h"]
+HBM_SOURCES = ["qlora_quant.hip", "qlora_gemv.hip", "qlora_adapter.hip", "qlora_aux.hip",
+               "qlora_common.h", "qlora_kernels.h"]
 
 
 def hbm_source_hash():
@@ -289,18 +292,23 @@ def pmc_pass_hbm():
     """Short run for the byte counters of the HBM-bound kernels: the fused
     quantiser (two launches) and the dequantiser on the 11008 x 4096 weight,
     the few-token forward (U launch + GEMV) at one token on the 8192 -> 28672
-    weight, three times each, and the calibration copy."""
+    weight, the rank-r streaming kernels of the LLaMA-65B q projection (2048
+    tokens, 8192 -> 8192, r = 64: U, then V and dB, then dA), three times
+    each, and the calibration copy."""
     import torch
 
     import bit_nf4_quantized_blockwise_amd as q
     import workloads as wl
 
     dev = torch.device("cuda:0")
-    # the few-token weight is quantised first: the summary takes the last three
-    # dispatches of each kernel
+    # the few-token and q-projection weights are quantised first: the summary
+    # takes the last three dispatches of each kernel
     g = wl.GEMV_70B
     gin = g.inputs(M=1)
     wg = q.quantize_weight(torch.from_numpy(gin["W"]).to(dev))
+    p = wl.LLAMA65B_LAYER[0]
+    pin = p.inputs()
+    wp = q.quantize_weight(torch.from_numpy(pin["W"]).to(dev))
     W = torch.from_numpy(wl.LLAMA7B_MLP.inputs(with_dy=False)["W"]).to(dev)
     for _ in range(3):
         o = q.quantize_nf4_dq(W, want_absmax=True)
@@ -312,6 +320,12 @@ def pmc_pass_hbm():
     X, A, B = (gin[k].to(dev) for k in ("X", "A", "B"))
     for _ in range(3):
         q.linear_fwd(wg, X, A, B, g.alpha)
+    del wg, X, A, B
+    X, A, B, dY = (pin[k].to(dev) for k in ("X", "A", "B", "dY"))
+    for _ in range(3):
+        U = q.lora_down(X, A)
+        q.linear_bwd(wp, X, dY, A, B, U, p.alpha)
+    del wp, X, A, B, dY, U
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -331,7 +345,11 @@ def summarize_hbm(out_path, fetch_csv, write_csv):
             "qlora::double_quant_kernel(": "DQ, second level",
             "qlora::dequantize_nf4_kernel(": "dequantise",
             "qlora::lora_down_small_kernel(": "U = X·Aᵀ, 1 token",
-            "qlora::nf4_gemv_kernel<": "few-token GEMV, 1 token", "copyBuffer": "copy"}
+            "qlora::nf4_gemv_kernel<": "few-token GEMV, 1 token",
+            "qlora::adapter_rows_kernel<2, false>(": "U = X·Aᵀ splits (q projection)",
+            "qlora::adapter_dy_kernel<2>(": "V = dY·B and dB = s·dYᵀ·U splits, one launch",
+            "qlora::adapter_cols_kernel<2, true>(": "dA = s·Vᵀ·X splits",
+            "copyBuffer": "copy"}
 
     def per_kernel(path, counter):
         vals = {}
@@ -364,11 +382,20 @@ def summarize_hbm(out_path, fetch_csv, write_csv):
         "qlora::lora_down_small_kernel(": (2 * 8192 + 2 * 16 * 8192, 2 * 16),
         "qlora::nf4_gemv_kernel<": (n70 // 2 + n70 // 64 + 4 * ng70 + 2 * 8192 + 2 * 16 * 28672 + 2 * 16,
                             2 * 28672),
+        # q projection, M = 2048, K = N = 8192, r = 64: each product's operands
+        # read once, its result written once (bf16 U and V, fp32 dA and dB)
+        "qlora::adapter_rows_kernel<2, false>(": (2 * 2048 * 8192 + 2 * 64 * 8192, 2 * 2048 * 64),
+        "qlora::adapter_dy_kernel<2>(": (2 * (2 * 2048 * 8192) + 2 * 8192 * 64 + 2 * 2048 * 64,
+                                        2 * 2048 * 64 + 4 * 8192 * 64),
+        "qlora::adapter_cols_kernel<2, true>(": (2 * 2048 * 8192 + 2 * 2048 * 64, 4 * 64 * 8192),
     }
     with open(out_path, "w") as fh:
         fh.write("# HBM traffic of the HBM-bound kernels: the fused quantiser (two launches) and the\n")
         fh.write("# dequantiser on the 11008 x 4096 weight, the few-token forward at 1 token on the\n")
-        fh.write("# 8192 -> 28672 weight (r = 16).  rocprofv3 FETCH_SIZE and WRITE_SIZE per launch\n")
+        fh.write("# 8192 -> 28672 weight (r = 16), the rank-r streaming kernels of the LLaMA-65B q\n")
+        fh.write("# projection (2048 tokens, r = 64; their writes are the fp32 partial sums of the\n")
+        fh.write("# splits, summed by the next launch, against the result written once).\n")
+        fh.write("# rocprofv3 FETCH_SIZE and WRITE_SIZE per launch\n")
         fh.write(f"# (the last three dispatches of each), each scaled by the same counter on a device copy of\n")
         fh.write(f"# {CALIB_BYTES} bytes.  Commands (from /tmp, TMPDIR=/tmp):\n")
         fh.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_f> -o f -- python3 <repo>/bench.py --pmc-pass-hbm\n")
@@ -452,8 +479,6 @@ def main():
                     help="only run the backward (input-gradient GEMM) for counters")
     ap.add_argument("--summarize-counters-bwd", nargs="+", metavar="PATH",
                     help="OUT_TXT then the counter CSVs of rocprofv3 --pmc runs of --pmc-pass-bwd")
-    ap.add_argument("--summarize-counters-adapter", nargs="+", metavar="PATH",
-                    help="OUT_TXT then the counter CSVs of --pmc-pass-bwd (dA / dB GEMMs)")
     ap.add_argument("--pmc-pass-hbm", action="store_true",
                     help="only run the HBM-bound kernels and a calibration copy (counters)")
     ap.add_argument("--summarize-hbm", nargs=3, metavar=("OUT_TXT", "FETCH_CSV", "WRITE_CSV"))
@@ -484,15 +509,10 @@ def main():
     if args.pmc_pass_bwd:
         pmc_pass_bwd()
         return
-    if args.summarize_counters_adapter:
-        summarize_counters(*args.summarize_counters_adapter, kernel=GRAD_GEMM,
-                           what="adapter-gradient GEMMs dA = s·Vᵀ·X and dB = s·dYᵀ·U (one kernel, "
-                                "both launches averaged)", pass_flag="--pmc-pass-bwd",
-                           summary_flag="--summarize-counters-adapter")
-        return
     if args.summarize_counters_bwd:
         summarize_counters(*args.summarize_counters_bwd, kernel=DX_GEMM,
                            what="input-gradient dequant-GEMM", pass_flag="--pmc-pass-bwd",
+                           workload="LLaMA-7B MLP: 4096 tokens, 4096 -> 11008, r = 64",
                            summary_flag="--summarize-counters-bwd")
         return
     if args.summarize_hbm:

@@ -174,6 +174,16 @@ __device__ inline void frags_tr(const char* t, int col0, int lane, bf16x8 (&f)[4
   f[3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r6, r7, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Workgroup b of a job of `total` runs on XCD (b + base) mod 8.  Deal each
+// XCD a contiguous run of the job's (tile, split) order, so that the
+// workgroups sharing a split (the same slice of the adapter factor) share that
+// XCD's L2 instead of every XCD fetching the whole factor.  A bijection on
+// [0, total).
+__device__ inline int xcd_order(int b, int total) {
+  const int per = total >> 3, rem = total & 7, x = b & 7;
+  return x * per + min(x, rem) + (b >> 3);
+}
+
 // acc += a·b with the operands swapped: lane l then holds stream index
 // l mod 32 and ranks 8 g + 4 (l / 32) + c for e = 4 g + c.
 __device__ inline floatx16 mma(const bf16x8& a, const bf16x8& b, const floatx16& acc) {
@@ -239,7 +249,8 @@ __device__ __attribute__((always_inline)) inline void rows_body(const AdapterArg
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = bx % g.tiles, split = bx / g.tiles;
+  const int lin = xcd_order(bx, g.tiles * g.nsplit);
+  const int tile = lin % g.tiles, split = lin / g.tiles;
   const int64_t m0 = (int64_t)tile * 128, j0 = (int64_t)blockIdx.y * 128;
   const int kt0 = split * g.kt_per_split;
   const int kt1 = min(g.nkt, kt0 + g.kt_per_split);
@@ -319,7 +330,8 @@ __device__ __attribute__((always_inline)) inline void cols_body(const AdapterArg
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = bx % g.tiles, split = bx / g.tiles;
+  const int lin = xcd_order(bx, g.tiles * g.nsplit);
+  const int tile = lin % g.tiles, split = lin / g.tiles;
   const int64_t l0 = (int64_t)tile * 128, j0 = (int64_t)blockIdx.y * 128;
   const int kt0 = split * g.kt_per_split;
   const int kt1 = min(g.nkt, kt0 + g.kt_per_split);

@@ -314,7 +314,7 @@ AdapterArgs ad_args(const AdPlan& p, const uint16_t* S, int64_t lds, const uint1
   a.s = S; a.lds = lds; a.f = F; a.ldf = ldf; a.r = r; a.nout = nout; a.red = red;
   a.part = part; a.ldp = p.ldp;
   a.part_stride = (tr ? (int64_t)32 * p.nb * p.ncg : nout) * p.ldp;
-  a.tiles = p.tiles; a.kt_per_split = p.ktps; a.nkt = p.nkt;
+  a.tiles = p.tiles; a.kt_per_split = p.ktps; a.nkt = p.nkt; a.nsplit = p.nsplit;
   return a;
 }
 

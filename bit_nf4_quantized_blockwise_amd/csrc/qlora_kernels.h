@@ -80,7 +80,7 @@ struct AdapterArgs {
   int64_t red;        // rows: columns of S; cols: tokens
   float* part;
   int64_t ldp, part_stride;
-  int32_t tiles, kt_per_split, nkt;
+  int32_t tiles, kt_per_split, nkt, nsplit;
 };
 constexpr int kAdapterTile = 128;  // stream indices per workgroup
 template <int NB, bool FN>
