@@ -90,6 +90,9 @@ def _run_case(M, K, N, r, alpha, seed, bwd=True):
     (9, 2048, 1000, 72, 16.0),    # ... two token groups, five rank groups
     (16, 4096, 4096, 256, 16.0),  # ... largest rank
     (5, 3072, 75, 3, 16.0),       # ... rank and n_out not multiples of 8
+    (300, 256, 264, 129, 16.0),   # two groups of ranks, the second holding one rank
+    (40, 192, 96, 200, 16.0),     # ... split-K path, a rank that is not a multiple of 8
+    (7, 512, 72, 129, 16.0),      # ... few-token path
 ])
 def test_small_shapes(M, K, N, r, alpha):
     _run_case(M, K, N, r, alpha, seed=M + K + N + r)
@@ -206,3 +209,44 @@ def test_llama7b_mlp_full_fwd_bwd():
     assert_close("dX", _f64(dX), dXr)
     assert_close("dA", _f64(dA), dAr)
     assert_close("dB", _f64(dB), dBr)
+
+
+def test_offsets_past_2_31_bytes():
+    """A 2.16 GB streamed operand: X [33000][32768] bf16, n_out = 64, r = 16.
+    The adapter-gradient kernel's splits then cap their rows so that buffer
+    offsets stay below 2^31 bytes (two splits of at most 32704 rows), and
+    every other kernel addresses rows far past 2^31 bytes.  U and dB in full;
+    Y, dX on sampled token rows; dA on sampled columns (whole NF4 blocks)."""
+    M, K, N, r, alpha = 33000, 32768, 64, 16, 16.0
+    say(f"[linear] M={M} K={K} N={N} r={r}: offsets past 2^31 bytes")
+    key = 960
+    W = wl.weight_f32(key, N, K)
+    A = wl.bf16_normal(key, (r, K), 0.01, tensor=wl.T_A)
+    B = wl.bf16_normal(key, (N, r), 0.01, tensor=wl.T_B)
+    X = wl.bf16_normal(key, (M, K), 1.0, tensor=wl.T_X)
+    dY = wl.bf16_normal(key, (M, N), 1.0, tensor=wl.T_DY)
+    o = oracle_weight(W)
+    wq = q.quantize_weight(to_dev(W))
+    Xd, Ad, Bd, dYd = to_dev(X), to_dev(A), to_dev(B), to_dev(dY)
+    Y, U = q.linear_fwd(wq, Xd, Ad, Bd, alpha)
+    dX, dA, dB = q.linear_bwd(wq, Xd, dYd, Ad, Bd, U, alpha)
+    torch.cuda.synchronize()
+    del Xd
+    s = lora_scale(alpha, r)
+    A64, B64, dY64 = _f64(A), _f64(B), _f64(dY)
+    # U = X·Aᵀ and V = dY·B in float64, X in row chunks
+    Ur = np.empty((M, r))
+    for r0 in range(0, M, 2048):
+        Ur[r0:r0 + 2048] = _f64(X[r0:r0 + 2048]) @ A64.T
+    assert_close("U", _f64(U), Ur)
+    assert_close("dB", _f64(dB), s * (dY64.T @ Ur))
+    rows = np.r_[0:3, 16380:16390, 32700:32710, M - 5:M]
+    Xr = _f64(X[torch.from_numpy(rows)])
+    Yr, _ = linear_fwd(Xr, o["w64"], A64, B64, s)
+    assert_close("Y rows", _f64(Y)[rows], Yr)
+    dXr, _, _ = linear_bwd(Xr, dY64[rows], o["w64"], A64, B64, s)
+    assert_close("dX rows", _f64(dX[torch.as_tensor(rows, device=dX.device)]), dXr)
+    cols = np.r_[0:64, 16384:16448, K - 64:K]
+    V = dY64 @ B64
+    dAr = s * (V.T @ _f64(X[:, torch.from_numpy(cols)]))
+    assert_close("dA cols", _f64(dA)[:, cols], dAr)
