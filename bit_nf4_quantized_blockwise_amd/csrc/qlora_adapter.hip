@@ -31,15 +31,11 @@ namespace qlora {
 
 namespace {
 
-// ring slots (stages): six while a stage is 20-24 KB, four at 32 KB (128 ranks)
-#ifndef QL_AD_RING
-#define QL_AD_RING 6
-#endif
-#ifndef QL_AD_RING4
-#define QL_AD_RING4 4
-#endif
+// ring slots (stages): six while a stage is 20-24 KB, four at 32 KB (128
+// ranks); one workgroup per CU (shallower rings with two or three workgroups
+// per CU, and so more splits, were slower)
 template <int NB>
-constexpr int ring_of() { return NB == 4 ? QL_AD_RING4 : QL_AD_RING; }
+constexpr int ring_of() { return NB == 4 ? 4 : 6; }
 // One stage: 16 KB of the streamed operand (128 rows x 64 k, or 64 tokens x
 // 128 columns) and 4 KB per block of 32 ranks of the factor.
 template <int NB>
@@ -48,7 +44,6 @@ constexpr int kOOBA = 0x7ffffff0;        // a buffer offset past every range: lo
 constexpr int kRsrcWord3A = 0x00020000;  // raw buffer, 32-bit data format
 
 typedef short s4v __attribute__((ext_vector_type(4)));
-
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
