@@ -370,7 +370,8 @@ qlora_status validate_linear(const qlora_nf4_weight* w, int64_t M, int32_t r) {
 
 #define ALIGNED_OR_NULL(p) QCHECK((p) != nullptr, QLORA_ERR_NULL); QCHECK(aligned16(p), QLORA_ERR_ALIGN)
 
-// U = X·Aᵀ (bf16 [M][r]) through split-K partials in ws.
+// U = X·Aᵀ (bf16 [M][r]): the rank-r streaming kernel's split partial sums in ws, then
+// their reduction (few tokens: one small kernel, no partial sums).
 qlora_status lora_down_impl(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r,
                             uint16_t* U, uint16_t* Upad, int64_t rp, char* ws, const FwdWs& L,
                             hipStream_t st) {
