@@ -37,9 +37,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-# float32 fma on the vector ALU without packed-float32 instructions (the
-# library is built without them): 256 CUs x 64 lanes x 2 flop x 2.4 GHz
-FP32_FMA_PEAK_TFLOPS = 78.6
+# float64 fma on the vector ALU: 256 CUs x 64 lanes x 2 flop x 2.4 GHz
+FP64_FMA_PEAK_TFLOPS = 78.6
 GEMM_SOURCES = ["qlora_gemm.hip", "qlora_common.h", "qlora_kernels.h", "qlora_philox.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_gemm_fwd_llama65b_layer.txt")
 CALIB_BYTES = 512 << 20  # plain device copy used to scale the byte counters
@@ -1063,7 +1062,7 @@ def variant_rows(W):
 
 def merge_row(W, B, A, alpha):
     """Adapter merge at the 11008 x 4096 shape, r = 64: the merge kernel alone
-    (2·n·r flop of float32 fma on the vector ALU, fixed order), the merge with
+    (2·n·r flop of float64 fma on the vector ALU, rounded once to bf16), the merge with
     re-quantisation, both bases, and how much of the adapter's delta survives
     re-quantisation on each path (its projection on the delta)."""
     import torch
@@ -1090,7 +1089,7 @@ def merge_row(W, B, A, alpha):
         out["delta_kept_" + name] = float(((d - ref) * D).sum() / (D * D).sum())
         out["rel_err_" + name] = float((d - (W16.float() + D)).norm() / (W16.float() + D).norm())
     return dict(r=r, ms_merge=ms_m, TFLOPs_merge=flops / (ms_m * 1e-3) / 1e12,
-                alu_frac=flops / (ms_m * 1e-3) / 1e12 / FP32_FMA_PEAK_TFLOPS,
+                alu_frac=flops / (ms_m * 1e-3) / 1e12 / FP64_FMA_PEAK_TFLOPS,
                 ms_merge_requant_16bit=ms_mq, ms_merge_requant_4bit=ms_m4, **out)
 
 

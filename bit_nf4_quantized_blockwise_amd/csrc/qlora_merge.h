@@ -23,8 +23,8 @@ struct MergeArgs {
   uint16_t* merged;        // [n_out][k_in] bf16
 };
 
-// merged = RNE_bf16(RN32(base + RN32(s · Σ_j B[n][j]·A[j][k]))), the float32
-// sum taken over j = 0, 1, …, r − 1 in order.
+// merged = RNE_bf16(RN64(base + RN64(s · Σ_j B[n][j]·A[j][k]))), the sum of
+// exact float64 products formed by float64 fma over j = 0, 1, …, r − 1.
 __global__ void merge_adapter_kernel(MergeArgs g);
 // quantize_nf4_dq_kernel on a bf16 input.
 __global__ void quantize_nf4_dq_bf16_kernel(const uint16_t* w, int64_t n, int64_t nblocks,

@@ -195,9 +195,11 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight *w /* host struct *
  * inference; merging into the 4-bit base re-rounds the sum onto the 4-bit
  * grid).  Exactly one base: w16 (bf16 [n_out][k_in], the recommended path) or
  * w4 (the NF4 + DQ weight, decoded as qlora_dequantize_nf4 does; the path the
- * page warns about).  With s = RN32(alpha / r), for every element:
- *   acc = Σ_j B[n][j]·A[j][k]   float32, j = 0, 1, …, r − 1 in order
- *   merged[n][k] = RNE_bf16(RN32(base + RN32(s·acc)))
+ * page warns about).  With s = RN32(alpha / r), for every element the page's
+ * W + s·B·A in float64, rounded once to bf16:
+ *   acc = Σ_j B[n][j]·A[j][k]   float64 (exact products; exact sums at the
+ *                               magnitudes of weights and adapters)
+ *   merged[n][k] = RNE_bf16(RN64(base + RN64(s·acc)))
  * A [r][k_in], B [n_out][r] bf16; merged bf16 [n_out][k_in] (required).  When
  * packed is not NULL, merged is then quantised exactly as
  * qlora_quantize_nf4_dq would quantise its float32 values: packed

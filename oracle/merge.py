@@ -16,56 +16,48 @@ Sources
 Readings taken where the pages leave a step open
 ------------------------------------------------
 * Merged value of element (n, k), base value w (the bf16 16-bit base, or the
-  decoded NF4 weight ŵ for the 4-bit path), s = RN32(α/r):
-      acc = Σ_j B[n][j]·A[j][k], summed in float32 in the order j = 0, 1, …,
-            r − 1 (each bf16 × bf16 product is exact in float32, so only the
-            additions round)
-      t   = RN32(s · acc)
-      x   = RN32(w + t)
-      m   = RNE_bf16(x)          the merged 16-bit weight the page saves
-  and the re-quantised weight is the NF4 + Double Quantization of m (the
-  quantiser's own readings).  Fixing the order of the float32 sum makes the
-  merged value — and so every code decided on it — a function of the inputs
-  alone.
+  decoded NF4 weight ŵ for the 4-bit path), s = RN32(α/r): the page's
+  W + (α/r)·B·A evaluated in float64 and rounded once to bf16,
+      m = RNE_bf16(w + s·Σ_j B[n][j]·A[j][k]).
+  Each bf16 × bf16 product is exact in float64, and so is the sum of the r
+  products unless their exponents span more than about 53 − 16 − log2(r)
+  bits; w + s·sum is then exact too for the weights and adapters of these
+  workloads.  Where it is not, the float64 result is within a few float64
+  ulps of the exact value and differs from the exact value's rounding only
+  for a value that close to a bf16 rounding boundary.  The re-quantised
+  weight is the NF4 + Double Quantization of m (the quantiser's own
+  readings).
 * The 4-bit path ("merge into the 4-bit base") is the same formula with
   w = ŵ, the decoded NF4 + DQ weight.
 
-Parity: pinned (tests/test_oracle_merge.py): the rank-r sum against exact
-rational arithmetic on dyadic inputs (no rounding) and within the float32
-error bound r·2⁻²⁴·Σ|B·A| on random inputs; A = 0 or B = 0 leaves the base
-(and a base on the bf16 grid) unchanged; re-quantising goes through the
-pinned quantiser; the page's warning holds: with an adapter smaller than
-half the local level gap the 4-bit merge returns the original codes (the
-delta is lost entirely), and the 4-bit path's error against W16 + delta
-exceeds the 16-bit path's.
+Parity: pinned (tests/test_oracle_merge.py): the merged value against the
+exact rational W + s·B·A rounded to the nearest bf16 by a search over the
+whole bf16 grid (ties to the even pattern), on random bf16 inputs; the
+rank-r sum against exact rational arithmetic; the float64 → bf16 rounding
+against that same search at ties, subnormals and the overflow boundary;
+A = 0 or B = 0 leaves the base (and a base on the bf16 grid) unchanged;
+re-quantising goes through the pinned quantiser; the page's warning holds:
+with an adapter smaller than half the local level gap the 4-bit merge
+returns the original codes (the delta is lost entirely), and the 4-bit
+path's error against W16 + delta exceeds the 16-bit path's.
 """
 
 import numpy as np
 
-from .quant import bf16_round, bf16_to_f64, dequantize_nf4, double_quant, quantize_nf4
-
-
-def _f32(bits_or_vals):
-    return np.asarray(bits_or_vals, dtype=np.float32)
+from .quant import bf16_round64, bf16_to_f64, dequantize_nf4, double_quant, quantize_nf4
 
 
 def rank_r_sum(A, B):
-    """acc[n][k] = Σ_j B[n][j]·A[j][k] in float32, j ascending (A [r][K], B [N][r],
-    float32 arrays holding bf16 values)."""
-    A = _f32(A)
-    B = _f32(B)
-    acc = np.zeros((B.shape[0], A.shape[1]), dtype=np.float32)
-    for j in range(A.shape[0]):
-        acc = acc + B[:, j:j + 1] * A[j:j + 1, :]  # exact products, float32 additions
-    return acc
+    """acc[n][k] = Σ_j B[n][j]·A[j][k] in float64 (A [r][K], B [N][r], arrays
+    holding bf16 values)."""
+    return np.asarray(B, dtype=np.float64) @ np.asarray(A, dtype=np.float64)
 
 
 def merge_bf16(base, A, B, s):
-    """m = RNE_bf16(RN32(base + RN32(s·acc))) as bf16 bit patterns [N][K]; base is
-    a float32 array of bf16 values."""
-    t = np.float32(s) * rank_r_sum(A, B)
-    x = _f32(base) + t
-    return bf16_round(x.ravel()).reshape(x.shape)
+    """m = RNE_bf16(base + s·acc), evaluated in float64 and rounded once, as
+    bf16 bit patterns [N][K]; base holds bf16 values."""
+    x = np.asarray(base, dtype=np.float64) + np.float64(np.float32(s)) * rank_r_sum(A, B)
+    return bf16_round64(x)
 
 
 def requantize(m_bits):

@@ -144,6 +144,26 @@ def bf16_round(x):
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def bf16_round64(x):
+    """float64 -> bfloat16 bit patterns, round to nearest, ties to even: the
+    bf16 value nearest to x, and of two equally near the one whose last
+    stored bit is 0.  bf16 keeps 8 significant bits, so with x = m·2^e
+    (m in [0.5, 1)) its spacing near x is 2^(e−8), and 2^-133 below 2^-126
+    (the subnormals); x / spacing is an exact power-of-two scaling, and its
+    nearest integer (ties to even) times the spacing is the rounded value,
+    which float32 holds exactly.  Values at or beyond the largest bf16 plus
+    half its spacing become ±inf (float32's own overflow on the last step)."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    _, e = np.frexp(ax)
+    q = np.maximum(e - 8, -133)
+    v = np.ldexp(np.rint(np.ldexp(ax, -q)), q)
+    with np.errstate(over="ignore"):
+        v32 = v.astype(np.float32)
+    bits = (v32.view(np.uint32) >> 16).astype(np.uint16)
+    return bits | (np.signbit(x).astype(np.uint16) << 15)
+
+
 def bf16_to_f64(bits):
     bits = np.asarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
