@@ -255,8 +255,8 @@ __device__ __attribute__((always_inline)) inline void rows_body(const AdapterArg
   // B's buffer starts at the split's first row (its offsets then stay small)
   const int64_t kbeg = (int64_t)kt0 * 64;
   __amdgpu_buffer_rsrc_t rf;
-  if constexpr (FN)
-    rf = make_rsrc(g.f + kbeg * g.ldf + j0, (g.red - kbeg) * g.ldf * 2 - j0 * 2);
+  if constexpr (FN)  // B ends at row frows (the reduction may run on over zeros of S)
+    rf = make_rsrc(g.f + kbeg * g.ldf + j0, (g.frows - kbeg) * g.ldf * 2 - j0 * 2);
   else
     rf = make_rsrc(g.f + j0 * g.ldf, ((int64_t)g.r - j0) * g.ldf * 2);
 

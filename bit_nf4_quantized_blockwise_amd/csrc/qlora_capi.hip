@@ -104,6 +104,14 @@ constexpr int64_t kFewM = 16;               // up to this many tokens: the strea
 
 bool use_big(int64_t M) { return M >= kBigM; }
 bool use_gemv(int64_t M) { return M <= kFewM; }
+// The one-launch forward of a small weight: few tokens, few ranks, k_in within
+// the kernel's k range (two 128-k chunks per wave), and at most one workgroup
+// of 16 columns per compute unit (every workgroup reads all of X and A, so a
+// second round of workgroups costs more than the GEMV's second launch).
+bool use_small(int64_t M, int64_t N, int64_t K, int32_t r) {
+  return M >= 1 && M <= kFewM && r <= kSmallMaxRank && K <= 128 * kSmallWaves * kSmallMaxCpw &&
+         ceil_div(N, 16) <= device_cus();
+}
 
 struct GemvPlan {
   int cpw, mg, ksplit, gx, groups;
@@ -311,7 +319,7 @@ constexpr ReduceOut kNoOut{nullptr, nullptr, 0};
 AdapterArgs ad_args(const AdPlan& p, const uint16_t* S, int64_t lds, const uint16_t* F, int64_t ldf,
                     int32_t r, int64_t nout, int64_t red, float* part, bool tr = false) {
   AdapterArgs a{};
-  a.s = S; a.lds = lds; a.f = F; a.ldf = ldf; a.r = r; a.nout = nout; a.red = red;
+  a.s = S; a.lds = lds; a.f = F; a.ldf = ldf; a.r = r; a.nout = nout; a.red = red; a.frows = red;
   a.part = part; a.ldp = p.ldp;
   a.part_stride = (tr ? (int64_t)32 * p.nb * p.ncg : nout) * p.ldp;
   a.tiles = p.tiles; a.kt_per_split = p.ktps; a.nkt = p.nkt; a.nsplit = p.nsplit;
@@ -476,9 +484,26 @@ float scale_of(float alpha, int32_t r) { return alpha / (float)r; }
 
 // Forward with the main product on X and the adapter on Xl (X itself, or its
 // dropout): U = Xl·Aᵀ, Y = X·Ŵᵀ + s·U·Bᵀ.
+// Y and U of a small weight for few tokens in one launch (both products read X).
+qlora_status small_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                       const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U,
+                       hipStream_t st) {
+  SmallFwdArgs a{};
+  a.x = X; a.M = (int32_t)M; a.K = w->k_in; a.N = w->n_out;
+  a.packed = w->packed; a.qabsmax = w->qabsmax; a.c2 = w->c2;
+  a.a = A; a.r = r; a.b = B; a.s = s; a.y = Y; a.u = U;
+  const dim3 grid((unsigned)ceil_div(w->n_out, 16));
+  if (w->k_in <= 128 * kSmallWaves)
+    hipLaunchKernelGGL(nf4_small_fwd_kernel<1>, grid, dim3(64 * kSmallWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL(nf4_small_fwd_kernel<2>, grid, dim3(64 * kSmallWaves), 0, st, a);
+  return launched();
+}
+
 qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* Xl,
                              int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float s,
                              uint16_t* Y, uint16_t* U, char* ws, const FwdWs& L, hipStream_t st) {
+  if (X == Xl && use_small(M, w->n_out, w->k_in, r)) return small_fwd(w, X, M, A, B, r, s, Y, U, st);
   const bool pad = r % 8 != 0 && !use_gemv(M);
   uint16_t* Up = pad ? reinterpret_cast<uint16_t*>(ws + L.pad_u) : nullptr;
   qlora_status e = lora_down_impl(Xl, M, w->k_in, A, r, U, Up, L.rp, ws, L, st);
@@ -588,11 +613,12 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const
   }
 
   // One launch streams dY for both V = dY·B (over the padded pitch: dY holds
-  // zeros past n_out and B's rows end there) and dB = s·dYᵀ·U; one more sums
+  // zeros past n_out, and B's rows past n_out read as zero) and dB = s·dYᵀ·U; one more sums
   // both products' splits: V [M][rp] bf16 (zero-padded) and dB [N][r].
   {
     float* part_db = reinterpret_cast<float*>(ws + L.part_db);
-    const AdapterArgs av = ad_args(L.pv, dYa, ldy, Ba, L.rp, r, M, L.Np, part);
+    AdapterArgs av = ad_args(L.pv, dYa, ldy, Ba, L.rp, r, M, L.Np, part);
+    av.frows = N;  // B has n_out rows; dY's padding columns meet zeros, not the memory past B
     const AdapterArgs ab = ad_args(L.pdb, dYa, ldy, Ua, L.rp, r, N, M, part_db);
     const int nv = L.pv.tiles * L.pv.nsplit;
     const dim3 grid((unsigned)(nv + L.pdb.tiles * L.pdb.nsplit), (unsigned)L.pv.ncg);

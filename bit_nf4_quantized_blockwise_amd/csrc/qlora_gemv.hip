@@ -379,6 +379,174 @@ __global__ __launch_bounds__(kDownThreads) void lora_down_small_kernel(
   }
 }
 
+// ---- small weights: the whole forward in one launch ----------------------------
+// Y = RNE_bf16(X·Ŵᵀ + s·U·Bᵀ) and U = RNE_bf16(X·Aᵀ) for at most 16 tokens and
+// kSmallMaxRank ranks ("QLoRAの理論と実装", QLoRAの計算フロー: the main path
+// and the adapter path of one layer).  Ŵ is decoded as the dequantiser decodes
+// it, RNE_bf16(RN32(c_idx · â)), so the matrix cores see the same bf16 weight
+// as in the many-token GEMMs.  One workgroup per 16 output rows; its 16 waves
+// split k into 128-k chunks (wave w takes chunks w, w + 16, ...), and every
+// lane issues all of its loads (B's rows, weight codes, block scales, tokens,
+// rows of A) before its first wait, so the launch pays one memory latency.
+// Each 16×16×32 MFMA takes the 16 tokens as its rows: against the decoded
+// weight it accumulates Y's partial sums, against 16 rows of A (zero past r)
+// U's.  The waves' sums meet in LDS in wave order; every workgroup forms the
+// same U (fixed order), rounds it to bf16 and adds s·U·Bᵀ to its columns, and
+// workgroup 0 writes U.
+//
+// Lane (c = l % 16, q = l / 16) of a chunk at k0 holds weight row n0 + c at
+// k = k0 + 32q .. k0 + 32q + 31 (one 16-byte load of 32 codes), and MFMA j of
+// the chunk takes k0 + 32q + 8j .. + 7 on both operands: a permutation of k
+// shared by both, so the sums are those of X·Ŵᵀ.  Every workgroup reads all of
+// X and A, so those loads are the ones to keep cheap: each covers 4 rows ×
+// 256 contiguous bytes (whole cache lines), and the chunk's 16 rows of tokens
+// and of A pass through a wave-private LDS area (row pitch 272 B, so both the
+// row writes and the operand reads are conflict-free) into operand order.
+template <int CPW>
+__global__ __launch_bounds__(64 * kSmallWaves) void nf4_small_fwd_kernel(SmallFwdArgs g) {
+  constexpr int NW = kSmallWaves;
+  constexpr int RP = kSmallMaxRank + 1;  // padded pitch of the LDS rows of B and U
+  constexpr int SP = 272;                // staging row pitch: 128 bf16 + 16 B
+  constexpr int kStage = 2 * 16 * SP;    // one wave's tokens and rows of A for one chunk
+  static_assert(NW * kStage >= 2 * NW * 64 * 16, "the reduction reuses the staging area");
+  __shared__ __attribute__((aligned(16))) char stage[NW * kStage];
+  __shared__ float cb[16];
+  __shared__ float bsh[16 * RP];  // B[n0 + c][j] at c·RP + j
+  __shared__ float ush[16 * RP];  // U rounded to bf16, token t at t·RP + j
+  floatx4(*red)[NW][64] = reinterpret_cast<floatx4(*)[NW][64]>(stage);  // after the MFMAs
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c16 = lane & 15, qd = lane >> 4;
+  const int64_t K = g.K, N = g.N;
+  const int M = g.M, r = g.r;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n = n0 + c16;
+  const int64_t bpr = K >> 6;  // 64-blocks per weight row
+
+  // Raw buffer loads: an offset past a buffer's end reads zero, so the rows
+  // past N, the tokens past M, the ranks past r and the k past K need no branch.
+  constexpr int kOut = 0x7ffffff0;
+  const int64_t rows = N - n0 < 16 ? N - n0 : 16;
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(g.b + n0 * r, rows * r * 2);
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.packed + n0 * (K >> 1), rows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(g.qabsmax + n0 * bpr, rows * bpr);
+  const __amdgpu_buffer_rsrc_t c2r = make_rsrc(g.c2, ((N * bpr + 255) >> 8) * 4);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(g.x, (int64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(g.a, (int64_t)r * K * 2);
+
+  // B's 16 rows first: the oldest load, so the wait before its LDS store waits
+  // for nothing else
+  const int bi = tid / r, bj = tid - bi * r;
+  const uint32_t bv =
+      __builtin_amdgcn_raw_buffer_load_b16(br, tid < 16 * r ? (bi * r + bj) * 2 : kOut, 0, 0);
+
+  // xs/as: rows 4j + q of the chunk's tokens / rows of A, 16 bytes at k0 + 8c
+  u32x4 pk[CPW], xs[CPW][4], as[CPW][4];
+  uint32_t qv[CPW], c2v[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int k0 = (w + NW * i) * 128;
+    const int kq = k0 + 32 * qd;
+    const bool kin = kq < K;  // K % 64 == 0: a lane's 32 k are all in or all out
+    pk[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, kin ? (int)((c16 * K + kq) >> 1) : kOut, 0, 0));
+    const int64_t b = n * bpr + (kq >> 6);  // the lane's 64-block
+    int qoff = kin ? (int)(c16 * bpr + (kq >> 6)) : kOut;
+    asm volatile("" : "+v"(qoff));  // one load with a lane offset, not one per side of the select
+    qv[i] = __builtin_amdgcn_raw_buffer_load_b8(qr, qoff, 0, 0);
+    c2v[i] = __builtin_amdgcn_raw_buffer_load_b32(c2r, kin && n < N ? (int)((b >> 8) * 4) : kOut, 0, 0);
+    const bool cin = k0 + 8 * c16 < K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * j + qd;
+      const int off = (int)((row * K + k0 + 8 * c16) * 2);
+      // groups of 4 rows wholly past M (past r) are not loaded (a uniform branch)
+      if (4 * j < M)
+        xs[i][j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, cin && row < M ? off : kOut, 0, 0));
+      if (4 * j < r)
+        as[i][j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, cin && row < r ? off : kOut, 0, 0));
+    }
+  }
+  if (tid < 16) cb[tid] = bits_to_float(level_bits(tid));
+  if (tid < 16 * r) bsh[bi * RP + bj] = bf16_bits_to_float(bv);
+  lds_barrier();  // the codebook is in place; the other loads stay in flight
+
+  const char* cbb = reinterpret_cast<const char*>(cb);
+  char* xst = stage + w * kStage;  // this wave's tokens, then its rows of A
+  char* ast = xst + 16 * SP;
+  floatx4 accY = floatx4{0.f, 0.f, 0.f, 0.f}, accU = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    if ((w + NW * i) * 128 >= K) break;  // wave-uniform: no chunk left
+    // rows into the staging area, then back in operand order (a wave's LDS
+    // operations complete in order, so the next chunk's writes cannot pass
+    // these reads).  Rows of groups that were not loaded keep whatever the area
+    // held: a token row past M only reaches outputs of that token, which are
+    // not stored, and a row of A past r only U's columns past r, which are
+    // neither stored nor used.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (4 * j < M) *reinterpret_cast<u32x4*>(xst + (4 * j + qd) * SP + 16 * c16) = xs[i][j];
+      if (4 * j < r) *reinterpret_cast<u32x4*>(ast + (4 * j + qd) * SP + 16 * c16) = as[i][j];
+    }
+    const float ah = __builtin_bit_cast(float, c2v[i]) * (float)(int8_t)qv[i];  // â = RN32(c2 · q)
+    // the chunk's 32 levels first, so their LDS reads share one latency; the
+    // decoded weight is RNE_bf16(RN32(level · â)), element 2t in the low nibble
+    // of byte t
+    float lv[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t ev = (pk[i][j] << 2) & 0x3c3c3c3cu;  // 4 · code of elements 0, 2, 4, 6
+      const uint32_t od = (pk[i][j] >> 2) & 0x3c3c3c3cu;  // 4 · code of elements 1, 3, 5, 7
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        lv[j][2 * d] = *reinterpret_cast<const float*>(cbb + ((ev >> (8 * d)) & 0xffu));
+        lv[j][2 * d + 1] = *reinterpret_cast<const float*>(cbb + ((od >> (8 * d)) & 0xffu));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 xo = *reinterpret_cast<const u32x4*>(xst + c16 * SP + 64 * qd + 16 * j);
+      const u32x4 ao = *reinterpret_cast<const u32x4*>(ast + c16 * SP + 64 * qd + 16 * j);
+      u32x4 bop;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) bop[d] = pack_bf16x2(lv[j][2 * d] * ah, lv[j][2 * d + 1] * ah);
+      accY = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xo),
+                                                     __builtin_bit_cast(bf16x8, bop), accY, 0, 0, 0);
+      accU = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xo),
+                                                     __builtin_bit_cast(bf16x8, ao), accU, 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with its staging area
+  red[0][w][lane] = accY;
+  red[1][w][lane] = accU;
+  __syncthreads();
+  // output (token t, column c) sits in lane 16·(t / 4) + c, entry t % 4
+  const int t = tid >> 4, c = tid & 15;
+  const int src = 16 * (t >> 2) + c, e = t & 3;
+  if (tid < 256) {
+    float u = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) u += red[1][ww][src][e];
+    const uint16_t ub = bf16_rne_bits(u);
+    ush[t * RP + c] = bf16_bits_to_float(ub);
+    if (blockIdx.x == 0 && t < M && c < r) g.u[t * r + c] = ub;
+  }
+  __syncthreads();
+  if (tid < 256 && t < M && n0 + c < N) {
+    float y = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) y += red[0][ww][src][e];
+    float l = 0.0f;
+    for (int j = 0; j < r; ++j) l += ush[t * RP + j] * bsh[c * RP + j];
+    g.y[(int64_t)t * N + n0 + c] = bf16_rne_bits(y + g.s * l);
+  }
+}
+
+template __global__ void nf4_small_fwd_kernel<1>(SmallFwdArgs);
+template __global__ void nf4_small_fwd_kernel<2>(SmallFwdArgs);
+
 template __global__ void nf4_gemv_kernel<1, 1, 1, false>(GemvArgs);
 template __global__ void nf4_gemv_kernel<1, 1, 2, false>(GemvArgs);
 template __global__ void nf4_gemv_kernel<1, 1, 3, false>(GemvArgs);

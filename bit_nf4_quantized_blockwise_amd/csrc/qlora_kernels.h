@@ -76,6 +76,7 @@ struct AdapterArgs {
   const uint16_t* f;  // the factor (A, B, U or V), row-major, pitch ldf
   int64_t ldf;
   int32_t r;          // rows of F when F = A
+  int64_t frows;      // rows of F when F = B: rows k >= frows read as zero
   int64_t nout;       // rows: tokens; cols: columns of S
   int64_t red;        // rows: columns of S; cols: tokens
   float* part;
@@ -93,6 +94,29 @@ __global__ void adapter_dy_kernel(AdapterArgs gv, AdapterArgs gb, int nv);
 constexpr int kGemvWaves = 8;   // waves per few-token GEMV workgroup (they split the reduction)
 template <int CPW, int MG, int G, bool QV>
 __global__ void nf4_gemv_kernel(GemvArgs g);
+
+// The whole forward of a small weight for few tokens in one launch (M <= 16,
+// r <= kSmallMaxRank, k_in <= 128 · kSmallWaves · kSmallMaxCpw): each
+// workgroup owns 16 output rows over all of k and forms U = X·Aᵀ itself.
+struct SmallFwdArgs {
+  const uint16_t* x;  // [M][K] bf16
+  int32_t M;
+  int64_t K, N;
+  const uint8_t* packed;  // W[N][K] NF4 + DQ
+  const int8_t* qabsmax;
+  const float* c2;
+  const uint16_t* a;  // [r][K] bf16
+  int32_t r;
+  const uint16_t* b;  // [N][r] bf16, pitch r
+  float s;
+  uint16_t* y;  // [M][N] bf16
+  uint16_t* u;  // [M][r] bf16, pitch r (written by workgroup 0)
+};
+constexpr int kSmallWaves = 16;   // waves per workgroup; they split k
+constexpr int kSmallMaxCpw = 2;   // 128-k chunks per wave
+constexpr int kSmallMaxRank = 16;
+template <int CPW>
+__global__ void nf4_small_fwd_kernel(SmallFwdArgs g);
 
 // xd = mask ⊙ x over n / 8 blocks of 8 bf16 (LoRA dropout, see qlora_philox.h).
 __global__ void lora_dropout_kernel(const uint16_t* x, int64_t nblk, DropoutKey d, uint16_t* xd);

@@ -93,6 +93,15 @@ def _run_case(M, K, N, r, alpha, seed, bwd=True):
     (300, 256, 264, 129, 16.0),   # two groups of ranks, the second holding one rank
     (40, 192, 96, 200, 16.0),     # ... split-K path, a rank that is not a multiple of 8
     (7, 512, 72, 129, 16.0),      # ... few-token path
+    # one-launch path for small weights (<= 16 tokens, r <= 16, k_in <= 4096,
+    # one workgroup of 16 columns per compute unit)
+    (16, 4096, 4096, 16, 32.0),   # largest rank, two 128-k chunks per wave
+    (1, 64, 16, 1, 2.0),          # one chunk, half of it past k_in, one rank
+    (7, 4032, 75, 5, 16.0),       # last chunk half past k_in; n_out and r ragged
+    (16, 2112, 4096, 16, 16.0),   # two chunks per wave, most waves' second chunk empty
+    (3, 128, 4096, 9, 16.0),      # rank group of 4 rows only partly used
+    (12, 4096, 17, 3, 16.0),      # one column past a workgroup of 16
+    (5, 1984, 33, 13, 8.0),       # token and rank groups partly used, ragged k
 ])
 def test_small_shapes(M, K, N, r, alpha):
     _run_case(M, K, N, r, alpha, seed=M + K + N + r)
@@ -145,6 +154,35 @@ def test_identity_grad_exposes_decoded_weight(K, N):
     torch.cuda.synchronize()
     assert torch.all(dB == 0)
     assert_close("dA", _f64(dA), lora_scale(16.0, 8) * (_f64(B).T @ _f64(X)))
+
+
+@pytest.mark.parametrize("M,K,N,r", [
+    (5, 1984, 33, 13),    # n_out and rank padded in the backward, few tokens
+    (5, 1984, 40, 16),    # the same unpadded
+    (40, 192, 75, 8),     # split-K path, n_out padded, rank a multiple of 8 (B not copied)
+    (300, 128, 75, 16),   # many-token path
+    (130, 64, 13, 3),
+    (12, 4096, 17, 3),    # one-launch forward
+    (3, 8448, 64, 8),     # few-token forward split over k (partial sums in the workspace)
+])
+def test_workspace_contents_do_not_matter(M, K, N, r):
+    """Every output is the same whether the workspace starts as zeros or as
+    0xFF bytes (NaN for every float type): nothing is read from it before it
+    is written, and no padding is read from past a buffer's rows."""
+    say(f"[workspace] M={M} K={K} N={N} r={r}")
+    W, A, B, X, dY = _inputs(M, K, N, r, seed=7 + M + N)
+    wq = q.quantize_weight(to_dev(W))
+    Xd, Ad, Bd, dYd = to_dev(X), to_dev(A), to_dev(B), to_dev(dY)
+    outs = []
+    for fill in (0, 255):
+        wf = torch.full((q.workspace_size(0, M, N, K, r),), fill, dtype=torch.uint8, device="cuda")
+        wb = torch.full((q.workspace_size(1, M, N, K, r),), fill, dtype=torch.uint8, device="cuda")
+        Y, U = q.linear_fwd(wq, Xd, Ad, Bd, 16.0, workspace=wf)
+        dX, dA, dB = q.linear_bwd(wq, Xd, dYd, Ad, Bd, U, 16.0, workspace=wb)
+        outs.append([host(t) for t in (Y, U, dX, dA, dB)])
+    for name, a, b in zip(("Y", "U", "dX", "dA", "dB"), *outs):
+        assert torch.isfinite(a.float()).all(), name
+        assert torch.equal(a, b), name
 
 
 def test_deterministic_repeat():
