@@ -36,7 +36,7 @@ qlora_status check_device() {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QLORA_ERR_DEVICE;
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (dev < kMaxDevices) {
-    // the CU count is published before the verdict, so a thread that sees the
+    // the CU count is published before the check result, so a thread that sees the
     // device checked also sees its count
     g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
