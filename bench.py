@@ -11,7 +11,8 @@ one reduction), the transposed dequant-GEMM for dX, and dA = s·Vᵀ·X
 resident seeded synthetic inputs; `value` = algorithmic TFLOP/s of the step.
 The roofline object is the forward dequant-GEMM over the layer's seven
 launches, timed on the stream it runs on; `roofline_gemv` is the few-token
-dequant-GEMV kernel (8192 -> 28672, 1 token) against HBM.  The same run also
+dequant-GEMV kernel (8192 -> 28672, 1 token) against HBM (its traffic from
+the committed summary of the HBM-bound kernels' byte counters).  The same run also
 measures, in `rows`, the LLaMA-7B MLP training step (4096 tokens, 4096 ->
 11008, r = 64), the fused NF4 + double-quant quantiser and the dequantiser
 (one matrix and the whole 224-matrix LLaMA-7B weight set), the few-token
@@ -69,6 +70,30 @@ def read_traffic():
         return float(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+HBM_SUMMARY = os.path.join(ROOT, "profiles", "traffic_hbm_bound_kernels.txt")
+
+
+def read_gemv_traffic():
+    """Counted HBM bytes per launch (read + write) of the few-token GEMV at one
+    token on the 8192 -> 28672 weight, from the committed summary of the
+    HBM-bound kernels, or None if absent or taken on a different kernel source."""
+    if not os.path.exists(HBM_SUMMARY):
+        return None
+    lines = open(HBM_SUMMARY).read().splitlines()
+    src = [ln.split("=", 1)[1].strip() for ln in lines if ln.startswith("kernel_source_sha256_16")]
+    if not src or src[0] != hbm_source_hash():
+        return None
+    for ln in lines:
+        if ln.startswith("few-token GEMV, 1 token:"):
+            try:
+                rd = ln.split("read", 1)[1].split("/", 1)[0]
+                wr = ln.split("write", 1)[1].split("/", 1)[0]
+                return float(rd) + float(wr)
+            except (IndexError, ValueError):
+                return None
+    return None
 
 
 def _layer_fwd_algo_bytes():
@@ -691,7 +716,7 @@ def gemv_roofline(dev, steps):
     return {"bound": "hbm", "kernel": "nf4_gemv_kernel (8192 -> 28672, r = 16, 1 token)",
             "achieved": a["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": a["GBps"] / HBM_PEAK_GBS, "us_per_launch": a["us"],
-            "bytes_per_launch": a["bytes"], "traffic": None,
+            "bytes_per_launch": a["bytes"], "traffic": read_gemv_traffic(),
             "tokens_8": dict(GBps=res[8]["GBps"], frac=res[8]["GBps"] / HBM_PEAK_GBS,
                              us_per_launch=res[8]["us"])}
 

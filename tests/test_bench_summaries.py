@@ -85,3 +85,22 @@ def test_layer_forward_algorithmic_bytes():
         n = K * N
         ref += n * 0.5 + n / 64 + 4 * n / 16384 + 2 * (M * K + M * r + N * r + M * N)
     assert abs(tot - ref) < 1e-6 * ref
+
+
+def test_gemv_traffic_read_from_the_hbm_summary(tmp_path, monkeypatch):
+    """The GEMV roofline's traffic is the summary's counted read + write bytes
+    of the few-token GEMV line, and None once the kernel sources differ."""
+    good = tmp_path / "hbm.txt"
+    good.write_text("# header\n"
+                    f"kernel_source_sha256_16 = {bench.hbm_source_hash()}\n"
+                    "dequantise: read 10 / 10, write 20 / 20, total 1.000\n"
+                    "few-token GEMV, 1 token: read 122789546 / 122101792, write 57344 / 57344, "
+                    "total 1.006\n")
+    monkeypatch.setattr(bench, "HBM_SUMMARY", str(good))
+    assert bench.read_gemv_traffic() == 122789546 + 57344
+    stale = tmp_path / "stale.txt"
+    stale.write_text(good.read_text().replace(bench.hbm_source_hash(), "0" * 16))
+    monkeypatch.setattr(bench, "HBM_SUMMARY", str(stale))
+    assert bench.read_gemv_traffic() is None
+    monkeypatch.setattr(bench, "HBM_SUMMARY", str(tmp_path / "absent.txt"))
+    assert bench.read_gemv_traffic() is None
