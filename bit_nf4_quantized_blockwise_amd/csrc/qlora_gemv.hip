@@ -146,7 +146,6 @@ __global__ __launch_bounds__(64 * kGemvWaves) void nf4_gemv_kernel(GemvArgs g) {
 
   const char* lutb = reinterpret_cast<const char*>(lut);
   const uint32_t lane4 = (uint32_t)lane * 4;
-  const int64_t ncg = (N + 15) / 16;
   const int64_t blocks_per_row = K >> 6;
   const __amdgpu_buffer_rsrc_t c2r = make_rsrc(g.c2, ((N * blocks_per_row + 255) >> 8) * 4);
   const int64_t cg0 = (int64_t)blockIdx.x * G;
@@ -408,12 +407,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void nf4_small_fwd_kernel(SmallFw
   constexpr int RP = kSmallMaxRank + 1;  // padded pitch of the LDS rows of B and U
   constexpr int SP = 272;                // staging row pitch: 128 bf16 + 16 B
   constexpr int kStage = 2 * 16 * SP;    // one wave's tokens and rows of A for one chunk
-  static_assert(NW * kStage >= 2 * NW * 64 * 16, "the reduction reuses the staging area");
+  static_assert(kStage >= 2 * 64 * 16, "a wave's sums fit its staging area");
   __shared__ __attribute__((aligned(16))) char stage[NW * kStage];
   __shared__ float cb[16];
   __shared__ float bsh[16 * RP];  // B[n0 + c][j] at c·RP + j
   __shared__ float ush[16 * RP];  // U rounded to bf16, token t at t·RP + j
-  floatx4(*red)[NW][64] = reinterpret_cast<floatx4(*)[NW][64]>(stage);  // after the MFMAs
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
   const int64_t K = g.K, N = g.N;
@@ -518,17 +516,21 @@ __global__ __launch_bounds__(64 * kSmallWaves) void nf4_small_fwd_kernel(SmallFw
                                                      __builtin_bit_cast(bf16x8, ao), accU, 0, 0, 0);
     }
   }
-  __syncthreads();  // every wave is done with its staging area
-  red[0][w][lane] = accY;
-  red[1][w][lane] = accU;
+  // each wave's sums go to its own staging area (after its own last reads of
+  // it: no barrier needed for that), Y's at offset 0, U's at 1 KB
+  reinterpret_cast<floatx4*>(xst)[lane] = accY;
+  reinterpret_cast<floatx4*>(xst + 1024)[lane] = accU;
   __syncthreads();
   // output (token t, column c) sits in lane 16·(t / 4) + c, entry t % 4
   const int t = tid >> 4, c = tid & 15;
   const int src = 16 * (t >> 2) + c, e = t & 3;
+  auto red = [&](int ww, int part) {
+    return reinterpret_cast<const floatx4*>(stage + ww * kStage + part * 1024)[src][e];
+  };
   if (tid < 256) {
     float u = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) u += red[1][ww][src][e];
+    for (int ww = 0; ww < NW; ++ww) u += red(ww, 1);
     const uint16_t ub = bf16_rne_bits(u);
     ush[t * RP + c] = bf16_bits_to_float(ub);
     if (blockIdx.x == 0 && t < M && c < r) g.u[t * r + c] = ub;
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void nf4_small_fwd_kernel(SmallFw
   if (tid < 256 && t < M && n0 + c < N) {
     float y = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) y += red[0][ww][src][e];
+    for (int ww = 0; ww < NW; ++ww) y += red(ww, 0);
     float l = 0.0f;
     for (int j = 0; j < r; ++j) l += ush[t * RP + j] * bsh[c * RP + j];
     g.y[(int64_t)t * N + n0 + c] = bf16_rne_bits(y + g.s * l);
