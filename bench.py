@@ -316,7 +316,8 @@ def pmc_pass_hbm():
     """Short run for the byte counters of the HBM-bound kernels: the fused
     quantiser (two launches) and the dequantiser on the 11008 x 4096 weight,
     the few-token forward (U launch + GEMV) at one token on the 8192 -> 28672
-    weight, the rank-r streaming kernels of the LLaMA-65B q projection (2048
+    weight, the one-launch forward of the single 16-token 4096 x 4096 linear
+    (r = 8), the rank-r streaming kernels of the LLaMA-65B q projection (2048
     tokens, 8192 -> 8192, r = 64: U, then V and dB, then dA), three times
     each, and the calibration copy."""
     import torch
@@ -333,6 +334,9 @@ def pmc_pass_hbm():
     p = wl.LLAMA65B_LAYER[0]
     pin = p.inputs()
     wp = q.quantize_weight(torch.from_numpy(pin["W"]).to(dev))
+    sl = wl.SINGLE_LINEAR
+    sin = sl.inputs()
+    wsl = q.quantize_weight(torch.from_numpy(sin["W"]).to(dev))
     W = torch.from_numpy(wl.LLAMA7B_MLP.inputs(with_dy=False)["W"]).to(dev)
     for _ in range(3):
         o = q.quantize_nf4_dq(W, want_absmax=True)
@@ -345,6 +349,10 @@ def pmc_pass_hbm():
     for _ in range(3):
         q.linear_fwd(wg, X, A, B, g.alpha)
     del wg, X, A, B
+    X, A, B = (sin[k].to(dev) for k in ("X", "A", "B"))
+    for _ in range(3):
+        q.linear_fwd(wsl, X, A, B, sl.alpha)
+    del wsl, X, A, B
     X, A, B, dY = (pin[k].to(dev) for k in ("X", "A", "B", "dY"))
     for _ in range(3):
         U = q.lora_down(X, A)
@@ -370,6 +378,7 @@ def summarize_hbm(out_path, fetch_csv, write_csv):
             "qlora::dequantize_nf4_kernel(": "dequantise",
             "qlora::lora_down_small_kernel(": "U = X·Aᵀ, 1 token",
             "qlora::nf4_gemv_kernel<": "few-token GEMV, 1 token",
+            "qlora::nf4_small_fwd_kernel<": "one-launch forward, 16 tokens, 4096 x 4096, r = 8",
             "qlora::adapter_rows_kernel<2, false>(": "U = X·Aᵀ splits (q projection)",
             "qlora::adapter_dy_kernel<2>(": "V = dY·B and dB = s·dYᵀ·U splits, one launch",
             "qlora::adapter_cols_kernel<2, true>(": "dA = s·Vᵀ·X splits",
@@ -399,6 +408,8 @@ def summarize_hbm(out_path, fetch_csv, write_csv):
     n = 11008 * 4096
     nb, ng = n // 64, (n // 64 + 255) // 256
     ng70, n70 = (28672 * 8192 // 64 + 255) // 256, 28672 * 8192
+    n1 = 4096 * 4096
+    ng1 = (n1 // 64 + 255) // 256
     algo = {
         "qlora::quantize_nf4_kernel(": (4 * n, n // 2 + 4 * nb),
         "qlora::double_quant_kernel(": (4 * nb, nb + 4 * ng),
@@ -406,6 +417,10 @@ def summarize_hbm(out_path, fetch_csv, write_csv):
         "qlora::lora_down_small_kernel(": (2 * 8192 + 2 * 16 * 8192, 2 * 16),
         "qlora::nf4_gemv_kernel<": (n70 // 2 + n70 // 64 + 4 * ng70 + 2 * 8192 + 2 * 16 * 28672 + 2 * 16,
                             2 * 28672),
+        # weight storage, X, A and B read once; Y and U written once (every
+        # workgroup reads all of X and A, from L2 after the first)
+        "qlora::nf4_small_fwd_kernel<": (n1 // 2 + n1 // 64 + 4 * ng1 + 2 * 16 * 4096 + 2 * 8 * 4096
+                                         + 2 * 4096 * 8, 2 * 16 * 4096 + 2 * 16 * 8),
         # q projection, M = 2048, K = N = 8192, r = 64: each product's operands
         # read once, its result written once (bf16 U and V, fp32 dA and dB)
         "qlora::adapter_rows_kernel<2, false>(": (2 * 2048 * 8192 + 2 * 64 * 8192, 2 * 2048 * 64),
@@ -416,7 +431,8 @@ def summarize_hbm(out_path, fetch_csv, write_csv):
     with open(out_path, "w") as fh:
         fh.write("# HBM traffic of the HBM-bound kernels: the fused quantiser (two launches) and the\n")
         fh.write("# dequantiser on the 11008 x 4096 weight, the few-token forward at 1 token on the\n")
-        fh.write("# 8192 -> 28672 weight (r = 16), the rank-r streaming kernels of the LLaMA-65B q\n")
+        fh.write("# 8192 -> 28672 weight (r = 16), the one-launch forward of the single 16-token\n")
+        fh.write("# 4096 x 4096 linear (r = 8), the rank-r streaming kernels of the LLaMA-65B q\n")
         fh.write("# projection (2048 tokens, r = 64; their writes are the fp32 partial sums of the\n")
         fh.write("# splits, summed by the next launch, against the result written once).\n")
         fh.write("# rocprofv3 FETCH_SIZE and WRITE_SIZE per launch\n")
