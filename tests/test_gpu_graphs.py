@@ -60,10 +60,16 @@ def _layer(M, K, N, r, seed):
     return wq, A, B, X, dY
 
 
-@pytest.mark.parametrize("M", [1, 8, 256])
-def test_training_step_graph(M):
-    K, N, r, alpha = 512, 1024, 16, 32.0
-    say(f"[graph] fwd + bwd M={M}")
+@pytest.mark.parametrize("M,r", [
+    (1, 16),    # one-launch small-weight forward
+    (8, 16),    # ... with the split-K backward
+    (4, 32),    # few-token GEMV + U launch (rank above the one-launch limit)
+    (40, 16),   # split-K forward
+    (256, 16),  # many-token forward and backward
+])
+def test_training_step_graph(M, r):
+    K, N, alpha = 512, 1024, 32.0
+    say(f"[graph] fwd + bwd M={M} r={r}")
     wq, A, B, X, dY = _layer(M, K, N, r, M)
     dev = X.device
     ws_f = torch.empty(q.workspace_size(0, M, N, K, r), dtype=torch.uint8, device=dev)
