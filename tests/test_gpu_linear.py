@@ -107,6 +107,34 @@ def test_small_shapes(M, K, N, r, alpha):
     _run_case(M, K, N, r, alpha, seed=M + K + N + r)
 
 
+def _sweep_shapes(n, seed, k_max, n_max, r_max):
+    """n seeded (M, K, N, r) of at most 16 tokens: K a multiple of 64 up to
+    k_max, N up to n_max, r up to r_max."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 17))
+        K = 64 * int(rng.integers(1, k_max // 64 + 1))
+        N = int(rng.integers(1, n_max + 1))
+        r = int(rng.integers(1, r_max + 1))
+        out.append((M, K, N, r))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,r", _sweep_shapes(16, 2026, 4096, 4096, 16))
+def test_one_launch_forward_sweep(M, K, N, r):
+    """Seeded shapes inside the one-launch forward's range (<= 16 tokens, r <=
+    16, k_in <= 4096, n_out <= 4096): every output against the oracle."""
+    _run_case(M, K, N, r, 16.0, seed=M * 7 + K + N + r, bwd=False)
+
+
+@pytest.mark.parametrize("M,K,N,r", _sweep_shapes(6, 77, 4096, 9000, 48))
+def test_few_token_forward_sweep(M, K, N, r):
+    """Seeded few-token shapes over both forward kernels (wider weights, larger
+    ranks and k_in take the GEMV): every output against the oracle."""
+    _run_case(M, K, N, r, 16.0, seed=M * 7 + K + N + r, bwd=False)
+
+
 def test_zero_tokens():
     W, A, B, X, dY = _inputs(1, 64, 16, 4, 7)
     wq = q.quantize_weight(to_dev(W))
