@@ -135,6 +135,28 @@ def test_few_token_forward_sweep(M, K, N, r):
     _run_case(M, K, N, r, 16.0, seed=M * 7 + K + N + r, bwd=False)
 
 
+def _fwd_bwd_shapes(n, seed):
+    """n seeded (M, K, N, r) across every path: tokens from the few-token to
+    the many-token range, ragged n_out, k_in a multiple of 64, r up to 130."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 128)),
+                            int(rng.integers(128, 700))]))
+        K = 64 * int(rng.integers(1, 33))
+        N = int(rng.integers(1, 3000))
+        r = int(rng.integers(1, 131))
+        out.append((M, K, N, r))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,r", _fwd_bwd_shapes(12, 4242))
+def test_fwd_bwd_sweep(M, K, N, r):
+    """Seeded shapes across all forward and backward paths: every output and
+    gradient against the oracle."""
+    _run_case(M, K, N, r, 16.0, seed=M * 3 + K + N * 5 + r)
+
+
 def test_zero_tokens():
     W, A, B, X, dY = _inputs(1, 64, 16, 4, 7)
     wq = q.quantize_weight(to_dev(W))
