@@ -94,6 +94,24 @@ def test_small_shapes(M, K, N, r, alpha, p):
     _run_case(M, K, N, r, alpha, p, seed=1000 + M, offset=r, dseed=M)
 
 
+def _sweep(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 128)),
+                            int(rng.integers(128, 600))]))
+        out.append((M, 64 * int(rng.integers(1, 25)), int(rng.integers(1, 2000)),
+                    int(rng.integers(1, 100)), float(rng.choice([0.05, 0.1, 0.5]))))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,r,p", _sweep(8, 515))
+def test_dropout_sweep(M, K, N, r, p):
+    """Seeded shapes and rates across the dropout paths, against the oracle
+    (mask bit-exact, outputs and gradients within tolerance)."""
+    _run_case(M, K, N, r, 16.0, p, seed=7 + M, offset=M * K, dseed=M + N)
+
+
 def test_masked_input_gradient_zero_pattern():
     """With a zero weight dX is the masked adapter term alone: every dropped
     element is exactly +0 and (generically) every kept one is not."""
