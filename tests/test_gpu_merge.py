@@ -68,6 +68,19 @@ def test_merge_16bit_and_4bit_bit_exact(N, K, r, alpha):
     _check_requant(out4, rq4)
 
 
+def _merge_sweep(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 300)), 64 * int(rng.integers(1, 40)), int(rng.integers(1, 257)),
+             float(rng.choice([2.0, 16.0, 32.0]))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("N,K,r,alpha", _merge_sweep(6, 4711))
+def test_merge_sweep(N, K, r, alpha):
+    """Seeded shapes and ranks: merged bf16 and re-quantised bytes bit-exact
+    against the oracle on both bases."""
+    test_merge_16bit_and_4bit_bit_exact(N, K, r, alpha)
+
+
 def test_merge_only_and_repeatable():
     N, K, r = 48, 640, 16
     W16 = torch.from_numpy(wl.weight_f32(990, N, K)).to(torch.bfloat16)
