@@ -254,6 +254,13 @@ size_t qlora_quant_error_workspace_size(int64_t n);
  *   Y = RNE_bf16(X·Ŵᵀ + s·U·Bᵀ)    (fp32 accumulation; Ŵ decoded tile by tile,
  *                                   never materialised)
  * X [M][k_in], A [r][k_in], B [n_out][r], Y [M][n_out] bf16.  M >= 0.
+ * Every path decodes Ŵ as qlora_dequantize_nf4 does and accumulates in fp32;
+ * paths differ only in the order of the fp32 sums, except that for at most
+ * 16 tokens on weights too wide for the one-launch kernel (more than 16
+ * output columns per compute unit, r > 16 or k_in > 4096) each 64-block's
+ * scale multiplies that block's fp32 partial sum of the bf16-rounded levels
+ * (a rounding difference of about 5e-4 relative).  Each path repeats its own
+ * bits exactly.
  * workspace: at least qlora_workspace_size(0, M, n_out, k_in, r) bytes. */
 qlora_status qlora_linear_fwd(const qlora_nf4_weight *w /* host struct */, const qlora_bf16 *X,
                               int64_t M, const qlora_bf16 *A, const qlora_bf16 *B, int32_t r,
