@@ -124,6 +124,39 @@ def test_linear_argument_errors(L):
     assert d(ctypes.byref(q.NF4Weight(FAKE, FAKE, FAKE, 4, 16)), MIS, None) == ALIGN
 
 
+def test_forward_parts_argument_errors(L):
+    down = L.qlora_lora_down
+    dargs = lambda **kw: dict(dict(X=FAKE, M=200, K=128, A=FAKE, r=8, U=FAKE, ws=FAKE,
+                                   wsb=1 << 30, st=None), **kw)
+    dcall = lambda d: down(*d.values())
+    assert dcall(dargs(r=0)) == UNSUP
+    assert dcall(dargs(r=257)) == UNSUP
+    assert dcall(dargs(M=-1)) == SHAPE
+    assert dcall(dargs(K=100)) == SHAPE
+    assert dcall(dargs(K=0)) == SHAPE
+    assert dcall(dargs(M=0, X=None, A=None, U=None, ws=None)) == OK  # no tokens
+    assert dcall(dargs(X=None)) == NULL
+    assert dcall(dargs(A=MIS)) == ALIGN
+    assert dcall(dargs(U=MIS)) == ALIGN
+    assert dcall(dargs(ws=None)) == WS  # many tokens: split partial sums in the workspace
+    assert dcall(dargs(wsb=16)) == WS
+    mm = L.qlora_nf4_matmul_fwd
+    margs = lambda **kw: dict(dict(w=_weight(), X=FAKE, M=16, U=FAKE, B=FAKE, r=8, alpha=16.0,
+                                   Y=FAKE, ws=FAKE, wsb=1 << 30, st=None), **kw)
+    mcall = lambda d: mm(*d.values())
+    assert mcall(margs(r=0)) == UNSUP
+    assert mcall(margs(M=-1)) == SHAPE
+    assert mcall(margs(w=_weight(k_in=100))) == SHAPE
+    assert mcall(margs(w=None)) == NULL
+    assert mcall(margs(w=_weight(packed=MIS))) == ALIGN
+    assert mcall(margs(M=0, X=None, U=None, B=None, Y=None, ws=None)) == OK  # no tokens
+    assert mcall(margs(U=None)) == NULL
+    assert mcall(margs(B=MIS)) == ALIGN
+    assert mcall(margs(Y=None)) == NULL
+    assert mcall(margs(ws=None)) == WS
+    assert mcall(margs(wsb=16)) == WS
+
+
 def test_batch_argument_errors(L):
     qb, db = L.qlora_quantize_nf4_dq_batch, L.qlora_dequantize_nf4_batch
     assert qb(None, 0, None) == OK
@@ -167,6 +200,8 @@ def test_valid_arguments_without_gpu_report_device(L):
                               None) == DEV
     assert L.qlora_linear_fwd_noalloc(_weight(), FAKE, 16, FAKE, FAKE, 8, 16.0, FAKE, FAKE,
                                       None) == DEV
+    # few tokens: U needs no workspace
+    assert L.qlora_lora_down(FAKE, 8, 128, FAKE, 8, FAKE, None, 0, None) == DEV
     # an 8-byte aligned sum is accepted (it is one double)
     assert L.qlora_quant_sq_error(FAKE, 100, 0, FAKE, FAKE, FAKE + 8, FAKE, 4096, None) == DEV
 
