@@ -1027,13 +1027,12 @@ def adamw_row(dev):
     ms_list = _time_ms(step_list, 20, warmup=5)
     nparam = n_t * size
     nbytes = 34 * nparam
-    # the paged step: m and v in pinned host memory (the device keeps p, g and
-    # a 64 MB window), paged in and out every step
+    # the paged step: m and v in pinned host memory (the device keeps p and g),
+    # read and written there by the update every step
     Mh, Vh = Mo.cpu().pin_memory(), V.cpu().pin_memory()
-    win = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
 
     def step_paged():
-        q.adamw_step_paged(list(P), list(G), list(Mh), list(Vh), it[0], win, params_bf16=list(PB),
+        q.adamw_step_paged(list(P), list(G), list(Mh), list(Vh), it[0], params_bf16=list(PB),
                            grad_norm=norm, workspace=ws)
         it[0] += 1
     ms_paged = _time_ms(step_paged, 5, warmup=2)
@@ -1041,7 +1040,7 @@ def adamw_row(dev):
     return dict(tensors=n_t, params=nparam, ms=ms, GBps=nbytes / ms / 1e6,
                 hbm_frac=nbytes / ms / 1e6 / HBM_PEAK_GBS, ms_unprepared_list=ms_list,
                 paged=dict(ms=ms_paged, host_link_GBps=moved / ms_paged / 1e6,
-                           window_bytes=64 << 20, device_bytes_saved=8 * nparam))
+                           device_bytes_saved=8 * nparam))
 
 
 def variant_rows(W):

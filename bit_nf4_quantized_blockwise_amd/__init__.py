@@ -95,7 +95,7 @@ _SIGNATURES = {
                           _SZ, _P], _I32),
     "qlora_adamw_workspace_size": ([_I32], _SZ),
     "qlora_adamw_step_paged": ([ctypes.POINTER(AdamWTensor), _I32, _F, _F, _F, _F, _F, _I64, _F, _P,
-                                _P, _SZ, _P, _SZ, _P], _I32),
+                                _P, _SZ, _P], _I32),
     "qlora_adamw_plan_size": ([ctypes.POINTER(AdamWTensor), _I32], _SZ),
     "qlora_adamw_plan_init": ([ctypes.POINTER(AdamWTensor), _I32, _P, _SZ,
                                ctypes.POINTER(AdamWPlanC), _P], _I32),
@@ -619,12 +619,12 @@ def adamw_step_list(lst, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight
            "qlora_adamw_step")
 
 
-def adamw_step_paged(params, grads, ms_host, vs_host, step, window, lr=2e-4, beta1=0.9,
+def adamw_step_paged(params, grads, ms_host, vs_host, step, lr=2e-4, beta1=0.9,
                      beta2=0.999, eps=1e-8, weight_decay=0.001, max_grad_norm=0.3,
                      params_bf16=None, grad_norm=None, workspace=None):
     """adamw_step with the states m, v in pinned host memory (CPU tensors made
-    with pin_memory=True), paged through `window` (a CUDA uint8 tensor of at
-    least 16 KB).  The copies run on the current stream: synchronise it before
+    with pin_memory=True), which the update reads and writes in place across
+    the host link.  It runs on the current stream: synchronise it before
     reading m or v on the host."""
     n = len(params)
     pbs = params_bf16 if params_bf16 is not None else [None] * n
@@ -645,16 +645,15 @@ def adamw_step_paged(params, grads, ms_host, vs_host, step, window, lr=2e-4, bet
         arr[i] = AdamWTensor(p.data_ptr(), grads[i].data_ptr(), ms_host[i].data_ptr(),
                              vs_host[i].data_ptr(),
                              pbs[i].data_ptr() if pbs[i] is not None else None, p.numel())
-    _need(window, "window", torch.uint8)
     _opt(grad_norm, "grad_norm", torch.float32, min_numel=1)
-    dev = params[0].device if n else window.device
+    dev = params[0].device if n else torch.device("cuda", torch.cuda.current_device())
     if workspace is None:
         workspace = torch.empty(adamw_workspace_size(n), dtype=torch.uint8, device=dev)
     _ws_need(workspace)
     _check(lib().qlora_adamw_step_paged(arr, n, lr, beta1, beta2, eps, weight_decay, step,
-                                        max_grad_norm, _ptr(grad_norm), _ptr(window),
-                                        window.numel(), _ptr(workspace), workspace.numel(),
-                                        _stream(dev)), "qlora_adamw_step_paged")
+                                        max_grad_norm, _ptr(grad_norm), _ptr(workspace),
+                                        workspace.numel(), _stream(dev)),
+           "qlora_adamw_step_paged")
 
 
 class AdamWPlan:

@@ -1305,8 +1305,6 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const qlora_bf1
 // AdamW workspace: the clipping coefficient (float) at byte 0, the norm
 // launches' float64 partial sums from byte kAdamPartialsOffset.
 constexpr size_t kAdamPartialsOffset = 256;
-// smallest window of the paged step: one chunk of m and one of v
-constexpr size_t kAdamPagedMinWindow = 2 * sizeof(float) * kAdamChunk;
 
 size_t qlora_adamw_workspace_size(int32_t count) {
   if (count < 0) return 0;
@@ -1314,24 +1312,36 @@ size_t qlora_adamw_workspace_size(int32_t count) {
   return kAdamPartialsOffset + (size_t)groups * kAdamNormWgs * sizeof(double);
 }
 
-qlora_status qlora_adamw_step(const qlora_adamw_tensor* t, int32_t count, float lr, float beta1,
-                              float beta2, float eps, float weight_decay, int64_t step,
-                              float max_grad_norm, float* grad_norm, void* workspace,
-                              size_t ws_bytes, void* stream) {
+namespace {
+
+// Arguments of both steps, checked before anything is enqueued.
+qlora_status validate_adamw_step(const qlora_adamw_tensor* t, int32_t count, float lr,
+                                 float beta1, float beta2, float eps, float weight_decay,
+                                 int64_t step, float max_grad_norm, float* grad_norm,
+                                 void* workspace, size_t ws_bytes) {
   qlora_status s = validate_adamw_tensors(t, count);
   if (s != QLORA_OK) return s;
   if ((s = validate_adamw_hyper(lr, beta1, beta2, eps, weight_decay, step, max_grad_norm,
                                 grad_norm)) != QLORA_OK)
     return s;
-  const bool clip = max_grad_norm > 0.0f;
-  const bool need_norm = clip || grad_norm != nullptr;
-  if (need_norm)
+  if (max_grad_norm > 0.0f || grad_norm != nullptr)
     QCHECK(workspace != nullptr && aligned16(workspace) &&
                ws_bytes >= qlora_adamw_workspace_size(count),
            QLORA_ERR_WORKSPACE);
-  s = check_device();
-  if (s != QLORA_OK) return s;
+  return check_device();
+}
+
+// The step itself (validated arguments): the norm passes and the clipping
+// coefficient when asked for, then the update, kAdamMaxTensors tensors per
+// launch.  m and v may be device memory or pinned host memory.
+qlora_status adamw_step_impl(const qlora_adamw_tensor* t, int32_t count, float lr, float beta1,
+                             float beta2, float eps, float weight_decay, int64_t step,
+                             float max_grad_norm, float* grad_norm, void* workspace,
+                             void* stream) {
+  qlora_status s;
   if (count == 0) return QLORA_OK;
+  const bool clip = max_grad_norm > 0.0f;
+  const bool need_norm = clip || grad_norm != nullptr;
   hipStream_t st = as_stream(stream);
   const AdamHyper h = adamw_hyper(lr, beta1, beta2, eps, weight_decay, step);
 
@@ -1377,129 +1387,47 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor* t, int32_t count, float 
   return launched();
 }
 
-// Paged step: m and v in pinned host memory, streamed through the device window
-// in pieces (whole 2048-element chunks, a tensor's last piece may be short):
-// per batch of pieces, page in (host -> window), update, page out (window ->
-// host), all in stream order.  Adjacent pieces whose host and window ranges
-// both continue each other travel in one copy.
+}  // namespace
+
+qlora_status qlora_adamw_step(const qlora_adamw_tensor* t, int32_t count, float lr, float beta1,
+                              float beta2, float eps, float weight_decay, int64_t step,
+                              float max_grad_norm, float* grad_norm, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  const qlora_status s = validate_adamw_step(t, count, lr, beta1, beta2, eps, weight_decay, step,
+                                             max_grad_norm, grad_norm, workspace, ws_bytes);
+  if (s != QLORA_OK) return s;
+  return adamw_step_impl(t, count, lr, beta1, beta2, eps, weight_decay, step, max_grad_norm,
+                         grad_norm, workspace, stream);
+}
+
+// Paged step: m and v stay in pinned host memory and the update kernel reads
+// and writes them there, across the host link (reads and writes flow at the
+// same time); the norm passes read only the gradients.
 qlora_status qlora_adamw_step_paged(const qlora_adamw_tensor* t, int32_t count, float lr,
                                     float beta1, float beta2, float eps, float weight_decay,
                                     int64_t step, float max_grad_norm, float* grad_norm,
-                                    void* window, size_t window_bytes, void* workspace,
-                                    size_t ws_bytes, void* stream) {
-  qlora_status s = validate_adamw_tensors(t, count);
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  qlora_status s = validate_adamw_step(t, count, lr, beta1, beta2, eps, weight_decay, step,
+                                       max_grad_norm, grad_norm, workspace, ws_bytes);
   if (s != QLORA_OK) return s;
-  if ((s = validate_adamw_hyper(lr, beta1, beta2, eps, weight_decay, step, max_grad_norm,
-                                grad_norm)) != QLORA_OK)
-    return s;
-  QCHECK(window != nullptr && aligned16(window), QLORA_ERR_WORKSPACE);
-  QCHECK(window_bytes >= kAdamPagedMinWindow, QLORA_ERR_WORKSPACE);
-  const bool clip = max_grad_norm > 0.0f;
-  const bool need_norm = clip || grad_norm != nullptr;
-  if (need_norm)
-    QCHECK(workspace != nullptr && aligned16(workspace) &&
-               ws_bytes >= qlora_adamw_workspace_size(count),
-           QLORA_ERR_WORKSPACE);
-  s = check_device();
-  if (s != QLORA_OK) return s;
-  // the states must be pinned host memory (else every copy would be a
-  // synchronous staged one); the query's error, if any, is cleared
-  for (int32_t i = 0; i < count; ++i) {
-    if (t[i].n == 0) continue;
-    for (const float* hp : {static_cast<const float*>(t[i].m), static_cast<const float*>(t[i].v)}) {
+  // the states must be page-locked host memory; the kernel reaches them at
+  // the device addresses of their mappings (the queries' errors, if any, are
+  // cleared)
+  std::vector<qlora_adamw_tensor> dt(t, t + count);
+  for (qlora_adamw_tensor& x : dt) {
+    if (x.n == 0) continue;
+    for (float** hp : {&x.m, &x.v}) {
       hipPointerAttribute_t at{};
-      const hipError_t e = hipPointerGetAttributes(&at, hp);
+      const hipError_t e = hipPointerGetAttributes(&at, *hp);
       (void)hipGetLastError();
-      QCHECK(e == hipSuccess && at.type == hipMemoryTypeHost, QLORA_ERR_UNSUPPORTED);
+      QCHECK(e == hipSuccess && at.type == hipMemoryTypeHost && at.devicePointer != nullptr,
+             QLORA_ERR_UNSUPPORTED);
+      QCHECK(aligned16(at.devicePointer), QLORA_ERR_ALIGN);
+      *hp = static_cast<float*>(at.devicePointer);
     }
   }
-  if (count == 0) return QLORA_OK;
-  hipStream_t st = as_stream(stream);
-  const AdamHyper h = adamw_hyper(lr, beta1, beta2, eps, weight_decay, step);
-
-  // the clipping coefficient: the same norm passes as qlora_adamw_step (the
-  // gradients are on the device), so both steps give the same bits
-  float* coef = static_cast<float*>(workspace);
-  if (need_norm) {
-    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) +
-                                                 kAdamPartialsOffset);
-    int32_t npart = 0;
-    for (int32_t first = 0; first < count; first += kAdamMaxTensors) {
-      AdamList L{};
-      L.count = std::min(kAdamMaxTensors, count - first);
-      int64_t c = 0;
-      for (int i = 0; i < L.count; ++i) {
-        const qlora_adamw_tensor& x = t[first + i];
-        L.t[i] = AdamTensor{x.param, x.grad, nullptr, nullptr, nullptr, x.n, c};
-        c += ceil_div(x.n, kAdamChunk);
-      }
-      L.chunks = c;
-      if (c == 0) continue;
-      const int grid = (int)std::min<int64_t>(c, kAdamNormWgs);
-      hipLaunchKernelGGL(adam_sqnorm_kernel, dim3(grid), dim3(kAdamThreads), 0, st, L,
-                         partials + npart);
-      npart += grid;
-    }
-    hipLaunchKernelGGL(adam_clip_kernel, dim3(1), dim3(kAdamThreads), 0, st, partials, npart,
-                       max_grad_norm, clip ? 1 : 0, coef, grad_norm);
-    if ((s = launched()) != QLORA_OK) return s;
-  }
-
-  // the window: m in the first half, v in the second, whole chunks each
-  const int64_t cap = (int64_t)(window_bytes / 2 / sizeof(float)) / kAdamChunk * kAdamChunk;
-  float* wm = static_cast<float*>(window);
-  float* wv = wm + cap;
-  struct Copy { float* dev; float* host; int64_t n; };
-  std::vector<Copy> cm, cv;
-  auto add = [](std::vector<Copy>& cs, float* dev, float* host, int64_t n) {
-    if (!cs.empty() && cs.back().dev + cs.back().n == dev && cs.back().host + cs.back().n == host)
-      cs.back().n += n;
-    else
-      cs.push_back(Copy{dev, host, n});
-  };
-  AdamList L{};
-  int64_t used = 0;
-  auto flush = [&]() -> qlora_status {
-    if (L.count == 0) return QLORA_OK;
-    for (const Copy& c : cm)
-      if (hipMemcpyAsync(c.dev, c.host, c.n * sizeof(float), hipMemcpyHostToDevice, st) != hipSuccess)
-        return QLORA_ERR_LAUNCH;
-    for (const Copy& c : cv)
-      if (hipMemcpyAsync(c.dev, c.host, c.n * sizeof(float), hipMemcpyHostToDevice, st) != hipSuccess)
-        return QLORA_ERR_LAUNCH;
-    const int grid = (int)std::min<int64_t>(L.chunks, kAdamMaxGrid);
-    hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kAdamThreads), 0, st, L, h,
-                       clip ? coef : nullptr);
-    if (hipGetLastError() != hipSuccess) return QLORA_ERR_LAUNCH;
-    for (const Copy& c : cm)
-      if (hipMemcpyAsync(c.host, c.dev, c.n * sizeof(float), hipMemcpyDeviceToHost, st) != hipSuccess)
-        return QLORA_ERR_LAUNCH;
-    for (const Copy& c : cv)
-      if (hipMemcpyAsync(c.host, c.dev, c.n * sizeof(float), hipMemcpyDeviceToHost, st) != hipSuccess)
-        return QLORA_ERR_LAUNCH;
-    L = AdamList{};
-    used = 0;
-    cm.clear();
-    cv.clear();
-    return QLORA_OK;
-  };
-  for (int32_t i = 0; i < count; ++i) {
-    const qlora_adamw_tensor& x = t[i];
-    for (int64_t off = 0; off < x.n;) {
-      if (used == cap || L.count == kAdamMaxTensors)
-        if ((s = flush()) != QLORA_OK) return s;
-      const int64_t piece = std::min(x.n - off, cap - used);
-      L.t[L.count] = AdamTensor{x.param + off, x.grad + off, wm + used, wv + used,
-                                x.param_bf16 ? x.param_bf16 + off : nullptr, piece, L.chunks};
-      L.chunks += ceil_div(piece, kAdamChunk);
-      ++L.count;
-      add(cm, wm + used, x.m + off, piece);
-      add(cv, wv + used, x.v + off, piece);
-      used += ceil_div(piece, kAdamChunk) * kAdamChunk;  // pieces start on chunk boundaries
-      off += piece;
-    }
-  }
-  return flush();
+  return adamw_step_impl(dt.data(), count, lr, beta1, beta2, eps, weight_decay, step,
+                         max_grad_norm, grad_norm, workspace, stream);
 }
 
 size_t qlora_adamw_plan_size(const qlora_adamw_tensor* tensors, int32_t count) {

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QLORA_ABI_VERSION 2
+#define QLORA_ABI_VERSION 3
 #define QLORA_BLOCKSIZE 64   /* first-level block (NF4), elements */
 #define QLORA_DQ_GROUP 256   /* second-level group, blocks */
 #define QLORA_MAX_RANK 256
@@ -354,22 +354,21 @@ size_t qlora_adamw_workspace_size(int32_t count);
 /* Paged optimizer states ("QLoRAの理論と実装", §5-3 Paged Optimizers: the
  * optimizer states leave GPU memory when it runs short and come back to the
  * GPU when the update needs them).  Exactly qlora_adamw_step (same bits),
- * except that every tensor's m and v are HOST pointers into pinned memory
- * (hipHostMalloc or another page-locked allocation; else
+ * except that every tensor's m and v are HOST pointers into page-locked
+ * memory (hipHostMalloc, or a tensor made with pin_memory; else
  * QLORA_ERR_UNSUPPORTED) that the caller owns and that stays the states'
- * home: they are paged in to `window` (caller-owned device memory,
- * window_bytes >= 16384, else QLORA_ERR_WORKSPACE), updated there and paged
- * out again, a window's worth at a time, all on `stream` (asynchronous copies;
- * the host must not touch m and v until the stream reaches them).  The
- * device then holds only p, g and the window — 8 bytes per parameter less
- * than the resident step.  These GPUs run without demand paging, so the
- * transfers are explicit; on one stream they do not overlap the update.
+ * home: the update kernel reads and writes them there, across the host
+ * link, at the device addresses of their mappings, on `stream` (the host
+ * must not touch m and v until the stream has passed the call).  The
+ * device holds only p and g: 8 bytes per parameter less than the resident
+ * step.  Reads and writes cross the link at the same time, so this moves
+ * the states faster than paging them in and out with copies on one stream.
  * Workspace as for qlora_adamw_step. */
 qlora_status qlora_adamw_step_paged(const qlora_adamw_tensor *tensors /* host array; m, v host */,
                                     int32_t count, float lr, float beta1, float beta2, float eps,
                                     float weight_decay, int64_t step, float max_grad_norm,
-                                    float *grad_norm, void *window, size_t window_bytes,
-                                    void *workspace, size_t ws_bytes, void *stream);
+                                    float *grad_norm, void *workspace, size_t ws_bytes,
+                                    void *stream);
 
 /* A prepared tensor list for a training loop that steps the same tensors
  * every iteration: the descriptors and a chunk -> tensor map copied once into

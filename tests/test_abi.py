@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_strings(L):
-    assert q.abi_version() == 2
+    assert q.abi_version() == 3
     for s in range(8):
         assert q.status_string(s).startswith(q.STATUS[s])
 
@@ -236,14 +236,14 @@ def test_adamw_argument_errors(L):
     assert call(a=bad, n=1) == SHAPE
     pg = L.qlora_adamw_step_paged
 
-    def paged(win=FAKE, winb=1 << 20, **kw):
+    def paged(ws=FAKE, wsb=1 << 20, **kw):
         p = dict(args, **kw)
         return pg(arr, 2, p["lr"], p["b1"], p["b2"], p["eps"], p["wd"], p["step"], p["clip"], None,
-                  win, winb, FAKE, 1 << 20, None)
-    assert paged(win=None) == WS
-    assert paged(winb=16383) == WS
-    assert paged(win=MIS) == WS
+                  ws, wsb, None)
+    assert paged(ws=None) == WS  # clipping needs the workspace
+    assert paged(wsb=8) == WS
     assert paged(step=0) == SHAPE
+    assert paged(b1=1.0) == UNSUP
     assert L.qlora_adamw_workspace_size(-1) == 0
     assert L.qlora_adamw_workspace_size(0) >= 256
     assert L.qlora_adamw_workspace_size(200) >= 5 * 256 * 8

@@ -164,10 +164,10 @@ def test_prepared_list_repeatable():
         assert np.array_equal(a, b)
 
 
-def _paged_vs_resident(sizes, steps, window_bytes, max_norm, seed):
-    """The paged step (m, v in pinned host memory, streamed through a device
-    window) against the resident step from the same state: p, m, v, the bf16
-    copies and the norm bit for bit, step after step."""
+def _paged_vs_resident(sizes, steps, max_norm, seed):
+    """The paged step (m, v in pinned host memory, updated there across the
+    host link) against the resident step from the same state: p, m, v, the
+    bf16 copies and the norm bit for bit, step after step."""
     rng = np.random.default_rng(seed)
     dev = torch.device("cuda:0")
     st = [_state(rng, n, 1) for n in sizes]
@@ -182,14 +182,12 @@ def _paged_vs_resident(sizes, steps, window_bytes, max_norm, seed):
            for i, n in enumerate(sizes)]
     PB2 = [torch.empty_like(x) if x is not None else None for x in PB1]
     n1, n2 = (torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(2))
-    window = torch.empty(window_bytes, dtype=torch.uint8, device=dev)
     for step in steps:
-        say(f"[adamw paged] {len(sizes)} tensors window={window_bytes} step={step} "
-            f"max_norm={max_norm}")
+        say(f"[adamw paged] {len(sizes)} tensors step={step} max_norm={max_norm}")
         for t in G:
             t.copy_(torch.from_numpy((rng.standard_normal(t.numel()) * 0.3).astype(np.float32)))
         q.adamw_step(P1, G, M1, V1, step, max_grad_norm=max_norm, params_bf16=PB1, grad_norm=n1)
-        q.adamw_step_paged(P2, G, M2, V2, step, window, max_grad_norm=max_norm, params_bf16=PB2,
+        q.adamw_step_paged(P2, G, M2, V2, step, max_grad_norm=max_norm, params_bf16=PB2,
                            grad_norm=n2)
         torch.cuda.synchronize()
         assert torch.equal(n1.view(torch.int32), n2.view(torch.int32))
@@ -201,32 +199,54 @@ def _paged_vs_resident(sizes, steps, window_bytes, max_norm, seed):
                 assert torch.equal(PB1[i].view(torch.int16), PB2[i].view(torch.int16)), i
 
 
-@pytest.mark.parametrize("window_kb", [16, 1024, 65536])
 @pytest.mark.parametrize("max_norm", [0.3, 0.0])
-def test_paged_step_equals_resident_step(window_kb, max_norm):
-    # the smallest window splits every tensor of more than 2048 elements into
-    # many pieces; the largest holds the whole set in one batch
-    _paged_vs_resident([1, 3, 4, 5, 257, 4096 * 64 + 3, 0, 11008, 100003], [1, 2, 3],
-                       window_kb * 1024, max_norm, seed=window_kb)
+def test_paged_step_equals_resident_step(max_norm):
+    # ragged sizes (tails of 1-3 elements, a partial last chunk, an empty tensor)
+    _paged_vs_resident([1, 3, 4, 5, 257, 4096 * 64 + 3, 0, 11008, 100003], [1, 2, 3], max_norm,
+                       seed=7)
 
 
-def test_paged_step_more_pieces_than_one_launch_holds():
-    # 100 small tensors: batches close at 48 descriptors before the window fills
-    _paged_vs_resident([17 + (i * 37) % 300 for i in range(100)], [1, 2], 1 << 20, 0.3, seed=11)
+def test_paged_step_more_tensors_than_one_launch_holds():
+    # 100 small tensors: three launches of at most 48 descriptors
+    _paged_vs_resident([17 + (i * 37) % 300 for i in range(100)], [1, 2], 0.3, seed=11)
 
 
-def test_paged_step_rejects_unpinned_states_and_small_windows():
+def test_paged_step_states_at_an_offset_into_their_allocation():
+    # m and v as views into larger pinned buffers (the device address of each
+    # view, not of its allocation, must be used)
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(13)
+    n = 5000
+    p0, m0, v0 = (rng.standard_normal(n).astype(np.float32) * s for s in (0.01, 1e-4, 1e-6))
+    v0 = np.abs(v0)
+    g = torch.from_numpy(rng.standard_normal(n).astype(np.float32) * 0.3).to(dev)
+    P1, P2 = torch.from_numpy(p0).to(dev), torch.from_numpy(p0).to(dev)
+    M1, V1 = torch.from_numpy(m0).to(dev), torch.from_numpy(v0).to(dev)
+    mbuf = torch.zeros(n + 1024).pin_memory()
+    vbuf = torch.zeros(n + 4096).pin_memory()
+    M2, V2 = mbuf[512:512 + n], vbuf[2048:2048 + n]
+    M2.copy_(torch.from_numpy(m0))
+    V2.copy_(torch.from_numpy(v0))
+    q.adamw_step([P1], [g], [M1], [V1], 1, max_grad_norm=0.3)
+    q.adamw_step_paged([P2], [g], [M2], [V2], 1, max_grad_norm=0.3)
+    torch.cuda.synchronize()
+    assert torch.equal(P1.view(torch.int32), P2.view(torch.int32))
+    assert torch.equal(host(M1).view(torch.int32), M2.view(torch.int32))
+    assert torch.equal(host(V1).view(torch.int32), V2.view(torch.int32))
+    assert torch.all(mbuf[:512] == 0) and torch.all(mbuf[512 + n:] == 0)
+    assert torch.all(vbuf[:2048] == 0) and torch.all(vbuf[2048 + n:] == 0)
+
+
+def test_paged_step_rejects_unpinned_states():
     dev = torch.device("cuda:0")
     p = torch.zeros(100, device=dev)
     g = torch.ones(100, device=dev)
-    m_pin, v_pin = torch.zeros(100).pin_memory(), torch.zeros(100).pin_memory()
+    v_pin = torch.zeros(100).pin_memory()
     m_pageable = torch.zeros(100)
-    win = torch.empty(16384, dtype=torch.uint8, device=dev)
     with pytest.raises(q.QloraError) as e:
-        q.adamw_step_paged([p], [g], [m_pageable], [v_pin], 1, win)
+        q.adamw_step_paged([p], [g], [m_pageable], [v_pin], 1)
     assert e.value.status == 4
-    with pytest.raises(q.QloraError) as e:
-        q.adamw_step_paged([p], [g], [m_pin], [v_pin], 1, win[:16000])
-    assert e.value.status == 5
+    with pytest.raises(ValueError):  # device memory is not a host state either
+        q.adamw_step_paged([p], [g], [torch.zeros(100, device=dev)], [v_pin], 1)
     torch.cuda.synchronize()
     assert torch.all(p == 0)  # nothing ran
