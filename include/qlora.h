@@ -22,7 +22,8 @@
  *     must be 16-byte aligned (unless its entry point states otherwise).  The caller owns every buffer; the library never
  *     allocates, frees or keeps a pointer past the call.
  *   * `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *     Work is enqueued asynchronously on it; no call synchronises.
+ *     Work is enqueued asynchronously on it; no call synchronises, except
+ *     qlora_adamw_plan_init (a one-time copy of its list from host memory).
  *   * Arguments are validated on the host before anything is enqueued.  On any
  *     error status nothing is launched and no output is touched.  A failed
  *     launch returns QLORA_ERR_LAUNCH.  Faults during execution surface at the
