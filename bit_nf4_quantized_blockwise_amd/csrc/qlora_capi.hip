@@ -753,7 +753,7 @@ const char* qlora_status_string(qlora_status s) {
     case QLORA_ERR_NULL: return "QLORA_ERR_NULL: a required pointer is NULL";
     case QLORA_ERR_SHAPE: return "QLORA_ERR_SHAPE: invalid size";
     case QLORA_ERR_ALIGN: return "QLORA_ERR_ALIGN: device pointer not 16-byte aligned";
-    case QLORA_ERR_UNSUPPORTED: return "QLORA_ERR_UNSUPPORTED: unsupported blocksize, group or rank";
+    case QLORA_ERR_UNSUPPORTED: return "QLORA_ERR_UNSUPPORTED: unsupported parameter (blocksize, group, rank, code, optimizer or dropout setting, or unpinned host states)";
     case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace missing or too small";
     case QLORA_ERR_DEVICE: return "QLORA_ERR_DEVICE: no gfx950 device current";
     case QLORA_ERR_LAUNCH: return "QLORA_ERR_LAUNCH: kernel launch failed";

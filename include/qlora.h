@@ -56,7 +56,10 @@ typedef enum {
   QLORA_ERR_NULL = 1,        /* a required pointer is NULL */
   QLORA_ERR_SHAPE = 2,       /* a size is negative, out of range or not a required multiple */
   QLORA_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
-  QLORA_ERR_UNSUPPORTED = 4, /* blocksize != 64, group != 256, r outside [1, 256] */
+  QLORA_ERR_UNSUPPORTED = 4, /* a parameter outside what is supported: blocksize != 64,
+                                group != 256, r outside [1, 256], an unknown 4-bit code,
+                                an optimizer or dropout setting out of range, or host
+                                states that are not page-locked */
   QLORA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than qlora_workspace_size() */
   QLORA_ERR_DEVICE = 6,      /* no device, or the current device is not gfx950 */
   QLORA_ERR_LAUNCH = 7       /* a kernel launch failed */
