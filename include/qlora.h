@@ -304,10 +304,14 @@ qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight *w /* host struct *
                                       const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *Y,
                                       qlora_bf16 *U, void *stream);
 
-/* The forward's two launches, callable on their own (the forward is exactly
- * qlora_lora_down then qlora_nf4_matmul_fwd):
+/* The forward's two parts, callable on their own:
  *   qlora_lora_down:      U = X·Aᵀ, bf16 [M][r]
- *   qlora_nf4_matmul_fwd: Y = RNE_bf16(X·Ŵᵀ + s·U·Bᵀ)
+ *   qlora_nf4_matmul_fwd: Y = RNE_bf16(X·Ŵᵀ + s·U·Bᵀ), U given
+ * qlora_linear_fwd is exactly these two calls, except on the weights its
+ * one-launch kernel takes (at most 16 tokens, r <= 16, k_in <= 4096, at most
+ * 16 output columns per compute unit), where it forms U and Y in one launch:
+ * there the two routes differ in the order of their fp32 sums, and the
+ * second uses the few-token path's per-block scaling described above.
  * Same shapes, preconditions and workspace as qlora_linear_fwd. */
 qlora_status qlora_lora_down(const qlora_bf16 *X, int64_t M, int64_t k_in, const qlora_bf16 *A,
                              int32_t r, qlora_bf16 *U, void *workspace, size_t ws_bytes,
